@@ -1,0 +1,192 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized attention forward pass on one MI355X.
+
+One step = the whole hot path on one batch of synthetic inputs already resident in HBM:
+K smoothing -> block quantization of Q, K (and V) -> (Thrift selection) -> fused attention.
+`value` is the step's throughput in the metric's units, 4*B*H*N^2*D ops per step (halved for
+causal) / step time, in TOPS.  The `roofline` object is the attention kernel alone, timed with
+HIP events around its launches on the stream it runs on.  `cpu_baseline` is the oracle timed
+on a bounded sample of the same workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload llm_int8] [--causal]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense peaks (TOPS / TFLOPS) and HBM bandwidth (GB/s)
+PEAK = {"int8": 5000.0, "fp8": 5000.0, "bf16": 2500.0, "fp4": 10100.0}
+HBM_GBS = 8000.0
+
+DEFAULT_VARIANT = {"tiny_int8": "int8", "llm_int8": "int8", "video_fp8": "int8_fp8pv", "fp4_search": "mxfp4",
+                   "thrift_long": "thrift"}
+VARIANT_PEAK = {"int8": "int8", "thrift": "int8", "int8_fp8pv": "int8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
+VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "int8_fp8pv": "int8+fp8", "mxfp4": "mxfp4",
+                 "nvfp4_search": "nvfp4->mxfp8"}
+
+
+def attention_kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn_i8.hip", "attn_mx.hip", "device.hpp"):
+        h.update(open(os.path.join(ROOT, "bit_quantized_attention_03_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str, causal: bool, variant: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "attn_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{workload}:{'causal' if causal else 'noncausal'}:{variant}")
+    except Exception:
+        return None
+    if not rec or rec.get("kernel_hash") != attention_kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float):
+    """The oracle as it stands, on whole (b, h) heads of the same workload (CPU tensors q, k,
+    v), until ~budget_s."""
+    import oracle
+    from tests.parity import oracle_pass
+
+    threads = min(16, oracle.hardware_threads())
+    heads = [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2), (0, w.Hq - 1), (w.B - 1, 0)]
+    g = w.Hq // w.Hkv
+    ops = 0.0
+    done = []
+    t0 = time.perf_counter()
+    for b, h in heads:
+        hk = h // g
+        qs, ks_, vs = (q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, hk:hk + 1].contiguous(),
+                       v[b:b + 1, hk:hk + 1].contiguous())
+        oracle_pass(qs, ks_, vs, causal, variant, threads=threads)
+        ops += 4.0 * w.N * w.N * w.D / (2.0 if causal else 1.0)
+        done.append(f"({b},{h})")
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t = time.perf_counter() - t0
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{len(done)} whole (b,h) heads {' '.join(done)} of {w.name} at N={w.N}, D={w.D}"
+                      f"{' causal' if causal else ''}: smoothing + quantization + tiled attention, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llm_int8")
+    ap.add_argument("--variant", default=None)
+    ap.add_argument("--causal", action="store_true", help="causal mask (the thrift workload is always causal)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path runs on a single MI355X and has no multi-GPU mode "
+              "(heads shard across GPUs with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bit_quantized_attention_03_amd import inputs as I
+    from bit_quantized_attention_03_amd import sage
+
+    w = I.workload(args.workload)
+    variant = args.variant or DEFAULT_VARIANT[w.name]
+    causal = bool(args.causal or w.causal)
+    dev = torch.device("cuda:0")
+    q_cpu, k_cpu, v_cpu = I.make_qkv(w, seed=0)
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    torch.cuda.synchronize()
+    B, Hq, N, D = q.shape
+    ops = 4.0 * B * Hq * N * N * D / (2.0 if causal else 1.0)
+
+    # the step, with events around the attention launch
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record: bool):
+        mean, ks = sage.smooth_k(k)
+        mask = None
+        if variant in ("int8", "thrift", "int8_fp8pv"):
+            qq = sage.quantize(q, sage.INT8, (128, D))
+            kq = sage.quantize(ks, sage.INT8, (64, D))
+            if variant == "int8_fp8pv":
+                vq, pf = sage.quantize(v, sage.E4M3, (0, 1)), sage.E4M3
+            else:
+                vq, pf = sage.QT(sage.BF16 if v.dtype == torch.bfloat16 else sage.FP16, v, None, tuple(v.shape)), sage.BF16
+                if variant == "thrift":
+                    mask = sage.thrift_select(q, ks, 0.05, causal)
+        elif variant == "mxfp4":
+            qq, kq = sage.quantize(q, sage.MXFP4, (1, 32)), sage.quantize(ks, sage.MXFP4, (1, 32))
+            vq, pf = sage.quantize(v, sage.MXFP4, (32, 1)), sage.MXFP4
+        else:
+            qq = sage.nvfp4_to_mxfp8(sage.quantize(q, sage.NVFP4, (1, 16), sage.SEARCH), False)
+            kq = sage.nvfp4_to_mxfp8(sage.quantize(ks, sage.NVFP4, (1, 16), sage.SEARCH), False)
+            vq = sage.nvfp4_to_mxfp8(sage.quantize(v, sage.NVFP4, (16, 1), sage.SEARCH), True)
+            pf = sage.NVFP4
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        out = sage.attn_fwd(qq, kq, vq, causal, pf, block_mask=mask,
+                            q_hi=q if mask is not None else None, k_hi=ks if mask is not None else None)
+        if record:
+            e1.record(stream)
+            ev.append((e0, e1))
+        return out
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+
+    achieved = ops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK[VARIANT_PEAK[variant]]
+    traffic = load_traffic(w.name, causal, variant)
+    rec = {
+        "metric": "quantized attention fwd TOPS (4*B*H*N^2*d/t) at d=128 N=4096 + % of MFMA peak",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": VARIANT_DTYPE[variant],
+        "data": "synthetic (seeded PCG64; shapes and value recipe of the workload)",
+        "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": w.Hkv, "N": N, "D": D, "causal": causal,
+                   "variant": variant, "input_dtype": str(w.dtype).replace("torch.", ""),
+                   "step": "smooth_k + quantize + " + ("thrift_select + " if variant == "thrift" else "") + "attn_fwd"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "attn_fwd", "kernel_ms": round(attn_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, variant, args.cpu_seconds)
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+// C ABI of libsage: argument validation on the host, then kernel launches on the
+// caller's stream.  No allocation, no synchronisation.
+#include "../../include/sage.h"
+#include "kernels.hpp"
+
+#include <math.h>
+#include <stdint.h>
+
+using namespace sage;
+
+namespace {
+
+constexpr int QBLK = 128, KBLK = 64;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool shape_ok(const sage_shape& s) { return s.B >= 0 && s.H >= 1 && s.N >= 0 && s.D >= 1 && s.B <= (1 << 20) && s.N <= (1ll << 31); }
+bool is16(sage_fmt f) { return f == SAGE_BF16 || f == SAGE_FP16; }
+int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int launched(hipError_t e) { return e == hipSuccess ? SAGE_OK : (e == hipErrorNotSupported ? SAGE_ENOTSUP : SAGE_EHIP); }
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_version(void) { return "sage-gfx950 0.1.0"; }
+
+const char* sage_strerror(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_EINVAL: return "invalid argument (null pointer, shape, or block not suited to the format)";
+    case SAGE_ENOTSUP: return "not supported (head dimension or format combination)";
+    case SAGE_EALIGN: return "pointer not 16-byte aligned";
+    case SAGE_EWORKSPACE: return "workspace missing or too small";
+    case SAGE_EHIP: return "HIP kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t sage_smooth_k_workspace_bytes(sage_shape ks) {
+  if (!shape_ok(ks)) return 0;
+  return (size_t)(ks.B * ks.H * ((ks.N + 63) / 64) * ks.D) * sizeof(float);
+}
+
+int sage_smooth_k(const void* k, sage_fmt dt, sage_shape ks, float* mean_out, void* k_smoothed_out, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  if (!k || !mean_out || !shape_ok(ks) || ks.D % 8 != 0) return SAGE_EINVAL;
+  if (!is16(dt)) return SAGE_ENOTSUP;
+  if (!aligned16(k) || !aligned16(mean_out) || (k_smoothed_out && !aligned16(k_smoothed_out))) return SAGE_EALIGN;
+  const size_t need = sage_smooth_k_workspace_bytes(ks);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
+  if (workspace && !aligned16(workspace)) return SAGE_EALIGN;
+  if (ks.B == 0) return SAGE_OK;
+  return launched(launch_smooth_k(k, dt == SAGE_FP16, ks.B * ks.H, ks.N, (int)ks.D, mean_out, k_smoothed_out,
+                                  (float*)workspace, stream));
+}
+
+int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* codes_bytes, size_t* scale_bytes) {
+  if (!codes_bytes || !scale_bytes || !shape_ok(xs)) return SAGE_EINVAL;
+  const int64_t BH = xs.B * xs.H, N = xs.N, D = xs.D;
+  const int64_t Np = roundup(N, 32);
+  switch (fmt) {
+    case SAGE_INT8:
+      if (block.tokens < 1 || block.channels != D) return SAGE_EINVAL;
+      *codes_bytes = (size_t)(BH * N * D);
+      *scale_bytes = (size_t)(BH * ((N + block.tokens - 1) / block.tokens)) * 4;
+      return SAGE_OK;
+    case SAGE_E4M3:
+      if (block.tokens != 0 || block.channels != 1) return SAGE_EINVAL;
+      *codes_bytes = (size_t)(BH * N * D);
+      *scale_bytes = (size_t)(BH * D) * 4;
+      return SAGE_OK;
+    case SAGE_MXFP4:
+    case SAGE_NVFP4: {
+      const int g = fmt == SAGE_MXFP4 ? 32 : 16;
+      if (block.tokens == 1 && block.channels == g) {
+        if (D % 32) return SAGE_EINVAL;
+        *codes_bytes = (size_t)(BH * N * D / 2);
+        *scale_bytes = (size_t)(BH * N * D / g);
+      } else if (block.tokens == g && block.channels == 1) {
+        *codes_bytes = (size_t)(BH * D * Np / 2);
+        *scale_bytes = (size_t)(BH * D * Np / g);
+      } else {
+        return SAGE_EINVAL;
+      }
+      return SAGE_OK;
+    }
+    default: return SAGE_ENOTSUP;
+  }
+}
+
+int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
+                         sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream) {
+  if (!x || !codes_out || !scales_out || !shape_ok(xs)) return SAGE_EINVAL;
+  if (!is16(in_dt)) return SAGE_ENOTSUP;
+  if (xs.D % 8 != 0) return SAGE_EINVAL;
+  size_t cb, sb;
+  int st = sage_quantized_bytes(fmt, block, xs, &cb, &sb);
+  if (st != SAGE_OK) return st;
+  if (mode != SAGE_SCALE_ABSMAX && fmt != SAGE_NVFP4) return SAGE_EINVAL;
+  if (mode != SAGE_SCALE_ABSMAX && mode != SAGE_SCALE_SEARCH && mode != SAGE_SCALE_SEARCH_OFFSETS) return SAGE_EINVAL;
+  if (!aligned16(x) || !aligned16(codes_out) || !aligned16(scales_out)) return SAGE_EALIGN;
+  if (fmt == SAGE_E4M3 && xs.D > 128) return SAGE_ENOTSUP;
+  if ((fmt == SAGE_MXFP4 || fmt == SAGE_NVFP4) && block.channels == 1 && xs.D > 128) return SAGE_ENOTSUP;
+  const int64_t BH = xs.B * xs.H;
+  if (BH == 0 || xs.N == 0) return SAGE_OK;
+  const bool f16 = in_dt == SAGE_FP16;
+  switch (fmt) {
+    case SAGE_INT8:
+      return launched(launch_quant_int8(x, f16, BH, xs.N, (int)xs.D, block.tokens, (int8_t*)codes_out,
+                                        (float*)scales_out, stream));
+    case SAGE_E4M3:
+      return launched(launch_quant_fp8_channel(x, f16, BH, xs.N, (int)xs.D, (uint8_t*)codes_out, (float*)scales_out,
+                                               stream));
+    default:
+      return launched(launch_quant_fp4(x, f16, BH, xs.N, (int)xs.D, fmt == SAGE_NVFP4, block.channels == 1 ? 1 : 0,
+                                       (int)mode, (uint8_t*)codes_out, (uint8_t*)scales_out, stream));
+  }
+}
+
+int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t len, void* f8_out,
+                        void* e8m0_out, hipStream_t stream) {
+  if (!codes || !scales || !f8_out || !e8m0_out || rows < 0 || len < 0 || len % 32) return SAGE_EINVAL;
+  if (!aligned16(codes) || !aligned16(f8_out)) return SAGE_EALIGN;
+  return launched(launch_nvfp4_to_mxfp8((const uint8_t*)codes, (const uint8_t*)scales, rows, len, (uint8_t*)f8_out,
+                                        (uint8_t*)e8m0_out, stream));
+}
+
+int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
+                  void* out, sage_fmt out_dt, hipStream_t stream) {
+  if (!q || !k || !v || !p || !out) return SAGE_EINVAL;
+  if (!q->codes || !k->codes || !v->codes) return SAGE_EINVAL;
+  const sage_shape &qs = q->shape, &ks = k->shape, &vs = v->shape;
+  if (!shape_ok(qs) || !shape_ok(ks) || !shape_ok(vs)) return SAGE_EINVAL;
+  if (ks.B != qs.B || vs.B != qs.B || ks.N != qs.N || vs.N != qs.N || ks.D != qs.D || vs.D != qs.D || vs.H != ks.H)
+    return SAGE_EINVAL;
+  if (qs.H % ks.H != 0) return SAGE_EINVAL;
+  if (qs.D != 64 && qs.D != 128) return SAGE_ENOTSUP;
+  if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
+  if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
+  if (p->causal != 0 && p->causal != 1) return SAGE_EINVAL;
+  if (!(p->sm_scale >= 0.0f) || isinf(p->sm_scale)) return SAGE_EINVAL;
+
+  AttnArgs a;
+  a.B = qs.B; a.Hq = qs.H; a.Hkv = ks.H; a.N = qs.N; a.D = (int)qs.D;
+  a.causal = p->causal;
+  a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / sqrtf((float)qs.D);
+  a.q_codes = q->codes; a.q_scales = q->scales;
+  a.k_codes = k->codes; a.k_scales = k->scales;
+  a.v_codes = v->codes; a.v_scales = v->scales;
+  a.v_is_f16 = v->fmt == SAGE_FP16;
+  a.mask = p->block_mask; a.q_hi = (const uint16_t*)p->q_hi; a.k_hi = (const uint16_t*)p->k_hi;
+  a.out = out; a.out_bf16 = out_dt == SAGE_BF16;
+
+  if (q->fmt == SAGE_INT8 && k->fmt == SAGE_INT8) {
+    if (!q->scales || !k->scales) return SAGE_EINVAL;
+    if (is16(v->fmt) && p->p_fmt == SAGE_BF16) {
+      if (p->block_mask) {
+        if (!p->q_hi || !p->k_hi || p->hi_dt != SAGE_BF16) return SAGE_EINVAL;
+        if (!aligned16(p->q_hi) || !aligned16(p->k_hi)) return SAGE_EALIGN;
+      }
+      if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
+      return launched(launch_attn_int8(a, 0, stream));
+    }
+    if (v->fmt == SAGE_E4M3 && p->p_fmt == SAGE_E4M3) {
+      if (!v->scales || p->block_mask) return SAGE_EINVAL;
+      if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
+      return launched(launch_attn_int8(a, 1, stream));
+    }
+    return SAGE_ENOTSUP;
+  }
+  if (p->block_mask) return SAGE_ENOTSUP;
+  if (q->fmt == SAGE_MXFP4 && k->fmt == SAGE_MXFP4 && v->fmt == SAGE_MXFP4 && p->p_fmt == SAGE_MXFP4) {
+    if (!q->scales || !k->scales || !v->scales) return SAGE_EINVAL;
+    if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
+    return launched(launch_attn_mx(a, 0, stream));
+  }
+  if (q->fmt == SAGE_MXFP8 && k->fmt == SAGE_MXFP8 && v->fmt == SAGE_MXFP8 && p->p_fmt == SAGE_NVFP4) {
+    if (!q->scales || !k->scales || !v->scales) return SAGE_EINVAL;
+    if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
+    return launched(launch_attn_mx(a, 1, stream));
+  }
+  return SAGE_ENOTSUP;
+}
+
+size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_block) {
+  if (!shape_ok(qs) || !shape_ok(ks) || q_block != QBLK || k_block != KBLK) return 0;
+  return thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
+}
+
+int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sage_shape qs, sage_shape ks,
+                         int q_block, int k_block, double frac, int causal, uint8_t* mask_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k_smoothed || !mask_out || !shape_ok(qs) || !shape_ok(ks)) return SAGE_EINVAL;
+  if (ks.B != qs.B || ks.N != qs.N || ks.D != qs.D || qs.H % ks.H != 0 || qs.D % 8 != 0) return SAGE_EINVAL;
+  if (dt != SAGE_BF16 || q_block != QBLK || k_block != KBLK) return SAGE_ENOTSUP;
+  if (!(frac >= 0.0 && frac <= 1.0) || (causal != 0 && causal != 1)) return SAGE_EINVAL;
+  if (!aligned16(q) || !aligned16(k_smoothed)) return SAGE_EALIGN;
+  const size_t need = thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
+  if (!workspace || workspace_bytes < need) return SAGE_EWORKSPACE;
+  if (!aligned16(workspace)) return SAGE_EALIGN;
+  if (qs.B == 0 || qs.N == 0) return SAGE_OK;
+  return launched(launch_thrift_select((const uint16_t*)q, (const uint16_t*)k_smoothed, qs.B, qs.H, ks.H, qs.N,
+                                       (int)qs.D, frac, causal, mask_out, workspace, stream));
+}
+
+int sage_convert_f32(const float* x, int64_t n, sage_fmt fmt, void* out, hipStream_t stream) {
+  if (!x || !out || n < 0) return SAGE_EINVAL;
+  if (fmt != SAGE_BF16 && fmt != SAGE_FP16 && fmt != SAGE_E4M3 && fmt != SAGE_MXFP4 && fmt != SAGE_NVFP4)
+    return SAGE_ENOTSUP;
+  return launched(launch_convert_f32(x, n, (int)fmt, out, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,48 @@
+// Internal launchers shared between the kernel translation units and the C-ABI layer.
+// Arguments are validated by the C-ABI layer before any launcher is called.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+// K smoothing (three kernels: per-run partial sums, per-channel mean, subtract+round).
+hipError_t launch_smooth_k(const void* k, bool is_f16, int64_t BH, int64_t N, int D, float* mean, void* ks,
+                           float* partials, hipStream_t st);
+
+// Block quantizers.
+hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, int8_t* codes,
+                             float* scales, hipStream_t st);
+hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int64_t N, int D, uint8_t* codes_t,
+                                    float* scales, hipStream_t st);
+hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
+                            int mode, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len,
+                                 uint8_t* f8, uint8_t* e8, hipStream_t st);
+hipError_t launch_convert_f32(const float* x, int64_t n, int fmt, void* out, hipStream_t st);
+
+// Thrift block selection.
+hipError_t launch_thrift_select(const uint16_t* q, const uint16_t* ks, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
+                                int D, double frac, int causal, uint8_t* mask, void* ws, hipStream_t st);
+size_t thrift_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int D);
+
+// Attention kernels.
+struct AttnArgs {
+  int64_t B, Hq, Hkv, N;
+  int D;
+  int causal;
+  float sm_scale;
+  // INT8 / MX codes and scales
+  const void* q_codes; const void* q_scales;
+  const void* k_codes; const void* k_scales;
+  const void* v_codes; const void* v_scales;   // v_codes = 16-bit V for the bf16/fp16 P.V path
+  int v_is_f16;
+  // Thrift
+  const uint8_t* mask; const uint16_t* q_hi; const uint16_t* k_hi;
+  void* out;
+  int out_bf16;
+};
+hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st);
+hipError_t launch_attn_mx(const AttnArgs& a, int nvfp4_variant, hipStream_t st);
+
+}  // namespace sage

@@ -1,0 +1,392 @@
+// Block quantizers.
+//  * INT8 per block (SageAttention, Technical approach: Q and K in 8 bits): s = amax / 127,
+//    code = clamp(round_half_even(x * (1/s)), -127, 127).  Two passes over the block (the
+//    second read hits L2), 3 bytes of HBM per 16-bit element.
+//  * E4M3 per channel for V: amax over all tokens (atomic max on the bit pattern of a
+//    non-negative float), then codes written channel-major through an LDS transpose.
+//  * MX-FP4 (SageAttention3's microscaled FP4): E8M0 per 32 elements, e = smallest integer
+//    with 6 * 2^e >= amax, codes E2M1(x * 2^-e).
+//  * NVFP4 with max-scaling or ScaleSearch ("Search Your Block Floating Point Scales!",
+//    Method > ScaleSearch): per 16 elements, the UE4M3 scale among the candidates whose
+//    E2M1 reconstruction has the least squared error (fp32, balanced index-order tree, first
+//    strictly smaller wins, the max-scaling candidate first).  This one is ALU-bound: about
+//    nine candidates x ten operations per element.
+//  * NVFP4 -> MXFP8 for the FP8 matrix-core path.
+// Compiled with -ffp-contract=off: every expression rounds as written.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace sage {
+namespace {
+
+// ------------------------------------------------------------------ INT8 per block
+template <bool F16>
+__global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int T,
+                                                         int8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t nblk = (N + T - 1) / T;
+  const int64_t blk = blockIdx.x, bh = blockIdx.y;
+  const int64_t t0 = blk * T;
+  const int rows = (int)((N - t0) < T ? (N - t0) : T);
+  const int nchunk = rows * D / 8;
+  const uint16_t* base = x + (bh * N + t0) * D;
+  float amax = 0.0f;
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    v4i raw = *(const v4i*)(base + (int64_t)c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t u = (uint32_t)raw[w];
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u & 0xffffu))));
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u >> 16))));
+    }
+  }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  const float r = s > 0.0f ? 1.0f / s : 0.0f;
+  if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
+  int8_t* out = codes + (bh * N + t0) * D;
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    v4i raw = *(const v4i*)(base + (int64_t)c * 8);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t h = (uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1)));
+      float q = __builtin_rintf(in16_to_f32<F16>(h) * r);
+      q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+      packed[e >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (e & 3));
+    }
+    *(v2i*)(out + (int64_t)c * 8) = v2i{(int)packed[0], (int)packed[1]};
+  }
+}
+
+// ------------------------------------------------------------------ E4M3 per channel
+__global__ void fill_u32(uint32_t* p, int64_t n, uint32_t v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __restrict__ x, int64_t BH, int64_t N, int D,
+                                                           uint32_t* __restrict__ amax_bits) {
+  // thread: (bh, run of 64 tokens, 8 channels)
+  const int64_t nrun = (N + 63) / 64;
+  const int cg = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= BH * nrun * cg) return;
+  const int c8 = (int)(gid % cg);
+  const int64_t run = (gid / cg) % nrun, bh = gid / cg / nrun;
+  const int64_t t0 = run * 64;
+  const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
+  const uint16_t* p = x + (bh * N + t0) * D + c8 * 8;
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = 0; t < rows; ++t) {
+    v4i raw = *(const v4i*)(p + (int64_t)t * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))))));
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) atomicMax(amax_bits + bh * D + c8 * 8 + e, __float_as_uint(m[e]));
+}
+
+__global__ void channel_scale_kernel(uint32_t* sc, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) sc[i] = __float_as_uint(__uint_as_float(sc[i]) / 448.0f);
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* __restrict__ x, int64_t N, int D,
+                                                                const float* __restrict__ scales,
+                                                                uint8_t* __restrict__ codes_t) {
+  // block: (64-token run, bh); LDS tile [D][64] bytes, written transposed, stored as rows.
+  __shared__ uint8_t tile[128 * 80];
+  constexpr int PITCH = 80;
+  const int64_t run = blockIdx.x, bh = blockIdx.y;
+  const int64_t t0 = run * 64;
+  const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
+  const float* sc = scales + bh * D;
+  const int nchunk = 64 * D / 8;
+  for (int c = threadIdx.x; c < nchunk; c += 256) {
+    const int t = c / (D / 8), c8 = (c % (D / 8)) * 8;
+    if (t >= rows) continue;
+    v4i raw = *(const v4i*)(x + (bh * N + t0 + t) * D + c8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float s = sc[c8 + e];
+      float r = s > 0.0f ? 1.0f / s : 0.0f;
+      float v = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
+      tile[(c8 + e) * PITCH + t] = f32_to_e4m3(v * r);
+    }
+  }
+  __syncthreads();
+  // each thread stores 4 bytes of one channel row
+  for (int c = threadIdx.x; c < D * 16; c += 256) {
+    const int ch = c / 16, t4 = (c % 16) * 4;
+    uint8_t* dst = codes_t + (bh * D + ch) * N + t0 + t4;
+    if (t4 + 4 <= rows && ((N & 3) == 0)) {
+      *(uint32_t*)dst = *(const uint32_t*)&tile[ch * PITCH + t4];
+    } else {
+      for (int j = 0; j < 4 && t4 + j < rows; ++j) dst[j] = tile[ch * PITCH + t4 + j];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ FP4 (MX and NV)
+// Squared error of an NVFP4 candidate scale code over 16 values; codes written to c[0..1].
+__device__ __forceinline__ float nv_candidate(const float* v, uint32_t scode, uint32_t* c) {
+  const float s = e4m3_to_f32(scode);
+  const float r = 1.0f / s;
+  float se[16];
+  c[0] = c[1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    uint32_t two = f32x2_to_e2m1(v[i] * r, v[i + 1] * r);
+    c[i >> 3] |= two << (4 * (i & 7));
+    float x0 = e2m1_to_f32(two & 15u) * s, x1 = e2m1_to_f32(two >> 4) * s;
+    float e0 = v[i] - x0, e1 = v[i + 1] - x1;
+    se[i] = e0 * e0;
+    se[i + 1] = e1 * e1;
+  }
+#pragma unroll
+  for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * w) se[i] = se[i] + se[i + w];
+  return se[0];
+}
+
+// NVFP4 scale choice for one 16-value group (mode 0 max-scaling, 1 grid search, 2 offsets).
+__device__ __forceinline__ uint32_t nv_quant16(const float* v, int mode, uint32_t* codes) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  const float smax = amax / 6.0f;
+  uint32_t c0 = f32_to_e4m3(smax);
+  if (c0 == 0) c0 = 1;
+  uint32_t best_c = c0;
+  float best = nv_candidate(v, c0, codes);
+  if (mode == 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float g = (float)(0.85 + k * 0.3 / 7.0);
+      uint32_t ck = f32_to_e4m3(smax * g);
+      if (ck == 0) ck = 1;
+      uint32_t cc[2];
+      float sse = nv_candidate(v, ck, cc);
+      if (sse < best) { best = sse; best_c = ck; codes[0] = cc[0]; codes[1] = cc[1]; }
+    }
+  } else if (mode == 2) {
+    const int offs[8] = {-2, -1, 1, 2, 3, 4, 5, 6};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      int ck = (int)c0 + offs[k];
+      if (ck < 1 || ck > 0x7e) continue;
+      uint32_t cc[2];
+      float sse = nv_candidate(v, (uint32_t)ck, cc);
+      if (sse < best) { best = sse; best_c = (uint32_t)ck; codes[0] = cc[0]; codes[1] = cc[1]; }
+    }
+  }
+  return best_c;
+}
+
+// MX-FP4 of one 32-value group: returns the E8M0 byte, codes in c[0..3].
+__device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* c) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[i]));
+  const int e = mx_exp_e2m1(amax);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) c[w] = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; i += 2)
+    c[i >> 3] |= f32x2_to_e2m1(__builtin_ldexpf(v[i], -e), __builtin_ldexpf(v[i + 1], -e)) << (4 * (i & 7));
+  return (uint32_t)(e + 127);
+}
+
+// Along D: one thread per group (32 values for MX, 16 for NV) of one token row.
+template <bool F16, bool NV>
+__global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int D, int mode,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int G = NV ? 16 : 32;
+  const int gpr = D / G;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * gpr) return;
+  const uint16_t* p = x + gid * G;
+  float v[G];
+#pragma unroll
+  for (int q = 0; q < G / 8; ++q) {
+    v4i raw = *(const v4i*)(p + q * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[q * 8 + e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
+  }
+  if (NV) {
+    uint32_t c[2];
+    scales[gid] = (uint8_t)nv_quant16(v, mode, c);
+    *(v2i*)(codes + gid * 8) = v2i{(int)c[0], (int)c[1]};
+  } else {
+    uint32_t c[4];
+    scales[gid] = (uint8_t)mx_quant32(v, c);
+    *(v4i*)(codes + gid * 16) = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+  }
+}
+
+// Along tokens (V): block = (64-token run, bh); LDS tile [64][D] of fp32; thread per
+// (channel, group of G tokens).  Output rows are channels, Np = N rounded up to 32.
+template <bool F16, bool NV>
+__global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int mode,
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int G = NV ? 16 : 32;
+  __shared__ float tile[64][129];
+  const int64_t run = blockIdx.x, bh = blockIdx.y;
+  const int64_t t0 = run * 64;
+  const int64_t Np = (N + 31) / 32 * 32;
+  const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
+  for (int c = threadIdx.x; c < 64 * D / 8; c += 256) {
+    const int t = c / (D / 8), c8 = (c % (D / 8)) * 8;
+    if (t < rows) {
+      v4i raw = *(const v4i*)(x + (bh * N + t0 + t) * D + c8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[t][c8 + e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[t][c8 + e] = 0.0f;
+    }
+  }
+  __syncthreads();
+  const int groups = 64 / G;
+  const int tmax = (int)((Np - t0) < 64 ? (Np - t0) : 64);   // tokens of this run inside Np
+  for (int w = threadIdx.x; w < D * groups; w += 256) {
+    const int ch = w % D, g = w / D;
+    if (g * G >= tmax) continue;
+    float v[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) v[i] = tile[g * G + i][ch];
+    const int64_t tok = t0 + g * G;
+    if (NV) {
+      uint32_t c[2];
+      scales[(bh * D + ch) * (Np / 16) + tok / 16] = (uint8_t)nv_quant16(v, mode, c);
+      *(v2i*)(codes + (bh * D + ch) * (Np / 2) + tok / 2) = v2i{(int)c[0], (int)c[1]};
+    } else {
+      uint32_t c[4];
+      scales[(bh * D + ch) * (Np / 32) + tok / 32] = (uint8_t)mx_quant32(v, c);
+      *(v4i*)(codes + (bh * D + ch) * (Np / 2) + tok / 2) = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    }
+  }
+}
+
+// ------------------------------------------------------------------ NVFP4 -> MXFP8
+__global__ __launch_bounds__(256) void nv_to_mx8_kernel(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales, int64_t groups,
+                                                        uint8_t* __restrict__ f8, uint8_t* __restrict__ e8) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one 32-element group
+  if (gid >= groups) return;
+  v4i raw = *(const v4i*)(codes + gid * 16);
+  const float s0 = e4m3_to_f32(scales[gid * 2]), s1 = e4m3_to_f32(scales[gid * 2 + 1]);
+  float xh[32];
+  float A = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    uint32_t c = ((uint32_t)raw[i >> 3] >> (4 * (i & 7))) & 15u;
+    xh[i] = e2m1_to_f32(c) * (i < 16 ? s0 : s1);
+    A = __builtin_fmaxf(A, __builtin_fabsf(xh[i]));
+  }
+  const int E = mx_exp_e4m3(A);
+  e8[gid] = (uint8_t)(E + 127);
+  v8i out;
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    out[w] = (int)f32x4_to_e4m3(__builtin_ldexpf(xh[4 * w], -E), __builtin_ldexpf(xh[4 * w + 1], -E),
+                                __builtin_ldexpf(xh[4 * w + 2], -E), __builtin_ldexpf(xh[4 * w + 3], -E));
+  *(v8i*)(f8 + gid * 32) = out;
+}
+
+// ------------------------------------------------------------------ conversions (verification)
+__global__ void convert_kernel(const float* __restrict__ x, int64_t n, int fmt, void* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = x[i];
+  switch (fmt) {
+    case 0: ((uint16_t*)out)[i] = f32_to_bf16(v); break;
+    case 1: ((uint16_t*)out)[i] = f32_to_f16(v); break;
+    case 4: ((uint8_t*)out)[i] = f32_to_e4m3(v); break;
+    default: ((uint8_t*)out)[i] = (uint8_t)(f32x2_to_e2m1(v, 0.0f) & 15u); break;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, int8_t* codes,
+                             float* scales, hipStream_t st) {
+  const int64_t nblk = (N + T - 1) / T;
+  if (nblk == 0 || BH == 0) return hipSuccess;
+  dim3 g((unsigned)nblk, (unsigned)BH);
+  if (is_f16) quant_int8_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+  else quant_int8_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int64_t N, int D, uint8_t* codes_t,
+                                    float* scales, hipStream_t st) {
+  const int64_t ns = BH * D;
+  fill_u32<<<(unsigned)((ns + 255) / 256), 256, 0, st>>>((uint32_t*)scales, ns, 0u);
+  const int64_t nrun = (N + 63) / 64;
+  const int64_t t1 = BH * nrun * (D / 8);
+  if (t1 > 0) {
+    if (is_f16) channel_amax_kernel<true><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, BH, N, D, (uint32_t*)scales);
+    else channel_amax_kernel<false><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, BH, N, D, (uint32_t*)scales);
+  }
+  channel_scale_kernel<<<(unsigned)((ns + 255) / 256), 256, 0, st>>>((uint32_t*)scales, ns);
+  if (nrun > 0) {
+    dim3 g((unsigned)nrun, (unsigned)BH);
+    if (is_f16) fp8_channel_codes_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, scales, codes_t);
+    else fp8_channel_codes_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, scales, codes_t);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
+                            int mode, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const uint16_t* xs = (const uint16_t*)x;
+  if (!along_tokens) {
+    const int64_t groups = BH * N * (D / (nv ? 16 : 32));
+    if (groups == 0) return hipSuccess;
+    const unsigned g = (unsigned)((groups + 255) / 256);
+    if (nv) {
+      if (is_f16) fp4_rows_kernel<true, true><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
+      else fp4_rows_kernel<false, true><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
+    } else {
+      if (is_f16) fp4_rows_kernel<true, false><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
+      else fp4_rows_kernel<false, false><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
+    }
+  } else {
+    const int64_t nrun = (N + 63) / 64;
+    if (nrun == 0 || BH == 0) return hipSuccess;
+    dim3 g((unsigned)nrun, (unsigned)BH);
+    if (nv) {
+      if (is_f16) fp4_cols_kernel<true, true><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
+      else fp4_cols_kernel<false, true><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
+    } else {
+      if (is_f16) fp4_cols_kernel<true, false><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
+      else fp4_cols_kernel<false, false><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len,
+                                 uint8_t* f8, uint8_t* e8, hipStream_t st) {
+  const int64_t groups = rows * (len / 32);
+  if (groups == 0) return hipSuccess;
+  nv_to_mx8_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, st>>>(codes, scales, groups, f8, e8);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_f32(const float* x, int64_t n, int fmt, void* out, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  convert_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(x, n, fmt, out);
+  return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,101 @@
+// K smoothing — "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+// Acceleration" (Contributions / Technical approach): K's channel-wise outliers are removed
+// before 8-bit quantization by subtracting each channel's mean over the tokens.
+//
+// HBM-bound, 6 bytes per element for 16-bit K (read K twice, write K_s once):
+//   1. smooth_partial: fp32 running sum over each run of 64 tokens, in token order, for 8
+//      channels per thread (one 16-byte load per token row) -> partials [BH, runs, D].
+//   2. smooth_mean:    per (bh, channel) running sum of the partials in run order, / N.
+//   3. smooth_apply:   K_s = round_to_dtype(fp32(k - mean)), 8 elements per thread.
+// The fixed summation order makes the mean reproducible bit for bit.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace sage {
+namespace {
+
+constexpr int RUN = 64;
+
+template <bool F16>
+__global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict__ k, int64_t BH, int64_t N, int D,
+                                                      float* __restrict__ part) {
+  const int64_t nrun = (N + RUN - 1) / RUN;
+  const int cg = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= BH * nrun * cg) return;
+  const int c8 = (int)(gid % cg);
+  const int64_t run = (gid / cg) % nrun, bh = gid / cg / nrun;
+  const int64_t t0 = run * RUN;
+  const int rows = (int)((N - t0) < RUN ? (N - t0) : RUN);
+  const uint16_t* p = k + (bh * N + t0) * D + c8 * 8;
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = 0; t < rows; ++t) {
+    v4i raw = *(const v4i*)(p + (int64_t)t * D);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t h = (uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1)));
+      s[e] = s[e] + in16_to_f32<F16>(h);
+    }
+  }
+  float* o = part + (bh * nrun + run) * D + c8 * 8;
+  *(v4f*)o = v4f{s[0], s[1], s[2], s[3]};
+  *(v4f*)(o + 4) = v4f{s[4], s[5], s[6], s[7]};
+}
+
+__global__ __launch_bounds__(256) void smooth_mean(const float* __restrict__ part, int64_t BH, int64_t N, int D,
+                                                   float* __restrict__ mean) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= BH * D) return;
+  const int64_t nrun = (N + RUN - 1) / RUN;
+  const int64_t bh = gid / D, c = gid % D;
+  const float* p = part + bh * nrun * D + c;
+  float total = 0.0f;
+  for (int64_t r = 0; r < nrun; ++r) total = total + p[r * D];
+  mean[gid] = N > 0 ? total / (float)N : 0.0f;
+}
+
+template <bool F16>
+__global__ __launch_bounds__(256) void smooth_apply(const uint16_t* __restrict__ k, const float* __restrict__ mean,
+                                                    int64_t BH, int64_t N, int D, uint16_t* __restrict__ ks) {
+  const int64_t n8 = BH * N * D / 8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = i * 8;
+    const int64_t bh = e0 / (N * D);
+    const int c0 = (int)(e0 % D);
+    v4i raw = *(const v4i*)(k + e0);
+    const float* mu = mean + bh * D + c0;
+    v4i outv;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t u = (uint32_t)raw[w];
+      float a = in16_to_f32<F16>((uint16_t)(u & 0xffffu)) - mu[2 * w];
+      float b = in16_to_f32<F16>((uint16_t)(u >> 16)) - mu[2 * w + 1];
+      outv[w] = (int)((uint32_t)f32_to_in16<F16>(a) | ((uint32_t)f32_to_in16<F16>(b) << 16));
+    }
+    *(v4i*)(ks + e0) = outv;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_smooth_k(const void* k, bool is_f16, int64_t BH, int64_t N, int D, float* mean, void* ks,
+                           float* partials, hipStream_t st) {
+  const int64_t nrun = (N + RUN - 1) / RUN;
+  const int64_t t1 = BH * nrun * (D / 8);
+  if (t1 > 0) {
+    dim3 g((unsigned)((t1 + 255) / 256));
+    if (is_f16) smooth_partial<true><<<g, 256, 0, st>>>((const uint16_t*)k, BH, N, D, partials);
+    else smooth_partial<false><<<g, 256, 0, st>>>((const uint16_t*)k, BH, N, D, partials);
+  }
+  smooth_mean<<<(unsigned)((BH * D + 255) / 256), 256, 0, st>>>(partials, BH, N, D, mean);
+  if (ks && BH * N > 0) {
+    int64_t n8 = BH * N * D / 8;
+    int64_t blocks = (n8 + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (is_f16) smooth_apply<true><<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)k, mean, BH, N, D, (uint16_t*)ks);
+    else smooth_apply<false><<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)k, mean, BH, N, D, (uint16_t*)ks);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sage

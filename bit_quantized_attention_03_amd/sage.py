@@ -1,0 +1,253 @@
+"""ctypes binding of libsage.so (the gfx950 HIP library).  Marshalling only.
+
+Every function takes torch tensors that already live on the GPU, allocates its outputs with
+torch (device memory and the current stream are all torch is used for), and calls the C ABI
+of the same name.  There is no CPU path: if the library is missing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage.so")
+
+BF16, FP16, FP32, INT8, E4M3, MXFP4, NVFP4, MXFP8 = range(8)
+ABSMAX, SEARCH, SEARCH_OFFSETS = 0, 1, 2
+_TORCH_FMT = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
+
+
+class Shape(C.Structure):
+    _fields_ = [("B", C.c_int64), ("H", C.c_int64), ("N", C.c_int64), ("D", C.c_int64)]
+
+
+class Block(C.Structure):
+    _fields_ = [("tokens", C.c_int32), ("channels", C.c_int32)]
+
+
+class QTensorC(C.Structure):
+    _fields_ = [("fmt", C.c_int), ("codes", C.c_void_p), ("scales", C.c_void_p), ("shape", Shape)]
+
+
+class AttnParamsC(C.Structure):
+    _fields_ = [("causal", C.c_int32), ("sm_scale", C.c_float), ("p_fmt", C.c_int),
+                ("block_mask", C.c_void_p), ("q_hi", C.c_void_p), ("k_hi", C.c_void_p), ("hi_dt", C.c_int)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libsage.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_quantized_attention_03_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        L.sage_version.restype = C.c_char_p
+        L.sage_strerror.restype = C.c_char_p
+        L.sage_strerror.argtypes = [C.c_int]
+        L.sage_smooth_k_workspace_bytes.restype = C.c_size_t
+        L.sage_smooth_k_workspace_bytes.argtypes = [Shape]
+        L.sage_smooth_k.argtypes = [C.c_void_p, C.c_int, Shape, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        L.sage_quantize_blocks.argtypes = [C.c_void_p, C.c_int, Shape, C.c_int, Block, C.c_int, C.c_void_p, C.c_void_p,
+                                           C.c_void_p]
+        L.sage_quantized_bytes.argtypes = [C.c_int, Block, Shape, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
+        L.sage_nvfp4_to_mxfp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
+                                          C.c_void_p]
+        L.sage_attn_fwd.argtypes = [C.POINTER(QTensorC), C.POINTER(QTensorC), C.POINTER(QTensorC),
+                                    C.POINTER(AttnParamsC), C.c_void_p, C.c_int, C.c_void_p]
+        L.thrift_select_blocks.argtypes = [C.c_void_p, C.c_void_p, C.c_int, Shape, Shape, C.c_int, C.c_int, C.c_double,
+                                           C.c_int, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        L.thrift_workspace_bytes.restype = C.c_size_t
+        L.thrift_workspace_bytes.argtypes = [Shape, Shape, C.c_int, C.c_int]
+        L.sage_convert_f32.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+        _lib = L
+    return _lib
+
+
+def version() -> str:
+    return lib().sage_version().decode()
+
+
+class SageError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {lib().sage_strerror(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SageError(fn, status)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _shape(t: torch.Tensor) -> Shape:
+    B, H, N, D = t.shape
+    return Shape(B, H, N, D)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+# ------------------------------------------------------------------------------------ steps
+def smooth_k(k: torch.Tensor, want_smoothed: bool = True):
+    """K smoothing: returns (mean [B,H,D] fp32, K_s like k or None)."""
+    _dev(k)
+    B, H, N, D = k.shape
+    mean = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
+    ks = torch.empty_like(k) if want_smoothed else None
+    shp = _shape(k)
+    ws = torch.empty(max(1, lib().sage_smooth_k_workspace_bytes(shp)), dtype=torch.uint8, device=k.device)
+    _check("sage_smooth_k", lib().sage_smooth_k(_ptr(k), _TORCH_FMT[k.dtype], shp, _ptr(mean), _ptr(ks), _ptr(ws),
+                                                ws.numel(), _stream()))
+    return mean, ks
+
+
+def quantized_bytes(fmt: int, block: tuple, shape: tuple):
+    cb, sb = C.c_size_t(), C.c_size_t()
+    _check("sage_quantized_bytes", lib().sage_quantized_bytes(fmt, Block(*block), Shape(*shape), C.byref(cb), C.byref(sb)))
+    return cb.value, sb.value
+
+
+@dataclass
+class QT:
+    """A quantized operand: format, code and scale tensors, logical [B,H,N,D] shape."""
+    fmt: int
+    codes: torch.Tensor
+    scales: Optional[torch.Tensor]
+    shape: tuple
+
+    def c(self) -> QTensorC:
+        return QTensorC(self.fmt, _ptr(self.codes), _ptr(self.scales), Shape(*self.shape))
+
+
+def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
+    """Block quantization (layouts as in sage.h); returns a QT with flat code/scale buffers."""
+    _dev(x)
+    cb, sb = quantized_bytes(fmt, block, tuple(x.shape))
+    codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)
+    _check("sage_quantize_blocks", lib().sage_quantize_blocks(_ptr(x), _TORCH_FMT[x.dtype], _shape(x), fmt,
+                                                              Block(*block), mode, _ptr(codes), _ptr(scales), _stream()))
+    return QT(fmt, codes[:cb], scales[:sb], tuple(x.shape))
+
+
+def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
+    B, H, N, D = qt.shape
+    Np = (N + 31) // 32 * 32
+    rows, length = (B * H * D, Np) if along_tokens else (B * H * N, D)
+    f8 = torch.empty(max(rows * length, 16), dtype=torch.uint8, device=qt.codes.device)
+    e8 = torch.empty(max(rows * length // 32, 16), dtype=torch.uint8, device=qt.codes.device)
+    _check("sage_nvfp4_to_mxfp8", lib().sage_nvfp4_to_mxfp8(_ptr(qt.codes), _ptr(qt.scales), rows, length, _ptr(f8),
+                                                            _ptr(e8), _stream()))
+    return QT(MXFP8, f8[:rows * length], e8[:rows * length // 32], qt.shape)
+
+
+def attn_fwd(q: QT, k: QT, v: QT, causal: bool, p_fmt: int, sm_scale: float = 0.0,
+             block_mask: Optional[torch.Tensor] = None, q_hi: Optional[torch.Tensor] = None,
+             k_hi: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    B, Hq, N, D = q.shape
+    dev = q.codes.device
+    if out is None:
+        out = torch.empty((B, Hq, N, D), dtype=out_dtype, device=dev)
+    params = AttnParamsC(int(causal), float(sm_scale), p_fmt, _ptr(block_mask), _ptr(q_hi), _ptr(k_hi), BF16)
+    qc, kc, vc = q.c(), k.c(), v.c()
+    _check("sage_attn_fwd", lib().sage_attn_fwd(C.byref(qc), C.byref(kc), C.byref(vc), C.byref(params), _ptr(out),
+                                                _TORCH_FMT[out.dtype], _stream()))
+    return out
+
+
+def thrift_select(q: torch.Tensor, k_smoothed: torch.Tensor, frac: float, causal: bool,
+                  q_block: int = 128, k_block: int = 64) -> torch.Tensor:
+    _dev(q, k_smoothed)
+    B, Hq, N, D = q.shape
+    nQB, nKB = (N + q_block - 1) // q_block, (N + k_block - 1) // k_block
+    mask = torch.empty((B, Hq, nQB, nKB), dtype=torch.uint8, device=q.device)
+    wsb = lib().thrift_workspace_bytes(_shape(q), _shape(k_smoothed), q_block, k_block)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    _check("thrift_select_blocks", lib().thrift_select_blocks(_ptr(q), _ptr(k_smoothed), _TORCH_FMT[q.dtype], _shape(q),
+                                                              _shape(k_smoothed), q_block, k_block, float(frac),
+                                                              int(causal), _ptr(mask), _ptr(ws), ws.numel(), _stream()))
+    return mask
+
+
+def convert_f32(x: torch.Tensor, fmt: int) -> torch.Tensor:
+    _dev(x)
+    out = torch.empty(x.numel(), dtype=torch.int16 if fmt in (BF16, FP16) else torch.uint8, device=x.device)
+    _check("sage_convert_f32", lib().sage_convert_f32(_ptr(x), x.numel(), fmt, _ptr(out), _stream()))
+    return out
+
+
+# ------------------------------------------------------------------------------------ whole pass
+VARIANTS = ("int8", "int8_fp8pv", "mxfp4", "nvfp4_search", "thrift")
+
+
+@dataclass
+class Pass:
+    """Intermediate tensors of one forward pass (kept for parity checks)."""
+    mean: torch.Tensor
+    k_smoothed: torch.Tensor
+    q: QT
+    k: QT
+    v: QT
+    mask: Optional[torch.Tensor]
+    out: torch.Tensor
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str = "int8",
+            sm_scale: float = 0.0, thrift_frac: float = 0.05, search_mode: int = SEARCH,
+            out_dtype: torch.dtype = torch.float32) -> Pass:
+    """K smoothing -> block quantization -> (Thrift selection) -> fused attention."""
+    B, Hq, N, D = q.shape
+    mean, ks = smooth_k(k)
+    mask = None
+    if variant in ("int8", "int8_fp8pv", "thrift"):
+        qq = quantize(q, INT8, (128, D))
+        kq = quantize(ks, INT8, (64, D))
+        if variant == "int8_fp8pv":
+            vq = quantize(v, E4M3, (0, 1))
+            out = attn_fwd(qq, kq, vq, causal, E4M3, sm_scale, out_dtype=out_dtype)
+        else:
+            vq = QT(_TORCH_FMT[v.dtype], v, None, tuple(v.shape))
+            if variant == "thrift":
+                mask = thrift_select(q, ks, thrift_frac, causal)
+                out = attn_fwd(qq, kq, vq, causal, BF16, sm_scale, block_mask=mask, q_hi=q, k_hi=ks,
+                               out_dtype=out_dtype)
+            else:
+                out = attn_fwd(qq, kq, vq, causal, BF16, sm_scale, out_dtype=out_dtype)
+    elif variant == "mxfp4":
+        qq = quantize(q, MXFP4, (1, 32))
+        kq = quantize(ks, MXFP4, (1, 32))
+        vq = quantize(v, MXFP4, (32, 1))
+        out = attn_fwd(qq, kq, vq, causal, MXFP4, sm_scale, out_dtype=out_dtype)
+    elif variant == "nvfp4_search":
+        qq = nvfp4_to_mxfp8(quantize(q, NVFP4, (1, 16), search_mode), False)
+        kq = nvfp4_to_mxfp8(quantize(ks, NVFP4, (1, 16), search_mode), False)
+        vq = nvfp4_to_mxfp8(quantize(v, NVFP4, (16, 1), search_mode), True)
+        out = attn_fwd(qq, kq, vq, causal, NVFP4, sm_scale, out_dtype=out_dtype)
+    else:
+        raise ValueError(f"unknown variant {variant!r}; one of {VARIANTS}")
+    return Pass(mean, ks, qq, kq, vq, mask, out)
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False, variant: str = "int8",
+              **kw) -> torch.Tensor:
+    """Drop-in quantized attention: [B,Hq,N,D] x [B,Hkv,N,D] x [B,Hkv,N,D] -> [B,Hq,N,D]."""
+    return forward(q, k, v, causal, variant, **kw).out

@@ -1,0 +1,179 @@
+/*
+ * sage.h — C ABI of the MI355X (gfx950) quantized attention forward library (libsage.so).
+ *
+ * The calls split the quantized attention forward pass of the SageAttention family into
+ * its steps: K smoothing, block quantization (INT8, FP8-E4M3, MX-FP4, NVFP4 with
+ * max-scaling or ScaleSearch), an NVFP4 -> FP8 dequantization pass, Thrift block
+ * selection, and the fused attention (low-bit QK^T, block-scale dequantization, fp32
+ * online softmax, P.V on bf16 / FP8 / FP4 matrix cores).
+ *
+ * Conventions (all calls):
+ *  - Every pointer argument is a DEVICE pointer unless stated otherwise; the caller
+ *    allocates and owns every buffer.  The library never allocates, frees or synchronises:
+ *    it validates on the host, enqueues kernels on `stream` and returns.
+ *  - Tensors are contiguous, row-major [B, H, N, D] (D contiguous) unless a layout below
+ *    says otherwise.  Base pointers must be 16-byte aligned.
+ *  - Return value 0 = success; negative = error (SAGE_E*).  Validation happens before any
+ *    launch, so on a validation error no output has been touched.  SAGE_EHIP reports a
+ *    failed launch (hipGetLastError after the enqueue).
+ *  - Calls are stateless and thread-safe; calls on different streams may overlap.
+ *  - NaN / Inf inputs are outside the contract.
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_OK 0
+#define SAGE_EINVAL (-1)     /* null pointer, bad shape, block that does not suit the format */
+#define SAGE_ENOTSUP (-2)    /* D not in {64, 128}, or a format combination that is not built */
+#define SAGE_EALIGN (-3)     /* a base pointer that is not 16-byte aligned */
+#define SAGE_EWORKSPACE (-4) /* workspace missing or smaller than the size query returns */
+#define SAGE_EHIP (-5)       /* kernel launch failed */
+
+typedef enum {
+  SAGE_BF16 = 0,   /* bfloat16 */
+  SAGE_FP16 = 1,   /* IEEE binary16 */
+  SAGE_FP32 = 2,   /* IEEE binary32 */
+  SAGE_INT8 = 3,   /* int8 codes in [-127, 127] with an fp32 scale per block */
+  SAGE_E4M3 = 4,   /* OCP FP8 E4M3 ("FN": max 448, no inf) with an fp32 scale per channel */
+  SAGE_MXFP4 = 5,  /* E2M1 codes, two per byte, one E8M0 scale byte per 32 elements */
+  SAGE_NVFP4 = 6,  /* E2M1 codes, two per byte, one UE4M3 scale byte per 16 elements */
+  SAGE_MXFP8 = 7   /* E4M3 codes, one per byte, one E8M0 scale byte per 32 elements */
+} sage_fmt;
+
+typedef enum {
+  SAGE_SCALE_ABSMAX = 0,         /* max-scaling: the block maximum fits the format's range */
+  SAGE_SCALE_SEARCH = 1,         /* ScaleSearch over max-scale x {0.85 .. 1.15} (8 steps) */
+  SAGE_SCALE_SEARCH_OFFSETS = 2  /* ScaleSearch over UE4M3 bit offsets f in [-2, 6] */
+} sage_scale_mode;
+
+typedef struct { int64_t B, H, N, D; } sage_shape;
+
+/* Block of a quantizer.  Supported (tokens, channels):
+ *   SAGE_INT8 : (T, D) with T >= 1   — T consecutive tokens x all channels (Q: 128, K: 64)
+ *   SAGE_E4M3 : (0, 1)               — one scale per channel over all N tokens (V)
+ *   SAGE_MXFP4: (1, 32) along D (Q, K)  or (32, 1) along tokens (V)
+ *   SAGE_NVFP4: (1, 16) along D (Q, K)  or (16, 1) along tokens (V)                       */
+typedef struct { int32_t tokens, channels; } sage_block;
+
+/* A quantized (or 16-bit) operand of sage_attn_fwd; codes/scales in the layouts of
+ * sage_quantize_blocks.  `shape` is the logical [B, H, N, D] of the tensor.             */
+typedef struct {
+  sage_fmt fmt;
+  const void* codes;   /* codes, or the 16-bit tensor itself for SAGE_BF16 / SAGE_FP16 */
+  const void* scales;  /* NULL for 16-bit tensors */
+  sage_shape shape;
+} sage_qtensor;
+
+typedef struct {
+  int32_t causal;             /* 1: key j > query i is masked (top-left aligned, N_q = N_k) */
+  float sm_scale;             /* softmax scale on Q.K; 0 selects 1 / sqrt(D) */
+  sage_fmt p_fmt;             /* P operand of P.V: SAGE_BF16 | SAGE_E4M3 | SAGE_MXFP4 | SAGE_NVFP4 */
+  const uint8_t* block_mask;  /* NULL, or [B, Hq, ceil(N/128), ceil(N/64)]: 1 = run this (Q block,
+                                 K block) tile on bf16 Q and K_s (Thrift), 0 = INT8 */
+  const void* q_hi;           /* 16-bit Q   [B, Hq,  N, D] read for masked tiles (else NULL) */
+  const void* k_hi;           /* 16-bit K_s [B, Hkv, N, D] read for masked tiles (else NULL) */
+  sage_fmt hi_dt;             /* dtype of q_hi / k_hi: SAGE_BF16 */
+} sage_attn_params;
+
+/* Library version string (static storage). */
+const char* sage_version(void);
+/* Static description of an error code. */
+const char* sage_strerror(int status);
+
+/* K smoothing — "SageAttention: Accurate 8-Bit Attention for Plug-and-play Inference
+ * Acceleration", Contributions / Technical approach: K's channel-wise outliers are removed
+ * before 8-bit quantization.  Computes mean[b,h,c] = (1/N) sum_t k[b,h,t,c] in fp32 with a
+ * fixed order (fp32 running sums over each run of 64 tokens in token order, then a running
+ * sum of those partials in run order, then one division by N) and, if k_smoothed_out is
+ * not NULL, k_smoothed_out = round_to_dtype(fp32(k - mean)) (round-to-nearest-even).
+ *   k              [B,H,N,D] dtype dt (SAGE_BF16 | SAGE_FP16)
+ *   mean_out       [B,H,D] fp32
+ *   k_smoothed_out [B,H,N,D] dtype dt, or NULL
+ *   workspace      >= sage_smooth_k_workspace_bytes(ks) bytes of device memory      */
+int sage_smooth_k(const void* k, sage_fmt dt, sage_shape ks, float* mean_out, void* k_smoothed_out,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+size_t sage_smooth_k_workspace_bytes(sage_shape ks);
+
+/* Block quantization — SageAttention (Technical approach: Q and K in 8 bits), SageAttention3
+ * (microscaled FP4 attention) and "Search Your Block Floating Point Scales!" (Method >
+ * ScaleSearch: max-scale s = amax / 6 rounded to E4M3, or the scale with the least squared
+ * error among nearby candidates).  x is [B,H,N,D] in in_dt (SAGE_BF16 | SAGE_FP16).
+ * Element rule for every format: code = round_to_format(fp32(x * fp32(1 / s))), ties to
+ * even, saturating; the scale rules:
+ *   INT8 : s = fp32(amax / 127) per block; codes int8 [B,H,N,D]; scales fp32 [B,H,ceil(N/T)].
+ *          An all-zero block has s = 0 and codes 0.
+ *   E4M3 : s_c = fp32(amax_c / 448) per channel over all tokens; codes u8 [B,H,D,N]
+ *          (channel-major: tokens contiguous); scales fp32 [B,H,D].
+ *   MXFP4: e = smallest integer with 6 * 2^e >= amax (amax = 0: -127), x * 2^-e is exact.
+ *          Along D: codes [B,H,N,D/2], scales E8M0 [B,H,N,D/32].  Along tokens: codes
+ *          [B,H,D,Np/2], scales [B,H,D,Np/32], Np = N rounded up to 32 (padding = zeros).
+ *          Two codes per byte along the block axis, even element in the low nibble.
+ *   NVFP4: baseline scale code c0 = UE4M3(fp32(amax / 6)) (0 becomes 0x01); mode
+ *          SAGE_SCALE_SEARCH also evaluates UE4M3(fp32(amax/6) * g_k), g_k = fp32(0.85 +
+ *          k * 0.3 / 7), k = 0..7; SAGE_SCALE_SEARCH_OFFSETS evaluates c0 + f for f in
+ *          {-2,-1,1,..,6} within 0x01..0x7E.  Each candidate's squared error is summed in
+ *          fp32 as the balanced index-order pairwise tree; the first strictly smaller sum
+ *          wins (c0 first).  Layout as MXFP4 with one scale byte per 16 elements.
+ * Scale mode must be SAGE_SCALE_ABSMAX except for SAGE_NVFP4.                            */
+int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
+                         sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream);
+/* Host-side size query for the outputs of sage_quantize_blocks (host pointers out). */
+int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* codes_bytes, size_t* scale_bytes);
+
+/* NVFP4 -> MXFP8, the operand form the gfx950 matrix cores take for NVFP4 data (they have
+ * no UE4M3-scaled FP4 product).  For each 32 elements along the block axis: xhat = E2M1 x
+ * UE4M3 (exact), A = max |xhat|, E = smallest integer with 448 * 2^E >= A (A = 0: -127),
+ * f = E4M3(xhat * 2^-E).  `rows` x `len` elements: codes [rows, len/2], scales [rows,
+ * len/16] in; f8 [rows, len], e8m0 [rows, len/32] out.  len must be a multiple of 32.     */
+int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t len, void* f8_out,
+                        void* e8m0_out, hipStream_t stream);
+
+/* Fused quantized attention forward — SageAttention (8-bit QK^T, 16-bit P.V), SageAttention3
+ * and ScaleSearchAttention (FP4 QK^T and PV with fp32 accumulation), ThriftAttention
+ * (selected tiles in high precision, one joint softmax).
+ * out[b,h,i,:] = sum_j softmax_j(S[i,j]) V[j,:] with S = dequant(Q) dequant(K)^T * sm_scale,
+ * evaluated per Q block of 128 rows over K tiles of 64 keys in ascending order with an fp32
+ * running max and sum; P is quantized to p_fmt per tile before P.V.
+ * Supported operand sets (Hq a multiple of Hkv = k->shape.H; q-head h reads kv-head
+ * h / (Hq / Hkv)):
+ *   q, k SAGE_INT8 (blocks 128 / 64 tokens) + v SAGE_BF16 | SAGE_FP16 + p SAGE_BF16
+ *        (+ optional block_mask with bf16 q_hi / k_hi)
+ *   q, k SAGE_INT8 + v SAGE_E4M3 (per channel) + p SAGE_E4M3 (P scaled by 448)
+ *   q, k SAGE_MXFP4 (along D) + v SAGE_MXFP4 (along tokens) + p SAGE_MXFP4 (per 32 keys)
+ *   q, k SAGE_MXFP8 (along D) + v SAGE_MXFP8 (along tokens) + p SAGE_NVFP4 (max-scaled per
+ *        16 keys, then to MXFP8 like sage_nvfp4_to_mxfp8)
+ * out: [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16).  D in {64, 128}.                    */
+int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
+                  void* out, sage_fmt out_dt, hipStream_t stream);
+
+/* Thrift block selection — "ThriftAttention: Selective Mixed Precision for Long-Context FP4
+ * Attention", ¶1 and ¶3: a small fraction of query-key blocks runs in high precision.
+ * Score of (Q block qb, K block kb) = fp32 dot product (fma chain over channels) of
+ * bf16(mean of the block's Q rows) and bf16(mean of the block's K_s rows) (fp32 running
+ * sums in token order, one division by the block's length).  Per (b, q-head), over the
+ * causal-valid pairs (k_block*kb <= q_block*qb + q_block - 1 when causal), the
+ * min(n_valid, ceil(frac * n_valid)) highest scores are selected (ties: lower qb*nKB+kb).
+ *   q [B,Hq,N,D], k_smoothed [B,Hkv,N,D] in dt (SAGE_BF16);  mask_out [B,Hq,nQB,nKB] u8.
+ *   q_block = 128 and k_block = 64 are supported.  0 <= frac <= 1.                        */
+int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sage_shape qs, sage_shape ks,
+                         int q_block, int k_block, double frac, int causal, uint8_t* mask_out, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_block);
+
+/* Format conversion as the quantizers perform it, for verification: n fp32 values (device)
+ * to fmt codes (device): SAGE_BF16 / SAGE_FP16 (uint16 each), SAGE_E4M3 (byte each,
+ * saturating), SAGE_MXFP4 / SAGE_NVFP4 (an E2M1 code per byte, saturating).               */
+int sage_convert_f32(const float* x, int64_t n, sage_fmt fmt, void* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H_ */

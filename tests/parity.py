@@ -1,0 +1,99 @@
+"""Shared helpers of the GPU parity tests: run the oracle on the same seeded inputs and
+compare with the HIP path (bit-exact for codes/scales/masks, the stated tolerance for O)."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from bit_quantized_attention_03_amd import inputs as I
+
+# attention tolerance: max |O_gpu - O_oracle| <= ATOL_REL * max |O_oracle| and cosine >= COS_MIN
+ATOL_REL = 2e-3
+COS_MIN = 0.9995
+
+
+def np16(t: torch.Tensor) -> np.ndarray:
+    return I.bits16(t.detach().cpu())
+
+
+def u8(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().view(torch.uint8).numpy()
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = a.reshape(-1).astype(np.float64); b = b.reshape(-1).astype(np.float64)
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def check_out(gpu: np.ndarray, orc: np.ndarray, what: str = ""):
+    sel = ~np.isnan(orc)
+    g, o = gpu[sel].astype(np.float64), orc[sel]
+    err = float(np.max(np.abs(g - o))) if g.size else 0.0
+    ref = float(np.max(np.abs(o))) if o.size else 0.0
+    cos = cosine(g, o) if g.size else 1.0
+    assert err <= ATOL_REL * ref, f"{what}: max err {err:.3e} > {ATOL_REL} * {ref:.3e}"
+    assert cos >= COS_MIN, f"{what}: cosine {cos:.6f} < {COS_MIN}"
+    return err / max(ref, 1e-300), cos
+
+
+def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str,
+                bh=None, qb=None, frac: float = 0.05, search_mode: int = 1, threads=None):
+    """The whole quantize-and-attend pass on the oracle, from the same 16-bit inputs."""
+    dt = I.dtype_code(q.dtype)
+    qb16, kb16, vb16 = np16(q), np16(k), np16(v)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    mean, ks = oracle.smooth_k(kb16, dt)
+    res = {"mean": mean, "ks": ks}
+    if variant in ("int8", "int8_fp8pv", "thrift"):
+        qc, qs = oracle.quant_int8(qb16, dt, 128)
+        kc, kss = oracle.quant_int8(ks, dt, 64)
+        res.update(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=kss)
+        if variant == "int8_fp8pv":
+            vc, vs = oracle.quant_fp8_channel(vb16, dt)
+            res.update(v_codes=vc, v_scales=vs)
+            ops = oracle.AttnOperands(qk_fmt=oracle.QK_INT8, p_fmt=oracle.P_E4M3, v_fmt=oracle.V_E4M3, q_i8=qc, q_s=qs,
+                                      k_i8=kc, k_s=kss, v_lp=vc, v_s=vs)
+        else:
+            mask = None
+            if variant == "thrift":
+                mask, _ = oracle.thrift_select(qb16, ks, dt, 128, 64, frac, causal)
+                res["mask"] = mask
+            ops = oracle.AttnOperands(qk_fmt=oracle.QK_INT8, p_fmt=oracle.P_BF16, v_fmt=oracle.V_HI, q_i8=qc, q_s=qs,
+                                      k_i8=kc, k_s=kss, v_hi=vb16, v_dt=dt, q_hi=qb16, k_hi=ks, hi_dt=dt,
+                                      thrift_mask=mask)
+    elif variant == "mxfp4":
+        qc, qe = oracle.quant_mxfp4(qb16, dt, 0)
+        kc, ke = oracle.quant_mxfp4(ks, dt, 0)
+        vc, ve = oracle.quant_mxfp4(vb16, dt, 1)
+        res.update(q_codes=qc, q_scales=qe, k_codes=kc, k_scales=ke, v_codes=vc, v_scales=ve)
+        ops = oracle.AttnOperands(qk_fmt=oracle.QK_MXFP4, p_fmt=oracle.P_MXFP4, v_fmt=oracle.V_MXFP4, q_lp=qc,
+                                  q_e8=qe, k_lp=kc, k_e8=ke, v_lp=vc, v_e8=ve)
+    elif variant == "nvfp4_search":
+        qc, qsc, _ = oracle.quant_nvfp4(qb16, dt, 0, search_mode)
+        kc, ksc, _ = oracle.quant_nvfp4(ks, dt, 0, search_mode)
+        vc, vsc, _ = oracle.quant_nvfp4(vb16, dt, 1, search_mode)
+        res.update(q_nv=(qc, qsc), k_nv=(kc, ksc), v_nv=(vc, vsc))
+        q8, qe = oracle.nvfp4_to_mxfp8(qc, qsc)
+        k8, ke = oracle.nvfp4_to_mxfp8(kc, ksc)
+        v8, ve = oracle.nvfp4_to_mxfp8(vc, vsc)
+        res.update(q_codes=q8, q_scales=qe, k_codes=k8, k_scales=ke, v_codes=v8, v_scales=ve)
+        ops = oracle.AttnOperands(qk_fmt=oracle.QK_MXFP8, p_fmt=oracle.P_NVFP4_MXFP8, v_fmt=oracle.V_MXFP8, q_lp=q8,
+                                  q_e8=qe, k_lp=k8, k_e8=ke, v_lp=v8, v_e8=ve)
+    else:
+        raise ValueError(variant)
+    res["out"] = oracle.attention(ops, B, Hq, Hkv, N, D, causal, 1.0 / math.sqrt(D), bh=bh, qb=qb, threads=threads)
+    res["ops"] = ops
+    return res
+
+
+def fp64_reference(q, k, v, causal, bh=None):
+    """Unquantized fp64 attention on the 16-bit inputs (reported beside the parity numbers)."""
+    dt = I.dtype_code(q.dtype)
+    qv = oracle.decode16(np16(q), dt).astype(np.float64)
+    kv = oracle.decode16(np16(k), dt).astype(np.float64)
+    vv = oracle.decode16(np16(v), dt).astype(np.float64)
+    return oracle.attention_ref(qv, kv, vv, causal, 1.0 / math.sqrt(q.shape[-1]), bh=bh)

@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI (no GPU work): the library loads, exports every function
+include/sage.h declares, and rejects bad arguments before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from bit_quantized_attention_03_amd import sage
+    return sage.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ("sage_smooth_k", "sage_quantize_blocks", "sage_attn_fwd", "thrift_select_blocks",
+                 "sage_nvfp4_to_mxfp8", "sage_strerror", "sage_version"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror(L):
+    from bit_quantized_attention_03_amd import sage
+    assert sage.version().startswith("sage-gfx950")
+    for st in (0, -1, -2, -3, -4, -5):
+        assert L.sage_strerror(st)
+
+
+def test_quantized_bytes(L):
+    from bit_quantized_attention_03_amd import sage
+    assert sage.quantized_bytes(sage.INT8, (128, 128), (4, 32, 4096, 128)) == (4 * 32 * 4096 * 128, 4 * 32 * 32 * 4)
+    assert sage.quantized_bytes(sage.E4M3, (0, 1), (2, 24, 16384, 64)) == (2 * 24 * 16384 * 64, 2 * 24 * 64 * 4)
+    assert sage.quantized_bytes(sage.MXFP4, (1, 32), (2, 16, 8192, 128)) == (2 * 16 * 8192 * 64, 2 * 16 * 8192 * 4)
+    assert sage.quantized_bytes(sage.MXFP4, (32, 1), (1, 1, 200, 64)) == (64 * 224 // 2, 64 * 224 // 32)
+    assert sage.quantized_bytes(sage.NVFP4, (16, 1), (1, 1, 200, 64)) == (64 * 224 // 2, 64 * 224 // 16)
+    with pytest.raises(sage.SageError):
+        sage.quantized_bytes(sage.MXFP4, (1, 16), (1, 1, 64, 64))     # MX blocks are 32 wide
+    with pytest.raises(sage.SageError):
+        sage.quantized_bytes(sage.INT8, (128, 64), (1, 1, 64, 128))   # INT8 block spans all channels
+
+
+def test_validation_before_launch(L):
+    from bit_quantized_attention_03_amd import sage
+    shp = sage.Shape(1, 1, 128, 128)
+    # null pointers
+    assert L.sage_smooth_k(None, sage.BF16, shp, None, None, None, 0, None) == -1
+    assert L.sage_quantize_blocks(None, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 0, None, None, None) == -1
+    q = sage.QTensorC(sage.INT8, None, None, shp)
+    p = sage.AttnParamsC(0, 0.0, sage.BF16, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(q), C.byref(q), C.byref(q), C.byref(p), None, sage.FP32, None) == -1
+    # misaligned pointers (never dereferenced: validation fails first)
+    fake = 0x1000_0001
+    assert L.sage_quantize_blocks(fake, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 0, 0x2000_0000, 0x3000_0000,
+                                  None) == -3
+    # unsupported head dimension for attention
+    s96 = sage.Shape(1, 1, 128, 96)
+    q96 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, s96)
+    assert L.sage_attn_fwd(C.byref(q96), C.byref(q96), C.byref(q96), C.byref(p), 0x1000_0000, sage.FP32, None) == -2
+    # search mode only for NVFP4
+    assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 1, 0x2000_0000,
+                                  0x3000_0000, None) == -1
+    # GQA needs Hq to be a multiple of Hkv
+    qs = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 3, 128, 128))
+    ks = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 128, 128))
+    assert L.sage_attn_fwd(C.byref(qs), C.byref(ks), C.byref(ks), C.byref(p), 0x1000_0000, sage.FP32, None) == -1
+    # thrift: workspace required, frac in [0, 1]
+    assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, shp, shp, 128, 64, 0.05, 1, 0x1000_0000, None, 0,
+                                  None) == -4
+    assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, shp, shp, 128, 64, 1.5, 1, 0x1000_0000,
+                                  0x1000_0000, 1 << 30, None) == -1
+    # smoothing workspace
+    assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    from bit_quantized_attention_03_amd import sage
+    with pytest.raises(ValueError):
+        sage.smooth_k(torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16))
