@@ -6,33 +6,46 @@
 // V per channel).  ThriftAttention (¶1, ¶3): tiles flagged in a block mask use bf16 Q and
 // K_s instead, and every tile feeds one joint online softmax.
 //
-// Work decomposition: a workgroup (4 waves) owns one Q block of 128 rows of one (b, q-head);
-// each wave owns 32 rows.  K/V tiles of 64 keys stream through double-buffered LDS
-// (register-staged 16-byte loads).  Per tile and wave:
-//   S^T (64 keys x 32 queries) = K . Q^T on v_mfma_i32_32x32x32_i8 (two 32-key halves, D/32
-//       k-steps), so each lane holds 32 scores of ONE query row: softmax statistics are
-//       per-lane scalars.  K rows are loaded permuted so that lane half h holds the keys
-//       32h .. 32h+31 of the tile in register order (key = 32h + 16b + r for accumulator b,
-//       register r): the P registers line up with 8 consecutive keys per k-group of the
-//       next product.
-//   dequantize: s = float(acc) * (s_q * s_k * sm_scale * log2 e); the row max is taken on the
-//       raw accumulators and one swap across lane halves (v_permlane32_swap).
-//   online softmax in fp32, base 2: the running max only moves (and O, l are rescaled) when
-//       a row's tile max exceeds it by more than `tau` (0 for FP8 P, which must stay <= 448).
-//   O^T (D x 32) += V^T . P^T on v_mfma_f32_32x32x16_bf16: V^T fragments come straight from
-//       the row-major LDS tile through ds_read_b64_tr_b16 (each 16-lane group transposes a
-//       4-key x 16-channel block); or on the scaled FP8 MFMA (32x32x64) with V stored
-//       channel-major by its quantizer.
-// The causal mask is top-left aligned; fully masked tiles are skipped per wave, and Q blocks
-// are scheduled heaviest first.  Workgroup ids are remapped so consecutive Q blocks of a head
-// run on the same XCD and share its L2.
+// Work decomposition.  A workgroup of 8 waves owns two adjacent Q blocks of 128 rows of one
+// (b, q-head); waves 0-3 (group A) take the first block, waves 4-7 (group B) the second, 32
+// rows per wave.  Both groups stream the same K/V tiles of 64 keys through LDS.
+//
+// Per tile and wave:
+//   S^T (64 keys x 32 queries) = K . Q^T on v_mfma_i32_32x32x32_i8, so each lane holds 32
+//       scores of ONE query row and the softmax statistics are per-lane scalars.  K rows are
+//       read permuted so that lane half h holds keys 32h .. 32h+31 of the tile in register
+//       order (key = 32h + 16b + r for accumulator b, register r).
+//   softmax: s = float(acc) * (s_q s_k sm_scale log2 e); row max over the lane and one
+//       v_permlane32_swap; fp32 online softmax in base 2.  The running max moves (and O, l
+//       are rescaled) only when a row's tile max exceeds it by more than `tau` (0 for FP8 P,
+//       which must stay <= 448).
+//   O^T (D x 32) += V^T . P^T on v_mfma_f32_32x32x16_bf16 with V^T fragments read from the
+//       row-major LDS tile by ds_read_b64_tr_b16 (each 16-lane group transposes a 4-key x
+//       16-channel block), or on the scaled FP8 MFMA (32x32x64) with V stored channel-major.
+//
+// Ping-pong schedule.  Each wave alternates a VALU phase (softmax of tile t) and an MFMA
+// phase (P.V of tile t, then S of tile t+1).  Group B runs one phase behind group A, so on
+// every SIMD (one wave of each group) one wave keeps the matrix core busy while the other
+// uses the vector ALU.  Phases are separated by workgroup barriers:
+//     phase 2t+2: A = MFMA(t), B = VALU(t);   phase 2t+3: A = VALU(t+1), B = MFMA(t).
+// (Both groups run the same straight-line program, offset by one barrier, so the phase code
+// exists once and register pressure is that of one wave's program.)
+// Group A also moves the tiles: at the start of its VALU phase 2t+3 it issues direct
+// global->LDS loads (global_load_lds_dwordx4) of K(t+2) and V(t+1) and waits for them at the
+// end of that phase (a VALU phase reads no LDS, so nothing in it waits on those writes).  K(s)
+// is read in phases 2s, 2s+1 and V(t) in 2t+2, 2t+3, so two buffers of each are enough.
+// Tiles never pass through registers.
+//
+// The causal mask is top-left aligned; tiles entirely above a wave's rows are skipped and
+// workgroups are scheduled heaviest first.  Workgroup ids are remapped so consecutive Q-block
+// pairs of one head run on the same XCD and share its L2.
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace sage {
 namespace {
 
-constexpr int QB = 128, KT = 64, NTHREADS = 256;
+constexpr int QB = 128, KT = 64, NWAVES = 8, NTHREADS = 64 * NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct Params {
@@ -41,20 +54,42 @@ struct Params {
   const void* v; const float* vs;
   const uint8_t* mask; const uint16_t* qhi; const uint16_t* khi;
   void* out;
-  int64_t Hq, Hkv, N, nQB, nKB, total_wg;
+  int64_t Hq, Hkv, N, Np, nQB, nKB, nPairs, total_wg;
   float sm_log2;   // sm_scale * log2(e)
   float tau;       // lazy-rescale threshold (log2 units)
 };
 
-template <int D, bool PV8, bool THRIFT>
+// LDS: two K tiles (int8 [64][D]) and two V tiles (bf16 [64][D] row-major, or FP8 V^T
+// [D][64]), all unpadded with XOR-swizzled 16-byte chunks.
+template <int D, bool PV8>
 struct Smem {
-  static constexpr int PK = THRIFT ? (2 * D + 16) : (D + 16);   // K tile row pitch, bytes
-  static constexpr int PV = PV8 ? 80 : (2 * D + 64);            // V tile row pitch, bytes
-  static constexpr int K_BYTES = KT * PK;
-  static constexpr int V_BYTES = PV8 ? D * PV : KT * PV;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int TOTAL = 2 * STAGE;
+  static constexpr int K_BYTES = KT * D;
+  static constexpr int V_BYTES = PV8 ? D * KT : KT * 2 * D;
+  static constexpr int V_BASE = 2 * K_BYTES;
+  static constexpr int TOTAL = 2 * K_BYTES + 2 * V_BYTES;
 };
+
+// K: chunk c of row r at chunk position c ^ (r & (D/16 - 1)) of its row: the 32 rows one MFMA
+// operand read touches spread over all bank groups.
+template <int D>
+__device__ __forceinline__ int k_off(int row, int c) { return row * D + 16 * (c ^ (row & (D / 16 - 1))); }
+// bf16 V: chunk c of row r at c ^ f(r); f spreads the 4 consecutive rows that one transposed
+// read group touches over distinct 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+template <int D>
+__device__ __forceinline__ int v_off(int row, int byte) {   // byte offset within the row (< 2D)
+  return row * 2 * D + 16 * ((byte >> 4) ^ v_swz<D>(row)) + (byte & 15);
+}
+// FP8 V^T: chunk c (of 4) of channel row r at c ^ ((r >> 2) & 3).
+__device__ __forceinline__ int v8_off(int row, int c) { return row * KT + 16 * (c ^ ((row >> 2) & 3)); }
+
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// Workgroup barrier without a memory fence.  The loop's ordering needs are explicit: tile loads
+// are complete (wait_vmem) before the barrier that publishes them, and an LDS buffer is
+// overwritten only after the barrier following the matrix instructions that consumed its reads.
+// (__syncthreads would also drain the tile loads still in flight at every phase boundary.)
+__device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_s_barrier(); }
 
 __device__ __forceinline__ int tile_key(int b, int m) {   // accumulator row m of half b -> key in tile
   return ((m >> 2) & 1) * 32 + 16 * b + (m >> 3) * 4 + (m & 3);
@@ -71,273 +106,317 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D, bool PV8, bool THRIFT, bool VF16>
-struct Loader {
-  // per-thread register staging for one tile
-  static constexpr int K_CH = KT * D / 16 / NTHREADS;                 // 16-byte chunks of int8 K
-  static constexpr int KH_CH = THRIFT ? KT * D * 2 / 16 / NTHREADS : 0;  // bf16 K_s
-  static constexpr int V_CH = PV8 ? D * KT / 16 / NTHREADS : KT * D * 2 / 16 / NTHREADS;
-  v4i kreg[K_CH > KH_CH ? K_CH : KH_CH];
-  v4i vreg[V_CH];
-  bool hi;
+typedef __attribute__((address_space(3))) void lds_void;
 
-  __device__ __forceinline__ void load(const Params& p, int64_t bkv, int t, bool hi_tile, int tid) {
-    hi = hi_tile;
-    const int64_t key0 = (int64_t)t * KT;
-    if (!hi_tile) {
+// Direct global -> LDS tile copies by the 4 waves of group A.  Lane l of wave a in round i
+// fills LDS chunk (4i + a) * 64 + l; its source chunk (swizzle undone) is a per-lane
+// constant computed once.  A ragged last K/V tile re-reads row N-1 for rows past N (finite
+// data, masked keys).  FP8 V^T rows are padded to a multiple of 64 tokens by the quantizer.
+template <int D, bool PV8>
+struct DmaPlan {
+  static constexpr int K_ROUNDS = KT * D / 16 / 256;
+  static constexpr int V_ROUNDS = (PV8 ? D * KT : KT * 2 * D) / 16 / 256;
+  int koff[K_ROUNDS], krow[K_ROUNDS];
+  int voff[V_ROUNDS], vrow[V_ROUNDS];
+  __device__ __forceinline__ void init(int a, int lane, int64_t Np) {
 #pragma unroll
-      for (int i = 0; i < K_CH; ++i) {
-        const int c = tid + NTHREADS * i, row = c / (D / 16), col = c % (D / 16);
-        kreg[i] = (key0 + row < p.N) ? *(const v4i*)(p.k + ((bkv * p.N + key0 + row) * D + col * 16)) : v4i{0, 0, 0, 0};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KH_CH; ++i) {
-        const int c = tid + NTHREADS * i, row = c / (D / 8), col = c % (D / 8);
-        kreg[i] = (key0 + row < p.N) ? *(const v4i*)(p.khi + ((bkv * p.N + key0 + row) * D + col * 8)) : v4i{0, 0, 0, 0};
-      }
+    for (int i = 0; i < K_ROUNDS; ++i) {
+      const int pos = (i * 4 + a) * 64 + lane, row = pos / (D / 16), c = (pos % (D / 16)) ^ (row & (D / 16 - 1));
+      krow[i] = row; koff[i] = row * D + 16 * c;
     }
-    if (PV8) {   // V^T [D][N] bytes
-      const uint8_t* vt = (const uint8_t*)p.v;
 #pragma unroll
-      for (int i = 0; i < V_CH; ++i) {
-        const int c = tid + NTHREADS * i, ch = c / 4, col = c % 4;
-        const int64_t tok = key0 + col * 16;
-        const uint8_t* src = vt + (bkv * D + ch) * p.N + tok;
-        if (tok + 16 <= p.N && (p.N & 15) == 0) {
-          vreg[i] = *(const v4i*)src;
-        } else {
-          uint32_t w[4] = {0, 0, 0, 0};
-          for (int j = 0; j < 16; ++j)
-            if (tok + j < p.N) w[j >> 2] |= (uint32_t)src[j] << (8 * (j & 3));
-          vreg[i] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
-        }
-      }
-    } else {     // V [N][D] 16-bit
-      const uint16_t* v = (const uint16_t*)p.v;
-#pragma unroll
-      for (int i = 0; i < V_CH; ++i) {
-        const int c = tid + NTHREADS * i, row = c / (D / 8), col = c % (D / 8);
-        v4i x = (key0 + row < p.N) ? *(const v4i*)(v + ((bkv * p.N + key0 + row) * D + col * 8)) : v4i{0, 0, 0, 0};
-        if (VF16) {   // fp16 V is read as bf16 (nearest-even) for the bf16 product
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            uint32_t u = (uint32_t)x[w];
-            x[w] = (int)pack_bf16x2(f16_to_f32((uint16_t)(u & 0xffffu)), f16_to_f32((uint16_t)(u >> 16)));
-          }
-        }
-        vreg[i] = x;
+    for (int i = 0; i < V_ROUNDS; ++i) {
+      const int pos = (i * 4 + a) * 64 + lane;
+      if (PV8) {   // channel row of V^T, 4 chunks of 16 tokens
+        const int row = pos / 4, c = (pos % 4) ^ ((row >> 2) & 3);
+        vrow[i] = row; voff[i] = (int)(row * Np) + 16 * c;
+      } else {
+        const int row = pos / (2 * D / 16), c = (pos % (2 * D / 16)) ^ v_swz<D>(row);
+        vrow[i] = row; voff[i] = row * 2 * D + 16 * c;
       }
     }
   }
-
-  __device__ __forceinline__ void store(uint8_t* stage, int tid) const {
-    using S = Smem<D, PV8, THRIFT>;
-    uint8_t* ks = stage;
-    uint8_t* vs = stage + S::K_BYTES;
-    if (!hi) {
+  __device__ __forceinline__ void k_tile(const Params& p, int64_t bkv, int t, uint8_t* kb, int a) const {
+    const int64_t key0 = (int64_t)t * KT;
+    const char* base = (const char*)(p.k + (bkv * p.N + key0) * D);
+    const bool full = key0 + KT <= p.N;
 #pragma unroll
-      for (int i = 0; i < K_CH; ++i) {
-        const int c = tid + NTHREADS * i, row = c / (D / 16), col = c % (D / 16);
-        *(v4i*)(ks + row * S::PK + col * 16) = kreg[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KH_CH; ++i) {
-        const int c = tid + NTHREADS * i, row = c / (D / 8), col = c % (D / 8);
-        *(v4i*)(ks + row * S::PK + col * 16) = kreg[i];
-      }
+    for (int i = 0; i < K_ROUNDS; ++i) {
+      int off = koff[i];
+      if (!full && key0 + krow[i] >= p.N) off += (int)((p.N - 1 - key0 - krow[i]) * D);
+      __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(kb + (i * 4 + a) * 1024), 16, 0, 0);
     }
+  }
+  __device__ __forceinline__ void v_tile(const Params& p, int64_t bkv, int t, uint8_t* vb, int a) const {
+    const int64_t key0 = (int64_t)t * KT;
     if (PV8) {
+      const char* base = (const char*)p.v + bkv * D * p.Np + key0;
 #pragma unroll
-      for (int i = 0; i < V_CH; ++i) {
-        const int c = tid + NTHREADS * i, ch = c / 4, col = c % 4;
-        *(v4i*)(vs + ch * S::PV + col * 16) = vreg[i];
-      }
+      for (int i = 0; i < V_ROUNDS; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(base + voff[i]), (lds_void*)(vb + (i * 4 + a) * 1024), 16, 0, 0);
     } else {
+      const char* base = (const char*)((const uint16_t*)p.v + (bkv * p.N + key0) * D);
+      const bool full = key0 + KT <= p.N;
 #pragma unroll
-      for (int i = 0; i < V_CH; ++i) {
-        const int c = tid + NTHREADS * i, row = c / (D / 8), col = c % (D / 8);
-        *(v4i*)(vs + row * S::PV + col * 16) = vreg[i];
+      for (int i = 0; i < V_ROUNDS; ++i) {
+        int off = voff[i];
+        if (!full && key0 + vrow[i] >= p.N) off += (int)((p.N - 1 - key0 - vrow[i]) * 2 * D);
+        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(vb + (i * 4 + a) * 1024), 16, 0, 0);
       }
     }
   }
 };
 
 template <int D, bool CAUSAL, bool PV8, bool THRIFT, bool VF16, bool OUT_BF16>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_i8_kernel(Params p) {
-  using S = Smem<D, PV8, THRIFT>;
-  constexpr int NKC = D / 32;    // int8 k-steps of 32 channels
+__global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const float* __restrict__ k_scales,
+                                                              const float* __restrict__ q_scales,
+                                                              const uint8_t* __restrict__ blk_mask) {
+  using S = Smem<D, PV8>;
   constexpr int NCC = D / 32;    // 32-channel output chunks
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
-  // ---- workgroup -> (b, h, qb); XCD-aware: consecutive work items on one XCD
+  // ---- workgroup -> (b, h, pair of Q blocks); XCD-aware: consecutive work items on one XCD
   int64_t wg = blockIdx.x;
   if ((p.total_wg & 7) == 0) wg = (wg & 7) * (p.total_wg >> 3) + (wg >> 3);
-  const int64_t bh = wg / p.nQB;
-  int64_t qb = wg % p.nQB;
-  if (CAUSAL) qb = p.nQB - 1 - qb;            // heaviest Q blocks first
+  const int64_t bh = wg / p.nPairs;
+  int64_t pr = wg % p.nPairs;
+  if (CAUSAL) pr = p.nPairs - 1 - pr;         // heaviest pairs first
   const int64_t b = bh / p.Hq, h = bh % p.Hq;
   const int64_t bkv = b * p.Hkv + h / (p.Hq / p.Hkv);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  const int grp = w >> 2, a = w & 3;                         // group (0 = A, 1 = B), wave in group
   const int li = lane & 31, lh = lane >> 5;
-  const int64_t qrow0 = qb * QB + 32 * w;     // first row of this wave
-  const int64_t qrow = qrow0 + li;            // this lane's query row
+  const int64_t qb = 2 * pr + grp;                           // this group's Q block
+  const int64_t qrow0 = qb * QB + 32 * a;                    // first row of this wave
+  const int64_t qrow = qrow0 + li;                           // this lane's query row
   const bool row_ok = qrow < p.N;
+  const bool blk_ok = qb < p.nQB;
 
-  int nT = (int)p.nKB;
-  if (CAUSAL) {
-    const int64_t last = (qb * QB + QB - 1) / KT + 1;
-    nT = (int)(last < p.nKB ? last : p.nKB);
+  // tiles of this group, and of the workgroup (the longer of the two groups)
+  auto tiles_of = [&](int64_t q) -> int {
+    if (q >= p.nQB) return 0;
+    if (!CAUSAL) return (int)p.nKB;
+    const int64_t last = (q * QB + QB - 1) / KT + 1;
+    return (int)(last < p.nKB ? last : p.nKB);
+  };
+  const int nTg = tiles_of(qb);
+  const int nT = tiles_of(2 * pr + 1) > tiles_of(2 * pr) ? tiles_of(2 * pr + 1) : tiles_of(2 * pr);
+  const uint8_t* mrow = THRIFT && blk_ok ? blk_mask + (bh * p.nQB + qb) * p.nKB : nullptr;
+  auto active = [&](int t) { return t >= 0 && t < nTg && (!CAUSAL || (int64_t)t * KT <= qrow0 + 31); };
+  auto kbuf = [&](int t) { return smem + (t & 1) * S::K_BYTES; };
+  auto vbuf = [&](int t) { return smem + S::V_BASE + (t & 1) * S::V_BYTES; };
+
+  // ---- per-lane LDS read offsets (loop invariant; tile and chunk terms become immediates)
+  int kro[D / 32], vro[D / 32];
+  {
+    const int rk = tile_key(0, li);   // tile_key(b, li) = rk + 16 b; k_off's swizzle ignores the 16 b
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc) kro[kc] = k_off<D>(rk, 2 * kc + lh);
+    if (!PV8) {   // transposed V reads of k-group kg, half r2 touch row rv + 8 kg + 4 r2
+      const int g16 = lane >> 4, j = lane & 15;
+      const int rv = 32 * (g16 >> 1) + (j >> 2);
+#pragma unroll
+      for (int cc = 0; cc < D / 32; ++cc) vro[cc] = v_off<D>(rv, 2 * (32 * cc + 16 * (g16 & 1) + 4 * (j & 3)));
+    } else {      // V^T rows 32 cc + li, chunks 2 lh, 2 lh + 1
+#pragma unroll
+      for (int cc = 0; cc < D / 32; ++cc) vro[cc] = 32 * cc + li;
+    }
   }
-  const uint8_t* mrow = THRIFT ? p.mask + (bh * p.nQB + qb) * p.nKB : nullptr;
 
   // ---- Q fragments (B operand of the S^T product): row qrow, channels 32kc + 16lh .. +16
-  v4i qf[NKC];
+  v4i qf[D / 32];
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc)
+  for (int kc = 0; kc < D / 32; ++kc)
     qf[kc] = row_ok ? *(const v4i*)(p.q + (bh * p.N + qrow) * D + 32 * kc + 16 * lh) : v4i{0, 0, 0, 0};
-  const float qscale = p.qs[bh * p.nQB + qb];
+  const float qscale = blk_ok ? q_scales[__builtin_amdgcn_readfirstlane((int)(bh * p.nQB + qb))] : 0.0f;
 
   v16f o[NCC];
 #pragma unroll
   for (int c = 0; c < NCC; ++c) o[c] = v16f{};
   float m_run = -__builtin_inff(), l_run = 0.0f;
+  v16i acc[2];                  // S of the tile the next VALU phase works on
+  bool hi = false;              // that tile runs on bf16 (Thrift)
+  float dq = 0.0f;              // its dequantization factor (log2 units)
+  uint32_t pk[PV8 ? 8 : 16];    // P of the tile the next MFMA phase works on (bf16 pairs / FP8 quads)
 
-  Loader<D, PV8, THRIFT, VF16> ld;
-  ld.load(p, bkv, 0, THRIFT ? (mrow[0] != 0) : false, tid);
-  ld.store(smem, tid);
+  DmaPlan<D, PV8> dma;
+  if (grp == 0) {
+    dma.init(a, lane, p.Np);
+    dma.k_tile(p, bkv, 0, kbuf(0), a);
+  }
+  wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < nT; ++t) {
-    const bool hi = THRIFT ? (mrow[t] != 0) : false;
-    if (t + 1 < nT) ld.load(p, bkv, t + 1, THRIFT ? (mrow[t + 1] != 0) : false, tid);
-    const uint8_t* ks = smem + (t & 1) * S::STAGE;
-    const uint8_t* vs = ks + S::K_BYTES;
+  // ---- S of tile t for this wave.  The int8 K fragments are read from LDS by qk_load and
+  //      consumed by qk_mfma, so the reads can be issued ahead of other matrix work.
+  v4i kf[D / 32][2];
+  auto uni = [](int64_t x) { return (int64_t)__builtin_amdgcn_readfirstlane((int)x); };   // scalar loads below
+  auto qk_load = [&](int t) {
+    if (THRIFT && mrow[uni(t)] != 0) return;
+    const uint8_t* kb = kbuf(t);
+#pragma unroll
+    for (int kc = 0; kc < D / 32; ++kc)
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) kf[kc][bb] = *(const v4i*)(kb + kro[kc] + 16 * D * bb);
+  };
+  auto qk_mfma = [&](int t) {
+    hi = THRIFT && mrow[uni(t)] != 0;
+    dq = __builtin_fmaxf(hi ? p.sm_log2 : qscale * k_scales[uni(bkv * p.nKB + t)] * p.sm_log2, 1.17549435e-38f);
     const int64_t key0 = (int64_t)t * KT;
-    const bool wave_active = !CAUSAL || key0 <= qrow0 + 31;
-    if (wave_active) {
-      // ---------------- scores S^T for keys 32h + 16b + r
-      float s[2][16];
-      float dq;
-      if (!hi) {
-        v16i acc[2] = {v16i{}, v16i{}};
+    if (!hi) {
+      acc[0] = v16i{}; acc[1] = v16i{};
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc) {
+      for (int kc = 0; kc < D / 32; ++kc)
 #pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const v4i kf = *(const v4i*)(ks + tile_key(bb, li) * S::PK + 32 * kc + 16 * lh);
-            acc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[kc], acc[bb], 0, 0, 0);
-          }
-        }
+        for (int bb = 0; bb < 2; ++bb) acc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kc][bb], qf[kc], acc[bb], 0, 0, 0);
+    } else {   // Thrift tile: bf16 Q and K_s fragments straight from global memory (L2)
+      v16f f[2] = {v16f{}, v16f{}};
+      const int64_t k0 = key0 + tile_key(0, li), k1 = key0 + tile_key(1, li);
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[bb][r] = (float)acc[bb][r];
-        dq = qscale * p.ks[bkv * p.nKB + t] * p.sm_log2;
-      } else {
-        v16f acc[2] = {v16f{}, v16f{}};
-#pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const v8bf qh = row_ok ? *(const v8bf*)(p.qhi + (bh * p.N + qrow) * D + 16 * kc + 8 * lh) : v8bf{};
-#pragma unroll
-          for (int bb = 0; bb < 2; ++bb) {
-            const v8bf kh = *(const v8bf*)(ks + tile_key(bb, li) * S::PK + 2 * (16 * kc + 8 * lh));
-            acc[bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh, acc[bb], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[bb][r] = acc[bb][r];
-        dq = p.sm_log2;
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const v8bf qh = row_ok ? *(const v8bf*)(p.qhi + (bh * p.N + qrow) * D + 16 * kc + 8 * lh) : v8bf{};
+        const v8bf kh0 = k0 < p.N ? *(const v8bf*)(p.khi + (bkv * p.N + k0) * D + 16 * kc + 8 * lh) : v8bf{};
+        const v8bf kh1 = k1 < p.N ? *(const v8bf*)(p.khi + (bkv * p.N + k1) * D + 16 * kc + 8 * lh) : v8bf{};
+        f[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh0, qh, f[0], 0, 0, 0);
+        f[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh1, qh, f[1], 0, 0, 0);
       }
-      // ---------------- masks (causal diagonal tiles, ragged last tile)
-      const bool need_mask = (key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0);
-      if (need_mask) {
+      acc[0] = __builtin_bit_cast(v16i, f[0]);
+      acc[1] = __builtin_bit_cast(v16i, f[1]);
+    }
+  };
+
+  // ---- VALU phase: softmax of tile t -> P in pk
+  auto valu_phase = [&](int t) {
+    if (!active(t)) return;
+    const int64_t key0 = (int64_t)t * KT;
+    float s[2][16];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t kg = key0 + 32 * lh + 16 * bb + r;
-            if (kg >= p.N || (CAUSAL && kg > qrow)) s[bb][r] = -__builtin_inff();
-          }
-      }
-      // ---------------- online softmax (base 2)
-      float mx = s[0][0];
-#pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[bb][r]);
-      mx = halves_max(mx);
-      const float mt = mx * dq;                      // tile row max in scaled units (dq >= 0)
-      const bool grow = mt > m_run + p.tau;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // wave-uniform: move the running max
-        const float m_new = __builtin_fmaxf(m_run, mt);
-        const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int c = 0; c < NCC; ++c) o[c] *= alpha;
-      }
-      const float moff = (m_run == -__builtin_inff() ? 0.0f : m_run) - (PV8 ? 8.807354922057604f : 0.0f);  // FP8: P * 448
-      float pv[2][16];
-      float lsum = 0.0f;
+      for (int r = 0; r < 16; ++r) s[bb][r] = hi ? __int_as_float(acc[bb][r]) : (float)acc[bb][r];
+    if ((key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0)) {   // causal diagonal or ragged tile
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], dq, -moff));
-          if (need_mask && s[bb][r] == -__builtin_inff()) e = 0.0f;
-          pv[bb][r] = e;
-          lsum += e;
+          const int64_t kg = key0 + 32 * lh + 16 * bb + r;
+          if (kg >= p.N || (CAUSAL && kg > qrow)) s[bb][r] = -__builtin_inff();
         }
-      l_run += lsum;
-      // ---------------- O^T += V^T P^T
-      if (!PV8) {
-        uint32_t pk[2][8];
+    }
+    float mx = s[0][0];
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) pk[bb][r >> 1] = pack_bf16x2(pv[bb][r], pv[bb][r + 1]);
-        const int g16 = lane >> 4, j = lane & 15;
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[bb][r]);
+    mx = halves_max(mx);
+    const float mt = mx * dq;                      // tile row max in scaled units
+    if (__builtin_amdgcn_ballot_w64(mt > m_run + p.tau) != 0) {   // wave-uniform: move the running max
+      const float m_new = __builtin_fmaxf(m_run, mt);
+      const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) {
-          const int bb = kg >> 1, r0 = 4 * (kg & 1);
-          v4i pb = v4i{(int)pk[bb][r0], (int)pk[bb][r0 + 1], (int)pk[bb][r0 + 2], (int)pk[bb][r0 + 3]};
-          const v8bf pf = __builtin_bit_cast(v8bf, pb);
+      for (int c = 0; c < NCC; ++c) o[c] *= alpha;
+    }
+    const float moff = m_run - (PV8 ? 8.807354922057604f : 0.0f);   // FP8 P carries the factor 448
+    float lsum = 0.0f;
 #pragma unroll
-          for (int cc = 0; cc < NCC; ++cc) {
-            const int key = 32 * (g16 >> 1) + 8 * kg + (j >> 2);
-            const int ch = 32 * cc + 16 * (g16 & 1) + 4 * (j & 3);
-            const uint8_t* a0 = vs + key * S::PV + ch * 2;
-            const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0));
-            const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0 + 4 * S::PV));
-            const v8bf vf = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, o[cc], 0, 0, 0);
-          }
-        }
-      } else {
-        v8i pf;
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int q4 = 0; q4 < 8; ++q4) {
-          const int bb = q4 >> 2, r = 4 * (q4 & 3);
-          uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(pv[bb][r], pv[bb][r + 1], 0u, false);
-          pf[q4] = (int)__builtin_amdgcn_cvt_pk_fp8_f32(pv[bb][r + 2], pv[bb][r + 3], wv, true);
-        }
+      for (int r = 0; r < 16; ++r) {
+        s[bb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], dq, -moff));
+        lsum += s[bb][r];
+      }
+    l_run += lsum;
+    if (!PV8) {
 #pragma unroll
-        for (int cc = 0; cc < NCC; ++cc) {
-          const uint8_t* a0 = vs + (32 * cc + li) * S::PV + 32 * lh;
-          const v4i v0 = *(const v4i*)a0, v1 = *(const v4i*)(a0 + 16);
-          const v8i vf = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          o[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pf, o[cc], 0, 0, 0, 127, 0, 127);
-        }
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) pk[8 * bb + (r >> 1)] = pack_bf16x2(s[bb][r], s[bb][r + 1]);
+    } else {
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const int bb = q4 >> 2, r = 4 * (q4 & 3);
+        const uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][r], s[bb][r + 1], 0u, false);
+        pk[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][r + 2], s[bb][r + 3], wv, true);
       }
     }
-    if (t + 1 < nT) ld.store(smem + ((t + 1) & 1) * S::STAGE, tid);
-    __syncthreads();
+  };
+
+  // ---- MFMA phase: O += P(t) V(t), then S of tile t+1 (group A also issues the tile loads).
+  //      LDS fragment reads run one k-group ahead of the matrix instructions that use them.
+  auto v_frag = [&](const uint8_t* vs, int kg, int cc) -> v8bf {
+    const uint8_t* a0 = vs + vro[cc] + 8 * kg * 2 * D;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0));
+    const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0 + 4 * 2 * D));
+    v8us raw = __builtin_bit_cast(v8us, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (VF16) {   // fp16 V is multiplied as bf16 (nearest-even)
+      v4i pkd;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pkd[e] = (int)pack_bf16x2(f16_to_f32(raw[2 * e]), f16_to_f32(raw[2 * e + 1]));
+      raw = __builtin_bit_cast(v8us, pkd);
+    }
+    return __builtin_bit_cast(v8bf, raw);
+  };
+  auto mfma_phase = [&](int t) {
+    const bool next = active(t + 1);
+    if (next) qk_load(t + 1);
+    if (active(t)) {
+      const uint8_t* vs = vbuf(t);
+      if (!PV8) {
+        v8bf vf[2][NCC];
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) vf[0][cc] = v_frag(vs, 0, cc);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+          if (kg + 1 < 4) {
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) vf[(kg + 1) & 1][cc] = v_frag(vs, kg + 1, cc);
+          }
+          const v8bf pf = __builtin_bit_cast(v8bf, v4i{(int)pk[4 * kg], (int)pk[4 * kg + 1], (int)pk[4 * kg + 2],
+                                                        (int)pk[4 * kg + 3]});
+#pragma unroll
+          for (int cc = 0; cc < NCC; ++cc)
+            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kg & 1][cc], pf, o[cc], 0, 0, 0);
+        }
+      } else {
+        const v8i pf = v8i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+        v8i vf[NCC];
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) {
+          // operand bytes 16e .. 16e+15 = V^T row 32 cc + li, tokens 32 lh + 16 e ..
+          const int r = vro[cc];
+          const v4i v0 = *(const v4i*)(vs + v8_off(r, 2 * lh));
+          const v4i v1 = *(const v4i*)(vs + v8_off(r, 2 * lh + 1));
+          vf[cc] = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        }
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc)
+          o[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[cc], pf, o[cc], 0, 0, 0, 127, 0, 127);
+      }
+    }
+    if (next) qk_mfma(t + 1);
+  };
+
+  // ---- the schedule.  Both groups run the same program (MFMA phase of tile t, barrier, VALU
+  //      phase of tile t+1, barrier); group B starts it one barrier late and group A ends with
+  //      one extra barrier, so B runs exactly one phase behind A and both pass the same number
+  //      of barriers.  Group A waits for its tile loads at the end of its VALU phases.
+  if (grp == 1) phase_barrier();
+  for (int t = -1; t < nT; ++t) {
+    mfma_phase(t);
+    phase_barrier();
+    if (grp == 0) {   // tile loads overlap this wave's softmax (no LDS reads in the VALU phase)
+      if (t + 2 < nT) dma.k_tile(p, bkv, t + 2, kbuf(t + 2), a);
+      if (t + 1 < nT) dma.v_tile(p, bkv, t + 1, vbuf(t + 1), a);
+    }
+    valu_phase(t + 1);
+    if (grp == 0) wait_vmem();
+    phase_barrier();
   }
+  if (grp == 0) phase_barrier();
 
   // ---- epilogue: O / l (and the FP8 V channel scales); lane (li, lh) holds row qrow,
   //      channels 32cc + 8(r/4) + 4lh + (r%4).
@@ -366,7 +445,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_i8_kernel(Params p) {
 
 template <int D, bool CAUSAL, bool PV8, bool THRIFT, bool VF16, bool OUT_BF16>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
-  using S = Smem<D, PV8, THRIFT>;
+  using S = Smem<D, PV8>;
   auto kern = attn_i8_kernel<D, CAUSAL, PV8, THRIFT, VF16, OUT_BF16>;
   static bool attr_set = false;   // the attribute is per function; setting it twice is harmless
   if (!attr_set) {
@@ -374,7 +453,7 @@ hipError_t launch_cfg(const Params& p, hipStream_t st) {
     attr_set = true;
   }
   if (p.total_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(NTHREADS), S::TOTAL, st, p);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(NTHREADS), S::TOTAL, st, p, p.ks, p.qs, p.mask);
   return hipGetLastError();
 }
 
@@ -402,8 +481,10 @@ hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st) {
   p.mask = a.mask; p.qhi = a.q_hi; p.khi = a.k_hi;
   p.out = a.out;
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
+  p.Np = (a.N + KT - 1) / KT * KT;
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;
-  p.total_wg = a.B * a.Hq * p.nQB;
+  p.nPairs = (p.nQB + 1) / 2;
+  p.total_wg = a.B * a.Hq * p.nPairs;
   p.sm_log2 = a.sm_scale * LOG2E;
   p.tau = pv_fp8 ? 0.0f : 8.0f;
   const bool thrift = a.mask != nullptr;

@@ -57,7 +57,7 @@ int sage_smooth_k(const void* k, sage_fmt dt, sage_shape ks, float* mean_out, vo
 int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* codes_bytes, size_t* scale_bytes) {
   if (!codes_bytes || !scale_bytes || !shape_ok(xs)) return SAGE_EINVAL;
   const int64_t BH = xs.B * xs.H, N = xs.N, D = xs.D;
-  const int64_t Np = roundup(N, 32);
+  const int64_t Np = roundup(N, 64);   // channel-major (token-axis) layouts are padded to 64 tokens
   switch (fmt) {
     case SAGE_INT8:
       if (block.tokens < 1 || block.channels != D) return SAGE_EINVAL;
@@ -66,7 +66,7 @@ int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* 
       return SAGE_OK;
     case SAGE_E4M3:
       if (block.tokens != 0 || block.channels != 1) return SAGE_EINVAL;
-      *codes_bytes = (size_t)(BH * N * D);
+      *codes_bytes = (size_t)(BH * D * Np);
       *scale_bytes = (size_t)(BH * D) * 4;
       return SAGE_OK;
     case SAGE_MXFP4:

@@ -44,9 +44,11 @@ template <bool IS_F16>
 __device__ __forceinline__ float in16_to_f32(uint16_t h) { return IS_F16 ? f16_to_f32(h) : bf16_to_f32(h); }
 template <bool IS_F16>
 __device__ __forceinline__ uint16_t f32_to_in16(float x) { return IS_F16 ? f32_to_f16(x) : f32_to_bf16(x); }
-// two bf16 (RNE) packed in one dword, low half = a
+// two bf16 (RNE) packed in one dword, low half = a: one v_cvt_pk_bf16_f32
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // ---- E4M3 ----------------------------------------------------------------------------

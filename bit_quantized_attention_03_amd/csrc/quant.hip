@@ -106,12 +106,17 @@ __global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* 
   constexpr int PITCH = 80;
   const int64_t run = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = run * 64;
+  const int64_t Np = (N + 63) / 64 * 64;
   const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
   const float* sc = scales + bh * D;
   const int nchunk = 64 * D / 8;
   for (int c = threadIdx.x; c < nchunk; c += 256) {
     const int t = c / (D / 8), c8 = (c % (D / 8)) * 8;
-    if (t >= rows) continue;
+    if (t >= rows) {   // padding tokens: zero codes
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[(c8 + e) * PITCH + t] = 0;
+      continue;
+    }
     v4i raw = *(const v4i*)(x + (bh * N + t0 + t) * D + c8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -122,15 +127,10 @@ __global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* 
     }
   }
   __syncthreads();
-  // each thread stores 4 bytes of one channel row
-  for (int c = threadIdx.x; c < D * 16; c += 256) {
-    const int ch = c / 16, t4 = (c % 16) * 4;
-    uint8_t* dst = codes_t + (bh * D + ch) * N + t0 + t4;
-    if (t4 + 4 <= rows && ((N & 3) == 0)) {
-      *(uint32_t*)dst = *(const uint32_t*)&tile[ch * PITCH + t4];
-    } else {
-      for (int j = 0; j < 4 && t4 + j < rows; ++j) dst[j] = tile[ch * PITCH + t4 + j];
-    }
+  // each thread stores 16 bytes of one channel row (rows are Np = 64-multiple bytes long)
+  for (int c = threadIdx.x; c < D * 4; c += 256) {
+    const int ch = c / 4, t16 = (c % 4) * 16;
+    *(v4i*)(codes_t + (bh * D + ch) * Np + t0 + t16) = *(const v4i*)&tile[ch * PITCH + t16];
   }
 }
 
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restric
 }
 
 // Along tokens (V): block = (64-token run, bh); LDS tile [64][D] of fp32; thread per
-// (channel, group of G tokens).  Output rows are channels, Np = N rounded up to 32.
+// (channel, group of G tokens).  Output rows are channels, Np = N rounded up to 64.
 template <bool F16, bool NV>
 __global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int mode,
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restric
   __shared__ float tile[64][129];
   const int64_t run = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = run * 64;
-  const int64_t Np = (N + 31) / 32 * 32;
+  const int64_t Np = (N + 63) / 64 * 64;
   const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
   for (int c = threadIdx.x; c < 64 * D / 8; c += 256) {
     const int t = c / (D / 8), c8 = (c % (D / 8)) * 8;

@@ -150,7 +150,7 @@ def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
 
 def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
     B, H, N, D = qt.shape
-    Np = (N + 31) // 32 * 32
+    Np = (N + 63) // 64 * 64
     rows, length = (B * H * D, Np) if along_tokens else (B * H * N, D)
     f8 = torch.empty(max(rows * length, 16), dtype=torch.uint8, device=qt.codes.device)
     e8 = torch.empty(max(rows * length // 32, 16), dtype=torch.uint8, device=qt.codes.device)

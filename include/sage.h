@@ -110,11 +110,12 @@ size_t sage_smooth_k_workspace_bytes(sage_shape ks);
  * even, saturating; the scale rules:
  *   INT8 : s = fp32(amax / 127) per block; codes int8 [B,H,N,D]; scales fp32 [B,H,ceil(N/T)].
  *          An all-zero block has s = 0 and codes 0.
- *   E4M3 : s_c = fp32(amax_c / 448) per channel over all tokens; codes u8 [B,H,D,N]
- *          (channel-major: tokens contiguous); scales fp32 [B,H,D].
+ *   E4M3 : s_c = fp32(amax_c / 448) per channel over all tokens; codes u8 [B,H,D,Np]
+ *          (channel-major: tokens contiguous, Np = N rounded up to 64, zero padding);
+ *          scales fp32 [B,H,D].
  *   MXFP4: e = smallest integer with 6 * 2^e >= amax (amax = 0: -127), x * 2^-e is exact.
  *          Along D: codes [B,H,N,D/2], scales E8M0 [B,H,N,D/32].  Along tokens: codes
- *          [B,H,D,Np/2], scales [B,H,D,Np/32], Np = N rounded up to 32 (padding = zeros).
+ *          [B,H,D,Np/2], scales [B,H,D,Np/32], Np = N rounded up to 64 (padding = zeros).
  *          Two codes per byte along the block axis, even element in the low nibble.
  *   NVFP4: baseline scale code c0 = UE4M3(fp32(amax / 6)) (0 becomes 0x01); mode
  *          SAGE_SCALE_SEARCH also evaluates UE4M3(fp32(amax/6) * g_k), g_k = fp32(0.85 +

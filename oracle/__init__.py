@@ -135,16 +135,18 @@ def quant_int8(x16: np.ndarray, dt: int, block_tokens: int):
 
 
 def quant_fp8_channel(v16: np.ndarray, dt: int):
-    """Per-channel E4M3 of V: codes [B,H,D,N] (tokens contiguous), scales [B,H,D]."""
+    """Per-channel E4M3 of V: codes [B,H,D,Np] (tokens contiguous, Np = N rounded up to 64,
+    zero padding), scales [B,H,D]."""
     v16 = _c(v16, np.uint16); B, H, N, D = v16.shape
-    codes = np.empty((B, H, D, N), np.uint8); scales = np.empty((B, H, D), np.float32)
+    Np = (N + 63) // 64 * 64
+    codes = np.empty((B, H, D, Np), np.uint8); scales = np.empty((B, H, D), np.float32)
     _load().orc_quant_fp8_channel(_p(v16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), _p(codes), _p(scales))
     return codes, scales
 
 
 def quant_mxfp4(x16: np.ndarray, dt: int, axis: int):
     x16 = _c(x16, np.uint16); B, H, N, D = x16.shape
-    Np = (N + 31) // 32 * 32
+    Np = (N + 63) // 64 * 64
     rows, length = (N, D) if axis == 0 else (D, Np)
     codes = np.empty((B, H, rows, length // 2), np.uint8); scales = np.empty((B, H, rows, length // 32), np.uint8)
     _load().orc_quant_mxfp4(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), _p(codes), _p(scales))
@@ -155,7 +157,7 @@ def quant_nvfp4(x16: np.ndarray, dt: int, axis: int, mode: int):
     """mode 0 = max-scaling, 1 = ScaleSearch on the 0.85..1.15 grid, 2 = the page's bit offsets [-2, 6].
     Returns (codes, ue4m3 scales, index of the winning candidate per block)."""
     x16 = _c(x16, np.uint16); B, H, N, D = x16.shape
-    Np = (N + 31) // 32 * 32
+    Np = (N + 63) // 64 * 64
     rows, length = (N, D) if axis == 0 else (D, Np)
     codes = np.empty((B, H, rows, length // 2), np.uint8)
     scales = np.empty((B, H, rows, length // 16), np.uint8)

@@ -269,8 +269,9 @@ void orc_quant_int8(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, 
 
 // ----- FP8 E4M3 per-channel quantization of V -----
 // Per (b, h, channel): s_c = fp32(amax_c / 448) over all N tokens, r_c = fp32(1 / s_c),
-// code = E4M3(fp32(v * r_c)).  Codes are written channel-major, [B, H, D, N] (tokens
-// contiguous: the contraction axis of P.V), scales [B, H, D] fp32.
+// code = E4M3(fp32(v * r_c)).  Codes are written channel-major, [B, H, D, Np] with Np = N
+// rounded up to 64 and zero codes in the padding (tokens contiguous: the contraction axis of
+// P.V), scales [B, H, D] fp32.
 void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int64_t N, int64_t D,
                            uint8_t* codes_t, float* scales) {
   for (int64_t b = 0; b < B; ++b)
@@ -281,8 +282,9 @@ void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int6
         float s = amax / 448.0f;
         scales[(b * H + h) * D + c] = s;
         float r = s > 0.0f ? 1.0f / s : 0.0f;
-        for (int64_t t = 0; t < N; ++t)
-          codes_t[((b * H + h) * D + c) * N + t] = e4m3_encode(in_value(v, idx4(b, h, t, c, H, N, D), dt) * r);
+        const int64_t Np = (N + 63) / 64 * 64;
+        for (int64_t t = 0; t < Np; ++t)
+          codes_t[((b * H + h) * D + c) * Np + t] = t < N ? e4m3_encode(in_value(v, idx4(b, h, t, c, H, N, D), dt) * r) : 0;
       }
 }
 
@@ -293,12 +295,12 @@ void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int6
 // fits); element code = E2M1(x * 2^-e), exact scaling so the only rounding is E2M1's.
 // Packing: two codes per byte along the block axis, even element in the low nibble.
 // axis 0: codes [B,H,N,D/2], scales [B,H,N,D/32].
-// axis 1: codes [B,H,D,Np/2], scales [B,H,D,Np/32] with Np = N rounded up to 32 (the
+// axis 1: codes [B,H,D,Np/2], scales [B,H,D,Np/32] with Np = N rounded up to 64 (the
 //         padding tokens are zeros).
 void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis,
                      uint8_t* codes, uint8_t* scales) {
   const int64_t G = 32;
-  int64_t Np = (N + G - 1) / G * G;
+  int64_t Np = (N + 63) / 64 * 64;
   int64_t rows = axis == 0 ? N : D;        // rows of the output layout
   int64_t len = axis == 0 ? D : Np;        // elements along the block axis
   for (int64_t b = 0; b < B; ++b)
@@ -342,7 +344,7 @@ void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
 // in fp32 as a balanced pairwise tree in index order ((se0+se1)+(se2+se3))+...; the
 // first candidate with a strictly smaller sum wins (ties keep the earlier candidate).
 // axis 0: codes [B,H,N,D/2], scales [B,H,N,D/16];  axis 1: codes [B,H,D,Np/2], scales
-// [B,H,D,Np/16] with Np = N rounded up to 32.
+// [B,H,D,Np/16] with Np = N rounded up to 64.
 float nv_block_sse(const float* x, float s, uint8_t* codes_out) {
   float r = 1.0f / s;
   float se[16];
@@ -361,7 +363,7 @@ float nv_block_sse(const float* x, float s, uint8_t* codes_out) {
 void orc_quant_nvfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis, int mode,
                      uint8_t* codes, uint8_t* scales, uint8_t* chosen /* nullable: index of winning candidate */) {
   const int64_t G = 16;
-  int64_t Np = (N + 31) / 32 * 32;
+  int64_t Np = (N + 63) / 64 * 64;
   int64_t rows = axis == 0 ? N : D;
   int64_t len = axis == 0 ? D : Np;
   double grid[8];
@@ -518,7 +520,7 @@ struct orc_attn_args {
   // high-precision Q / K_s (16-bit patterns, dtype hi_dt): QK_HI tiles and Thrift-selected tiles
   const uint16_t* q_hi; const uint16_t* k_hi; int32_t hi_dt;
   const uint8_t* thrift_mask;  // nullable [B,Hq,nQB,nKB]; 1 = this tile uses q_hi/k_hi
-  // V: V_HI 16-bit [B,Hkv,N,D] (v_dt; rounded to bf16 before use); V_E4M3 codes [B,Hkv,D,N] + fp32 [B,Hkv,D];
+  // V: V_HI 16-bit [B,Hkv,N,D] (v_dt; rounded to bf16 before use); V_E4M3 codes [B,Hkv,D,Np] + fp32 [B,Hkv,D];
   //    V_MXFP4 packed [B,Hkv,D,Np/2] + E8M0 [B,Hkv,D,Np/32]; V_MXFP8 E4M3 [B,Hkv,D,Np] + E8M0 [B,Hkv,D,Np/32]
   const uint16_t* v_hi; int32_t v_dt;
   const uint8_t* v_lp; const float* v_s; const uint8_t* v_e8;
@@ -576,7 +578,7 @@ inline uint8_t nib(const uint8_t* base, int64_t i) { uint8_t b = base[i / 2]; re
 void orc_attention(const orc_attn_args* a) {
   const int64_t B = a->B, Hq = a->Hq, Hkv = a->Hkv, N = a->N, D = a->D, QB = a->q_block, KB = a->k_block;
   const int64_t nQB = (N + QB - 1) / QB, nKB = (N + KB - 1) / KB;
-  const int64_t Np = (N + 31) / 32 * 32;
+  const int64_t Np = (N + 63) / 64 * 64;   // padded token count of channel-major V layouts
   const double NEG_INF = -std::numeric_limits<double>::infinity();
   const bool need_hi = a->qk_fmt == QK_HI || a->thrift_mask != nullptr;
   (void)B;
@@ -618,7 +620,7 @@ void orc_attention(const orc_attn_args* a) {
         double v;
         switch (a->v_fmt) {
           case V_HI: v = bf16_decode(bf16_encode(in_value(a->v_hi, idx4(b, g, t, c, Hkv, N, D), a->v_dt))); break;
-          case V_E4M3: v = e4m3_decode(a->v_lp[((b * Hkv + g) * D + c) * N + t]); break;
+          case V_E4M3: v = e4m3_decode(a->v_lp[((b * Hkv + g) * D + c) * Np + t]); break;
           case V_MXFP4: {
             int e = (int)a->v_e8[((b * Hkv + g) * D + c) * (Np / 32) + t / 32] - 127;
             v = e2m1_decode(nib(a->v_lp + ((b * Hkv + g) * D + c) * (Np / 2), t)) * std::ldexp(1.0, e);

@@ -47,8 +47,9 @@ def test_quantized_bytes(L):
     assert sage.quantized_bytes(sage.INT8, (128, 128), (4, 32, 4096, 128)) == (4 * 32 * 4096 * 128, 4 * 32 * 32 * 4)
     assert sage.quantized_bytes(sage.E4M3, (0, 1), (2, 24, 16384, 64)) == (2 * 24 * 16384 * 64, 2 * 24 * 64 * 4)
     assert sage.quantized_bytes(sage.MXFP4, (1, 32), (2, 16, 8192, 128)) == (2 * 16 * 8192 * 64, 2 * 16 * 8192 * 4)
-    assert sage.quantized_bytes(sage.MXFP4, (32, 1), (1, 1, 200, 64)) == (64 * 224 // 2, 64 * 224 // 32)
-    assert sage.quantized_bytes(sage.NVFP4, (16, 1), (1, 1, 200, 64)) == (64 * 224 // 2, 64 * 224 // 16)
+    assert sage.quantized_bytes(sage.MXFP4, (32, 1), (1, 1, 200, 64)) == (64 * 256 // 2, 64 * 256 // 32)
+    assert sage.quantized_bytes(sage.NVFP4, (16, 1), (1, 1, 200, 64)) == (64 * 256 // 2, 64 * 256 // 16)
+    assert sage.quantized_bytes(sage.E4M3, (0, 1), (1, 2, 200, 64)) == (2 * 64 * 256, 2 * 64 * 4)
     with pytest.raises(sage.SageError):
         sage.quantized_bytes(sage.MXFP4, (1, 16), (1, 1, 64, 64))     # MX blocks are 32 wide
     with pytest.raises(sage.SageError):

@@ -83,7 +83,7 @@ def test_mxfp4_and_fp8_operands_are_dequantized_products():
     ops = oracle.AttnOperands(qk_fmt=oracle.QK_MXFP4, p_fmt=oracle.P_EXACT, v_fmt=oracle.V_E4M3,
                               q_lp=qc, q_e8=qe, k_lp=kc, k_e8=ke, v_lp=vc, v_s=vs)
     out = oracle.attention(ops, 1, 1, 1, 160, 64, False, 0.125)
-    vd = np.swapaxes(oracle.e4m3_decode(vc) * vs[..., None], 2, 3)
+    vd = np.swapaxes(oracle.e4m3_decode(vc[..., :160]) * vs[..., None], 2, 3)
     ref = oracle.attention_ref(dq(qc, qe), dq(kc, ke), vd, False, 0.125)
     assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
 

@@ -111,6 +111,9 @@ def test_fp8_channel_half_step(llm_small):
     codes, scales = oracle.quant_fp8_channel(vb, oracle.BF16)
     x = _val(vb)                                  # [B,H,N,D]
     xt = np.swapaxes(x, 2, 3)                     # [B,H,D,N] like the codes
+    N = x.shape[2]
+    assert np.all(codes[..., N:] == 0)            # padding to a multiple of 64 tokens
+    codes = codes[..., :N]
     s = scales.astype(np.float64)[..., None]
     rec = oracle.e4m3_decode(codes) * s
     # half an E4M3 step: relative 2^-4 for normals, absolute 2^-10 * s for subnormals
@@ -152,7 +155,7 @@ def _nv_blocks(x16, axis):
     x = _val(x16)
     if axis == 1:
         x = np.swapaxes(x, 2, 3)
-        pad = (-x.shape[-1]) % 32
+        pad = (-x.shape[-1]) % 64
         x = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,))], axis=-1)
     return x.reshape(-1, 16)
 
