@@ -31,15 +31,25 @@ HBM_GBS = 8000.0
 DEFAULT_VARIANT = {"tiny_int8": "int8", "llm_int8": "int8", "video_fp8": "int8_fp8pv", "fp4_search": "mxfp4",
                    "thrift_long": "thrift"}
 VARIANT_PEAK = {"int8": "int8", "thrift": "int8", "int8_fp8pv": "int8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
+PV_PEAK = {"int8": "bf16", "thrift": "bf16", "int8_fp8pv": "fp8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
 VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "int8_fp8pv": "int8+fp8", "mxfp4": "mxfp4",
                  "nvfp4_search": "nvfp4->mxfp8"}
 
 
-def attention_kernel_hash() -> str:
+KERNEL_SOURCES = {"int8": "attn_i8.hip", "thrift": "attn_i8.hip", "int8_fp8pv": "attn_i8.hip",
+                  "mxfp4": "attn_mx.hip", "nvfp4_search": "attn_mx.hip"}
+
+
+def attention_kernel_hash(variant: str) -> str:
+    """Hash of the sources the variant's attention kernel is built from."""
     h = hashlib.sha256()
-    for f in ("attn_i8.hip", "attn_mx.hip", "device.hpp"):
+    for f in (KERNEL_SOURCES[variant], "device.hpp"):
         h.update(open(os.path.join(ROOT, "bit_quantized_attention_03_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def traffic_key(workload: str, causal: bool, variant: str) -> str:
+    return f"{workload}:{'causal' if causal else 'noncausal'}:{variant}"
 
 
 def load_traffic(workload: str, causal: bool, variant: str):
@@ -49,10 +59,10 @@ def load_traffic(workload: str, causal: bool, variant: str):
     if not os.path.exists(path):
         return None
     try:
-        rec = json.load(open(path)).get(f"{workload}:{'causal' if causal else 'noncausal'}:{variant}")
+        rec = json.load(open(path)).get(traffic_key(workload, causal, variant))
     except Exception:
         return None
-    if not rec or rec.get("kernel_hash") != attention_kernel_hash():
+    if not rec or rec.get("kernel_hash") != attention_kernel_hash(variant):
         return None
     return rec.get("bytes_per_launch")
 
@@ -64,7 +74,10 @@ def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float):
     from tests.parity import oracle_pass
 
     threads = min(16, oracle.hardware_threads())
-    heads = [(0, 0), (w.B - 1, w.Hq - 1), (w.B // 2, w.Hq // 2), (0, w.Hq - 1), (w.B - 1, 0)]
+    # whole heads, spread over the batch and head axes, until the time budget is spent
+    order = sorted(range(w.B * w.Hq), key=lambda i: ((i * 2654435761) & 0xFFFFFFFF, i))
+    heads = [(0, 0), (w.B - 1, w.Hq - 1)] + [(i // w.Hq, i % w.Hq) for i in order
+                                              if (i // w.Hq, i % w.Hq) not in ((0, 0), (w.B - 1, w.Hq - 1))]
     g = w.Hq // w.Hkv
     ops = 0.0
     done = []
@@ -84,6 +97,50 @@ def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float):
                       f"{' causal' if causal else ''}: smoothing + quantization + tiled attention, {t:.1f} s"}
 
 
+def calibrate_copy(n: int = 1 << 28, reps: int = 3):
+    """Run the library's plain fp32 -> bf16 conversion kernel (reads 4n bytes, writes 2n) so
+    rocprofv3's FETCH_SIZE / WRITE_SIZE can be scaled by what they read for known traffic."""
+    import torch
+    from bit_quantized_attention_03_amd import sage
+    x = torch.randn(n, device="cuda:0")
+    for _ in range(reps):
+        sage.convert_f32(x, sage.BF16)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "convert_kernel", "read_bytes": 4 * n, "write_bytes": 2 * n, "reps": reps}))
+
+
+def _pmc_mean_kib(run_dir: str, kernel_re: str, counter: str) -> float:
+    import csv
+    import glob
+    import re
+    vals = []
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] == counter and re.search(kernel_re, row["Kernel_Name"]):
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for /{kernel_re}/ under {run_dir}")
+    return sum(vals) / len(vals)
+
+
+def traffic_from(dirs, key: str, kernel_re: str, out_path: str):
+    """Turn four rocprofv3 --pmc runs (attention FETCH_SIZE, attention WRITE_SIZE, calibration
+    FETCH_SIZE, calibration WRITE_SIZE; KiB per dispatch) into HBM bytes per attention launch,
+    each counter scaled by known-bytes / counter-bytes of the calibration kernel."""
+    fa, wa, fc, wc = dirs
+    n = 1 << 28
+    f_scale = 4 * n / (_pmc_mean_kib(fc, "convert_kernel", "FETCH_SIZE") * 1024)
+    w_scale = 2 * n / (_pmc_mean_kib(wc, "convert_kernel", "WRITE_SIZE") * 1024)
+    fetch = _pmc_mean_kib(fa, kernel_re, "FETCH_SIZE") * 1024 * f_scale
+    write = _pmc_mean_kib(wa, kernel_re, "WRITE_SIZE") * 1024 * w_scale
+    db = json.load(open(out_path)) if os.path.exists(out_path) else {}
+    db[key] = {"kernel_hash": attention_kernel_hash(key.split(":")[2]), "bytes_per_launch": round(fetch + write),
+               "fetch_bytes": round(fetch), "write_bytes": round(write),
+               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}
+    json.dump(db, open(out_path, "w"), indent=1, sort_keys=True)
+    print(json.dumps({key: db[key]}))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +151,11 @@ def main():
     ap.add_argument("--causal", action="store_true", help="causal mask (the thrift workload is always causal)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the known-size conversion kernel (for counter calibration)")
+    ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
+                    help="rocprofv3 --pmc output dirs: attn FETCH_SIZE, attn WRITE_SIZE, calibration "
+                         "FETCH_SIZE, calibration WRITE_SIZE; writes profiles/attn_traffic.json")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -101,13 +163,18 @@ def main():
               "(heads shard across GPUs with no exchange; see the design notes). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    import torch
+    if args.calibrate_copy:
+        return calibrate_copy()
     from bit_quantized_attention_03_amd import inputs as I
-    from bit_quantized_attention_03_amd import sage
-
     w = I.workload(args.workload)
     variant = args.variant or DEFAULT_VARIANT[w.name]
     causal = bool(args.causal or w.causal)
+    if args.traffic_from:
+        return traffic_from(args.traffic_from, traffic_key(w.name, causal, variant), "attn_",
+                            os.path.join(ROOT, "profiles", "attn_traffic.json"))
+
+    import torch
+    from bit_quantized_attention_03_amd import sage
     dev = torch.device("cuda:0")
     q_cpu, k_cpu, v_cpu = I.make_qkv(w, seed=0)
     q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
@@ -162,6 +229,8 @@ def main():
 
     achieved = ops / (attn_ms * 1e-3) / 1e12
     peak = PEAK[VARIANT_PEAK[variant]]
+    # half the counted ops are QK^T, half P.V: the ceiling of the pair of MFMA dtypes used
+    mixed = 1.0 / (0.5 / peak + 0.5 / PEAK[PV_PEAK[variant]])
     traffic = load_traffic(w.name, causal, variant)
     rec = {
         "metric": "quantized attention fwd TOPS (4*B*H*N^2*d/t) at d=128 N=4096 + % of MFMA peak",
@@ -181,7 +250,8 @@ def main():
                    "step": "smooth_k + quantize + " + ("thrift_select + " if variant == "thrift" else "") + "attn_fwd"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "kernel": "attn_fwd", "kernel_ms": round(attn_ms, 4)},
+                     "kernel": "attn_fwd", "kernel_ms": round(attn_ms, 4),
+                     "qk_pv_peak": round(mixed, 1), "qk_pv_frac": round(achieved / mixed, 4)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, variant, args.cpu_seconds)
