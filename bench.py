@@ -36,14 +36,14 @@ VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "int8_fp8pv": "int8
                  "nvfp4_search": "nvfp4->mxfp8"}
 
 
-KERNEL_SOURCES = {"int8": "attn_i8.hip", "thrift": "attn_i8.hip", "int8_fp8pv": "attn_i8.hip",
-                  "mxfp4": "attn_mx.hip", "nvfp4_search": "attn_mx.hip"}
+KERNEL_SOURCES = {"int8": ("attn_i8.hip",), "thrift": ("attn_i8.hip",), "int8_fp8pv": ("attn_i8.hip",),
+                  "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp")}
 
 
 def attention_kernel_hash(variant: str) -> str:
     """Hash of the sources the variant's attention kernel is built from."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[variant], "device.hpp"):
+    for f in (*KERNEL_SOURCES[variant], "device.hpp"):
         h.update(open(os.path.join(ROOT, "bit_quantized_attention_03_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

@@ -117,12 +117,16 @@ int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt 
   }
 }
 
-int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t len, void* f8_out,
+int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, int along_tokens, void* f8_out,
                         void* e8m0_out, hipStream_t stream) {
-  if (!codes || !scales || !f8_out || !e8m0_out || rows < 0 || len < 0 || len % 32) return SAGE_EINVAL;
+  if (!codes || !scales || !f8_out || !e8m0_out || !shape_ok(xs)) return SAGE_EINVAL;
+  if (along_tokens != 0 && along_tokens != 1) return SAGE_EINVAL;
+  if (!along_tokens && xs.D % 32) return SAGE_EINVAL;
   if (!aligned16(codes) || !aligned16(f8_out)) return SAGE_EALIGN;
-  return launched(launch_nvfp4_to_mxfp8((const uint8_t*)codes, (const uint8_t*)scales, rows, len, (uint8_t*)f8_out,
-                                        (uint8_t*)e8m0_out, stream));
+  const int64_t Np = roundup(xs.N, 64);
+  const int64_t rows = along_tokens ? xs.B * xs.H * xs.D : xs.B * xs.H * xs.N, len = along_tokens ? Np : xs.D;
+  return launched(launch_nvfp4_to_mxfp8((const uint8_t*)codes, (const uint8_t*)scales, rows, len,
+                                        along_tokens ? (int)xs.D : 0, (uint8_t*)f8_out, (uint8_t*)e8m0_out, stream));
 }
 
 int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
@@ -169,17 +173,15 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
     return SAGE_ENOTSUP;
   }
   if (p->block_mask) return SAGE_ENOTSUP;
-  if (q->fmt == SAGE_MXFP4 && k->fmt == SAGE_MXFP4 && v->fmt == SAGE_MXFP4 && p->p_fmt == SAGE_MXFP4) {
-    if (!q->scales || !k->scales || !v->scales) return SAGE_EINVAL;
-    if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
-    return launched(launch_attn_mx(a, 0, stream));
-  }
-  if (q->fmt == SAGE_MXFP8 && k->fmt == SAGE_MXFP8 && v->fmt == SAGE_MXFP8 && p->p_fmt == SAGE_NVFP4) {
-    if (!q->scales || !k->scales || !v->scales) return SAGE_EINVAL;
-    if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
-    return launched(launch_attn_mx(a, 1, stream));
-  }
-  return SAGE_ENOTSUP;
+  const bool mx4 = q->fmt == SAGE_MXFP4 && k->fmt == SAGE_MXFP4 && v->fmt == SAGE_MXFP4 && p->p_fmt == SAGE_MXFP4;
+  const bool mx8 = q->fmt == SAGE_MXFP8 && k->fmt == SAGE_MXFP8 && v->fmt == SAGE_MXFP8 && p->p_fmt == SAGE_NVFP4;
+  if (!mx4 && !mx8) return SAGE_ENOTSUP;
+  if (!q->scales || !k->scales || !v->scales) return SAGE_EINVAL;
+  if (qs.D != 128) return SAGE_ENOTSUP;   // the microscaled kernels are built for D = 128
+  // scale bytes are read as dwords (4 per Q/K row, 2*D per V tile)
+  if ((uintptr_t)q->scales % 4 || (uintptr_t)k->scales % 4 || (uintptr_t)v->scales % 4) return SAGE_EALIGN;
+  if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
+  return launched(launch_attn_mx(a, mx4 ? 0 : 1, stream));
 }
 
 size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_block) {

@@ -17,7 +17,9 @@ hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int6
                                     float* scales, hipStream_t st);
 hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
                             int mode, uint8_t* codes, uint8_t* scales, hipStream_t st);
-hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len,
+// rows x len elements along the block axis; D_tok = 0 along D, else the channel count of a
+// token-axis (V) layout whose scales are token-group major.
+hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len, int D_tok,
                                  uint8_t* f8, uint8_t* e8, hipStream_t st);
 hipError_t launch_convert_f32(const float* x, int64_t n, int fmt, void* out, hipStream_t st);
 

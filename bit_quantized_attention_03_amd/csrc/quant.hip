@@ -233,7 +233,8 @@ __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restric
 }
 
 // Along tokens (V): block = (64-token run, bh); LDS tile [64][D] of fp32; thread per
-// (channel, group of G tokens).  Output rows are channels, Np = N rounded up to 64.
+// (channel, group of G tokens).  Code rows are channels, Np = N rounded up to 64; scales
+// are token-group major [Np/G][D], so consecutive threads write consecutive bytes.
 template <bool F16, bool NV>
 __global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int mode,
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
@@ -266,24 +267,34 @@ __global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restric
     const int64_t tok = t0 + g * G;
     if (NV) {
       uint32_t c[2];
-      scales[(bh * D + ch) * (Np / 16) + tok / 16] = (uint8_t)nv_quant16(v, mode, c);
+      scales[(bh * (Np / 16) + tok / 16) * D + ch] = (uint8_t)nv_quant16(v, mode, c);
       *(v2i*)(codes + (bh * D + ch) * (Np / 2) + tok / 2) = v2i{(int)c[0], (int)c[1]};
     } else {
       uint32_t c[4];
-      scales[(bh * D + ch) * (Np / 32) + tok / 32] = (uint8_t)mx_quant32(v, c);
+      scales[(bh * (Np / 32) + tok / 32) * D + ch] = (uint8_t)mx_quant32(v, c);
       *(v4i*)(codes + (bh * D + ch) * (Np / 2) + tok / 2) = v4i{(int)c[0], (int)c[1], (int)c[2], (int)c[3]};
     }
   }
 }
 
 // ------------------------------------------------------------------ NVFP4 -> MXFP8
+// One thread per 32-element group; group gid = row * gpr + j of `rows` code rows with gpr
+// groups each.  Along D the scale bytes follow the codes' row order; along tokens
+// (rows = bh * D + channel) they are token-group major: [bh][group][D].
 __global__ __launch_bounds__(256) void nv_to_mx8_kernel(const uint8_t* __restrict__ codes,
-                                                        const uint8_t* __restrict__ scales, int64_t groups,
-                                                        uint8_t* __restrict__ f8, uint8_t* __restrict__ e8) {
+                                                        const uint8_t* __restrict__ scales, int64_t groups, int64_t gpr,
+                                                        int D_tok, uint8_t* __restrict__ f8, uint8_t* __restrict__ e8) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // one 32-element group
   if (gid >= groups) return;
   v4i raw = *(const v4i*)(codes + gid * 16);
-  const float s0 = e4m3_to_f32(scales[gid * 2]), s1 = e4m3_to_f32(scales[gid * 2 + 1]);
+  int64_t nv0, nv1, mx;   // scale byte indices: NVFP4 groups 2j, 2j+1 and the MXFP8 group j
+  if (D_tok == 0) {
+    nv0 = gid * 2; nv1 = nv0 + 1; mx = gid;
+  } else {
+    const int64_t row = gid / gpr, j = gid % gpr, bh = row / D_tok, ch = row % D_tok;
+    nv0 = (bh * 2 * gpr + 2 * j) * D_tok + ch; nv1 = nv0 + D_tok; mx = (bh * gpr + j) * D_tok + ch;
+  }
+  const float s0 = e4m3_to_f32(scales[nv0]), s1 = e4m3_to_f32(scales[nv1]);
   float xh[32];
   float A = 0.0f;
 #pragma unroll
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(256) void nv_to_mx8_kernel(const uint8_t* __restric
     A = __builtin_fmaxf(A, __builtin_fabsf(xh[i]));
   }
   const int E = mx_exp_e4m3(A);
-  e8[gid] = (uint8_t)(E + 127);
+  e8[mx] = (uint8_t)(E + 127);
   v8i out;
 #pragma unroll
   for (int w = 0; w < 8; ++w)
@@ -375,11 +386,11 @@ hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, i
   return hipGetLastError();
 }
 
-hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len,
+hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len, int D_tok,
                                  uint8_t* f8, uint8_t* e8, hipStream_t st) {
   const int64_t groups = rows * (len / 32);
   if (groups == 0) return hipSuccess;
-  nv_to_mx8_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, st>>>(codes, scales, groups, f8, e8);
+  nv_to_mx8_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, st>>>(codes, scales, groups, len / 32, D_tok, f8, e8);
   return hipGetLastError();
 }
 

@@ -58,8 +58,7 @@ def lib():
         L.sage_quantize_blocks.argtypes = [C.c_void_p, C.c_int, Shape, C.c_int, Block, C.c_int, C.c_void_p, C.c_void_p,
                                            C.c_void_p]
         L.sage_quantized_bytes.argtypes = [C.c_int, Block, Shape, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
-        L.sage_nvfp4_to_mxfp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
-                                          C.c_void_p]
+        L.sage_nvfp4_to_mxfp8.argtypes = [C.c_void_p, C.c_void_p, Shape, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
         L.sage_attn_fwd.argtypes = [C.POINTER(QTensorC), C.POINTER(QTensorC), C.POINTER(QTensorC),
                                     C.POINTER(AttnParamsC), C.c_void_p, C.c_int, C.c_void_p]
         L.thrift_select_blocks.argtypes = [C.c_void_p, C.c_void_p, C.c_int, Shape, Shape, C.c_int, C.c_int, C.c_double,
@@ -149,14 +148,16 @@ def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
 
 
 def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
+    """NVFP4 codes and UE4M3 scales (as sage_quantize_blocks wrote them) -> E4M3 codes with
+    E8M0 scales per 32 elements, the operand form of the scaled FP8 matrix product."""
     B, H, N, D = qt.shape
     Np = (N + 63) // 64 * 64
-    rows, length = (B * H * D, Np) if along_tokens else (B * H * N, D)
-    f8 = torch.empty(max(rows * length, 16), dtype=torch.uint8, device=qt.codes.device)
-    e8 = torch.empty(max(rows * length // 32, 16), dtype=torch.uint8, device=qt.codes.device)
-    _check("sage_nvfp4_to_mxfp8", lib().sage_nvfp4_to_mxfp8(_ptr(qt.codes), _ptr(qt.scales), rows, length, _ptr(f8),
-                                                            _ptr(e8), _stream()))
-    return QT(MXFP8, f8[:rows * length], e8[:rows * length // 32], qt.shape)
+    n = B * H * (D * Np if along_tokens else N * D)
+    f8 = torch.empty(max(n, 16), dtype=torch.uint8, device=qt.codes.device)
+    e8 = torch.empty(max(n // 32, 16), dtype=torch.uint8, device=qt.codes.device)
+    _check("sage_nvfp4_to_mxfp8", lib().sage_nvfp4_to_mxfp8(_ptr(qt.codes), _ptr(qt.scales), Shape(*qt.shape),
+                                                            int(along_tokens), _ptr(f8), _ptr(e8), _stream()))
+    return QT(MXFP8, f8[:n], e8[:n // 32], qt.shape)
 
 
 def attn_fwd(q: QT, k: QT, v: QT, causal: bool, p_fmt: int, sm_scale: float = 0.0,

@@ -115,14 +115,16 @@ size_t sage_smooth_k_workspace_bytes(sage_shape ks);
  *          scales fp32 [B,H,D].
  *   MXFP4: e = smallest integer with 6 * 2^e >= amax (amax = 0: -127), x * 2^-e is exact.
  *          Along D: codes [B,H,N,D/2], scales E8M0 [B,H,N,D/32].  Along tokens: codes
- *          [B,H,D,Np/2], scales [B,H,D,Np/32], Np = N rounded up to 64 (padding = zeros).
+ *          [B,H,D,Np/2], Np = N rounded up to 64 (padding = zeros), scales [B,H,Np/32,D]
+ *          (token-group major: the scales of 64 consecutive tokens are 2*D bytes).
  *          Two codes per byte along the block axis, even element in the low nibble.
  *   NVFP4: baseline scale code c0 = UE4M3(fp32(amax / 6)) (0 becomes 0x01); mode
  *          SAGE_SCALE_SEARCH also evaluates UE4M3(fp32(amax/6) * g_k), g_k = fp32(0.85 +
  *          k * 0.3 / 7), k = 0..7; SAGE_SCALE_SEARCH_OFFSETS evaluates c0 + f for f in
  *          {-2,-1,1,..,6} within 0x01..0x7E.  Each candidate's squared error is summed in
  *          fp32 as the balanced index-order pairwise tree; the first strictly smaller sum
- *          wins (c0 first).  Layout as MXFP4 with one scale byte per 16 elements.
+ *          wins (c0 first).  Layout as MXFP4 with one scale byte per 16 elements
+ *          (along tokens: scales [B,H,Np/16,D]).
  * Scale mode must be SAGE_SCALE_ABSMAX except for SAGE_NVFP4.                            */
 int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
                          sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream);
@@ -132,9 +134,11 @@ int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* 
 /* NVFP4 -> MXFP8, the operand form the gfx950 matrix cores take for NVFP4 data (they have
  * no UE4M3-scaled FP4 product).  For each 32 elements along the block axis: xhat = E2M1 x
  * UE4M3 (exact), A = max |xhat|, E = smallest integer with 448 * 2^E >= A (A = 0: -127),
- * f = E4M3(xhat * 2^-E).  `rows` x `len` elements: codes [rows, len/2], scales [rows,
- * len/16] in; f8 [rows, len], e8m0 [rows, len/32] out.  len must be a multiple of 32.     */
-int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int64_t len, void* f8_out,
+ * f = E4M3(xhat * 2^-E).  xs is the shape of the tensor that was quantized; codes and
+ * scales are sage_quantize_blocks' NVFP4 outputs along D (along_tokens = 0: D a multiple
+ * of 32) or along tokens (1).  Out: f8 one E4M3 byte per element ([B,H,N,D] or [B,H,D,Np])
+ * and E8M0 scales laid out like MXFP4's ([B,H,N,D/32] or [B,H,Np/32,D]).                 */
+int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, int along_tokens, void* f8_out,
                         void* e8m0_out, hipStream_t stream);
 
 /* Fused quantized attention forward — SageAttention (8-bit QK^T, 16-bit P.V), SageAttention3
@@ -151,7 +155,9 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, int64_t rows, int
  *   q, k SAGE_MXFP4 (along D) + v SAGE_MXFP4 (along tokens) + p SAGE_MXFP4 (per 32 keys)
  *   q, k SAGE_MXFP8 (along D) + v SAGE_MXFP8 (along tokens) + p SAGE_NVFP4 (max-scaled per
  *        16 keys, then to MXFP8 like sage_nvfp4_to_mxfp8)
- * out: [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16).  D in {64, 128}.                    */
+ * out: [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16).  D in {64, 128} for the INT8 sets;
+ * the microscaled sets take D = 128 (else SAGE_ENOTSUP) and 4-byte aligned scale arrays
+ * (else SAGE_EALIGN); their running max is exact (P is quantized relative to it).        */
 int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
                   void* out, sage_fmt out_dt, hipStream_t stream);
 

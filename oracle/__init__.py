@@ -148,7 +148,8 @@ def quant_mxfp4(x16: np.ndarray, dt: int, axis: int):
     x16 = _c(x16, np.uint16); B, H, N, D = x16.shape
     Np = (N + 63) // 64 * 64
     rows, length = (N, D) if axis == 0 else (D, Np)
-    codes = np.empty((B, H, rows, length // 2), np.uint8); scales = np.empty((B, H, rows, length // 32), np.uint8)
+    codes = np.empty((B, H, rows, length // 2), np.uint8)
+    scales = np.empty((B, H, rows, length // 32) if axis == 0 else (B, H, Np // 32, D), np.uint8)
     _load().orc_quant_mxfp4(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), _p(codes), _p(scales))
     return codes, scales
 
@@ -160,21 +161,25 @@ def quant_nvfp4(x16: np.ndarray, dt: int, axis: int, mode: int):
     Np = (N + 63) // 64 * 64
     rows, length = (N, D) if axis == 0 else (D, Np)
     codes = np.empty((B, H, rows, length // 2), np.uint8)
-    scales = np.empty((B, H, rows, length // 16), np.uint8)
-    chosen = np.empty((B, H, rows, length // 16), np.uint8)
+    sshape = (B, H, rows, length // 16) if axis == 0 else (B, H, Np // 16, D)
+    scales = np.empty(sshape, np.uint8)
+    chosen = np.empty(sshape, np.uint8)
     _load().orc_quant_nvfp4(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), C.c_int(mode),
                             _p(codes), _p(scales), _p(chosen))
     return codes, scales, chosen
 
 
-def nvfp4_to_mxfp8(codes: np.ndarray, scales: np.ndarray):
-    """NVFP4 (packed E2M1 [..., len/2], UE4M3 [..., len/16]) -> (E4M3 [..., len], E8M0 [..., len/32])."""
+def nvfp4_to_mxfp8(codes: np.ndarray, scales: np.ndarray, N: int, D: int, axis: int):
+    """NVFP4 in quant_nvfp4's layout for `axis` -> (E4M3 codes, E8M0 scales): along D
+    [B,H,N,D] + [B,H,N,D/32]; along tokens [B,H,D,Np] + [B,H,Np/32,D]."""
     codes = _c(codes, np.uint8); scales = _c(scales, np.uint8)
-    length = codes.shape[-1] * 2
-    rows = codes.size // (length // 2)
-    f8 = np.empty(codes.shape[:-1] + (length,), np.uint8)
-    e8 = np.empty(codes.shape[:-1] + (length // 32,), np.uint8)
-    _load().orc_nvfp4_to_mxfp8(_p(codes), _p(scales), _i(rows), _i(length), _p(f8), _p(e8))
+    B, H = codes.shape[:2]
+    Np = (N + 63) // 64 * 64
+    if axis == 0:
+        f8 = np.empty((B, H, N, D), np.uint8); e8 = np.empty((B, H, N, D // 32), np.uint8)
+    else:
+        f8 = np.empty((B, H, D, Np), np.uint8); e8 = np.empty((B, H, Np // 32, D), np.uint8)
+    _load().orc_nvfp4_to_mxfp8(_p(codes), _p(scales), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), _p(f8), _p(e8))
     return f8, e8
 
 

@@ -288,6 +288,12 @@ void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int6
       }
 }
 
+// Scale byte of (head bh, layout row r, group g) for `groups` groups per row: row major
+// along D (axis 0); group major along tokens (axis 1, rows = channels).
+inline int64_t scale_index(int64_t bh, int64_t r, int64_t g, int64_t rows, int64_t groups, int axis) {
+  return axis == 0 ? (bh * rows + r) * groups + g : (bh * groups + g) * rows + r;
+}
+
 // ----- MX-FP4 (E2M1 elements, one E8M0 scale per 32 elements) -----
 // Used by SageAttention3's microscaled FP4 attention.  The block runs along the
 // contraction axis: axis 0 = along D (Q, K), axis 1 = along tokens (V).
@@ -295,8 +301,9 @@ void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int6
 // fits); element code = E2M1(x * 2^-e), exact scaling so the only rounding is E2M1's.
 // Packing: two codes per byte along the block axis, even element in the low nibble.
 // axis 0: codes [B,H,N,D/2], scales [B,H,N,D/32].
-// axis 1: codes [B,H,D,Np/2], scales [B,H,D,Np/32] with Np = N rounded up to 64 (the
-//         padding tokens are zeros).
+// axis 1: codes [B,H,D,Np/2] with Np = N rounded up to 64 (the padding tokens are zeros),
+//         scales [B,H,Np/32,D] (token block major: the scales of 64 consecutive tokens
+//         are 2*D consecutive bytes).
 void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis,
                      uint8_t* codes, uint8_t* scales) {
   const int64_t G = 32;
@@ -315,7 +322,7 @@ void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
             amax = std::max(amax, std::fabs((double)vals[j]));
           }
           int e = mx_exponent(amax, 6.0);
-          scales[((b * H + h) * rows + r) * (len / G) + g0 / G] = (uint8_t)(e + 127);
+          scales[scale_index(b * H + h, r, g0 / G, rows, len / G, axis)] = (uint8_t)(e + 127);
           for (int64_t j = 0; j < G; j += 2) {
             uint8_t lo = e2m1_encode((float)std::ldexp((double)vals[j], -e));
             uint8_t hi = e2m1_encode((float)std::ldexp((double)vals[j + 1], -e));
@@ -344,7 +351,7 @@ void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
 // in fp32 as a balanced pairwise tree in index order ((se0+se1)+(se2+se3))+...; the
 // first candidate with a strictly smaller sum wins (ties keep the earlier candidate).
 // axis 0: codes [B,H,N,D/2], scales [B,H,N,D/16];  axis 1: codes [B,H,D,Np/2], scales
-// [B,H,D,Np/16] with Np = N rounded up to 64.
+// [B,H,Np/16,D] with Np = N rounded up to 64.
 float nv_block_sse(const float* x, float s, uint8_t* codes_out) {
   float r = 1.0f / s;
   float se[16];
@@ -408,9 +415,9 @@ void orc_quant_nvfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
             float sse = nv_block_sse(vals, (float)e4m3_decode((uint8_t)cand[i]), cc);
             if (sse < best) { best = sse; best_c = (uint8_t)cand[i]; best_i = (int)i; std::memcpy(best_codes, cc, 16); }
           }
-          int64_t srow = ((b * H + h) * rows + r);
-          scales[srow * (len / G) + g0 / G] = best_c;
-          if (chosen) chosen[srow * (len / G) + g0 / G] = (uint8_t)best_i;
+          int64_t srow = ((b * H + h) * rows + r), si = scale_index(b * H + h, r, g0 / G, rows, len / G, axis);
+          scales[si] = best_c;
+          if (chosen) chosen[si] = (uint8_t)best_i;
           for (int j = 0; j < G; j += 2)
             codes[srow * (len / 2) + (g0 + j) / 2] = (uint8_t)(best_codes[j] | (best_codes[j + 1] << 4));
         }
@@ -420,24 +427,28 @@ void orc_quant_nvfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
 // The target MFMA has no NVFP4 operand form, so NVFP4 operands are dequantized to FP8
 // before the matrix product.  For each 32-element run along the block axis:
 // xhat_i = E2M1 value * UE4M3 scale (exact in fp32); A = max |xhat|; E = smallest integer
-// with 448 * 2^E >= A (A = 0 gives -127); f_i = E4M3(xhat_i * 2^-E).  Layouts follow
-// orc_quant_nvfp4 with bytes per element (codes [rows, len]) and scales [rows, len/32].
-void orc_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len,
-                        uint8_t* f8, uint8_t* e8m0) {
-  for (int64_t r = 0; r < rows; ++r)
-    for (int64_t g0 = 0; g0 < len; g0 += 32) {
-      double xh[32], A = 0.0;
-      for (int j = 0; j < 32; ++j) {
-        int64_t i = g0 + j;
-        uint8_t byte = codes[r * (len / 2) + i / 2];
-        uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
-        xh[j] = e2m1_decode(c) * e4m3_decode(scales[r * (len / 16) + i / 16]);
-        A = std::max(A, std::fabs(xh[j]));
+// with 448 * 2^E >= A (A = 0 gives -127); f_i = E4M3(xhat_i * 2^-E).  Input layouts are
+// orc_quant_nvfp4's for the same axis; outputs: codes one byte per element ([B,H,N,D] or
+// [B,H,D,Np]) and E8M0 scales laid out like MX-FP4's ([B,H,N,D/32] or [B,H,Np/32,D]).
+void orc_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t B, int64_t H, int64_t N, int64_t D,
+                        int axis, uint8_t* f8, uint8_t* e8m0) {
+  const int64_t Np = (N + 63) / 64 * 64;
+  const int64_t rows = axis == 0 ? N : D, len = axis == 0 ? D : Np;
+  for (int64_t bh = 0; bh < B * H; ++bh)
+    for (int64_t r = 0; r < rows; ++r)
+      for (int64_t g0 = 0; g0 < len; g0 += 32) {
+        double xh[32], A = 0.0;
+        for (int j = 0; j < 32; ++j) {
+          int64_t i = g0 + j;
+          uint8_t byte = codes[(bh * rows + r) * (len / 2) + i / 2];
+          uint8_t c = (i & 1) ? (byte >> 4) : (byte & 15);
+          xh[j] = e2m1_decode(c) * e4m3_decode(scales[scale_index(bh, r, i / 16, rows, len / 16, axis)]);
+          A = std::max(A, std::fabs(xh[j]));
+        }
+        int E = mx_exponent(A, 448.0);
+        e8m0[scale_index(bh, r, g0 / 32, rows, len / 32, axis)] = (uint8_t)(E + 127);
+        for (int j = 0; j < 32; ++j) f8[(bh * rows + r) * len + g0 + j] = e4m3_encode((float)std::ldexp(xh[j], -E));
       }
-      int E = mx_exponent(A, 448.0);
-      e8m0[r * (len / 32) + g0 / 32] = (uint8_t)(E + 127);
-      for (int j = 0; j < 32; ++j) f8[r * len + g0 + j] = e4m3_encode((float)std::ldexp(xh[j], -E));
-    }
 }
 
 // ----- Thrift block selection ("ThriftAttention", ¶1 and ¶3) -----
@@ -521,7 +532,7 @@ struct orc_attn_args {
   const uint16_t* q_hi; const uint16_t* k_hi; int32_t hi_dt;
   const uint8_t* thrift_mask;  // nullable [B,Hq,nQB,nKB]; 1 = this tile uses q_hi/k_hi
   // V: V_HI 16-bit [B,Hkv,N,D] (v_dt; rounded to bf16 before use); V_E4M3 codes [B,Hkv,D,Np] + fp32 [B,Hkv,D];
-  //    V_MXFP4 packed [B,Hkv,D,Np/2] + E8M0 [B,Hkv,D,Np/32]; V_MXFP8 E4M3 [B,Hkv,D,Np] + E8M0 [B,Hkv,D,Np/32]
+  //    V_MXFP4 packed [B,Hkv,D,Np/2] + E8M0 [B,Hkv,Np/32,D]; V_MXFP8 E4M3 [B,Hkv,D,Np] + E8M0 [B,Hkv,Np/32,D]
   const uint16_t* v_hi; int32_t v_dt;
   const uint8_t* v_lp; const float* v_s; const uint8_t* v_e8;
   // work subset: flat (b*Hq + h) in [bh_begin, bh_end), Q blocks [qb_begin, qb_end)
@@ -622,12 +633,12 @@ void orc_attention(const orc_attn_args* a) {
           case V_HI: v = bf16_decode(bf16_encode(in_value(a->v_hi, idx4(b, g, t, c, Hkv, N, D), a->v_dt))); break;
           case V_E4M3: v = e4m3_decode(a->v_lp[((b * Hkv + g) * D + c) * Np + t]); break;
           case V_MXFP4: {
-            int e = (int)a->v_e8[((b * Hkv + g) * D + c) * (Np / 32) + t / 32] - 127;
+            int e = (int)a->v_e8[((b * Hkv + g) * (Np / 32) + t / 32) * D + c] - 127;
             v = e2m1_decode(nib(a->v_lp + ((b * Hkv + g) * D + c) * (Np / 2), t)) * std::ldexp(1.0, e);
             break;
           }
           default: {
-            int e = (int)a->v_e8[((b * Hkv + g) * D + c) * (Np / 32) + t / 32] - 127;
+            int e = (int)a->v_e8[((b * Hkv + g) * (Np / 32) + t / 32) * D + c] - 127;
             v = e4m3_decode(a->v_lp[((b * Hkv + g) * D + c) * Np + t]) * std::ldexp(1.0, e);
           }
         }

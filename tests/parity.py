@@ -77,9 +77,9 @@ def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
         kc, ksc, _ = oracle.quant_nvfp4(ks, dt, 0, search_mode)
         vc, vsc, _ = oracle.quant_nvfp4(vb16, dt, 1, search_mode)
         res.update(q_nv=(qc, qsc), k_nv=(kc, ksc), v_nv=(vc, vsc))
-        q8, qe = oracle.nvfp4_to_mxfp8(qc, qsc)
-        k8, ke = oracle.nvfp4_to_mxfp8(kc, ksc)
-        v8, ve = oracle.nvfp4_to_mxfp8(vc, vsc)
+        q8, qe = oracle.nvfp4_to_mxfp8(qc, qsc, N, D, 0)
+        k8, ke = oracle.nvfp4_to_mxfp8(kc, ksc, N, D, 0)
+        v8, ve = oracle.nvfp4_to_mxfp8(vc, vsc, N, D, 1)
         res.update(q_codes=q8, q_scales=qe, k_codes=k8, k_scales=ke, v_codes=v8, v_scales=ve)
         ops = oracle.AttnOperands(qk_fmt=oracle.QK_MXFP8, p_fmt=oracle.P_NVFP4_MXFP8, v_fmt=oracle.V_MXFP8, q_lp=q8,
                                   q_e8=qe, k_lp=k8, k_e8=ke, v_lp=v8, v_e8=ve)

@@ -85,6 +85,21 @@ def test_validation_before_launch(L):
                                   None) == -4
     assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, shp, shp, 128, 64, 1.5, 1, 0x1000_0000,
                                   0x1000_0000, 1 << 30, None) == -1
+    # microscaled attention: D = 128 only, dword-aligned scales
+    m64 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 128, 64))
+    p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(m64), C.byref(m64), C.byref(m64), C.byref(p4), 0x1000_0000, sage.FP32, None) == -2
+    mis = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0002, shp)
+    m128 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, shp)
+    assert L.sage_attn_fwd(C.byref(mis), C.byref(m128), C.byref(m128), C.byref(p4), 0x1000_0000, sage.FP32, None) == -3
+    # mixed operand sets are not built
+    p8 = sage.AttnParamsC(0, 0.0, sage.NVFP4, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(m128), C.byref(m128), C.byref(m128), C.byref(p8), 0x1000_0000, sage.FP32, None) == -2
+    # NVFP4 -> MXFP8: axis flag 0/1, D a multiple of 32 along D
+    assert L.sage_nvfp4_to_mxfp8(0x1000_0000, 0x1000_0000, shp, 2, 0x1000_0000, 0x1000_0000, None) == -1
+    assert L.sage_nvfp4_to_mxfp8(0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 64, 48), 0, 0x1000_0000, 0x1000_0000,
+                                 None) == -1
+    assert L.sage_nvfp4_to_mxfp8(0x1000_0008, 0x1000_0000, shp, 0, 0x1000_0000, 0x1000_0000, None) == -3
     # smoothing workspace
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
 

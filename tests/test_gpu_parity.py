@@ -111,7 +111,7 @@ def test_nvfp4_scalesearch_bit_exact(axis, mode):
     assert np.array_equal(u8(qt.scales).reshape(s_o.shape), s_o)
     assert np.array_equal(u8(qt.codes).reshape(c_o.shape), c_o)
     m8 = sage.nvfp4_to_mxfp8(qt, along_tokens=axis == 1)
-    f8_o, e8_o = oracle.nvfp4_to_mxfp8(c_o, s_o)
+    f8_o, e8_o = oracle.nvfp4_to_mxfp8(c_o, s_o, 200, q.shape[-1], axis)
     assert np.array_equal(u8(m8.codes).reshape(f8_o.shape), f8_o)
     assert np.array_equal(u8(m8.scales).reshape(e8_o.shape), e8_o)
 
@@ -141,6 +141,12 @@ ATT_CASES = [
     ("thrift_long", dict(B=1, Hq=2, Hkv=1, N=640), False, "thrift"),
     ("video_fp8", dict(B=1, Hq=2, Hkv=2, N=700), False, "int8_fp8pv"),
     ("video_fp8", dict(B=1, Hq=2, Hkv=2, N=1024), True, "int8_fp8pv"),
+    ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=333), False, "mxfp4"),
+    ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=512), True, "mxfp4"),
+    ("fp4_search", dict(B=1, Hq=4, Hkv=2, N=700), True, "mxfp4"),          # GQA
+    ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=333), False, "nvfp4_search"),
+    ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=512), True, "nvfp4_search"),
+    ("fp4_search", dict(B=2, Hq=4, Hkv=2, N=640), False, "nvfp4_search"),  # GQA
 ]
 
 

@@ -137,6 +137,8 @@ def test_mxfp4_scale_rule_and_half_step(axis):
         x = np.concatenate([x, np.zeros(x.shape[:-1] + (pad,))], axis=-1)
     lo = oracle.e2m1_decode(codes & 15); hi = oracle.e2m1_decode(codes >> 4)
     dec = np.stack([lo, hi], axis=-1).reshape(x.shape)
+    if axis == 1:   # scales are token-block major [B,H,Np/32,D]
+        scales = np.swapaxes(scales, 2, 3)
     e = scales.astype(np.int64) - 127
     blocks = x.reshape(x.shape[:-1] + (-1, 32))
     amax = np.abs(blocks).max(axis=-1)
@@ -160,7 +162,9 @@ def _nv_blocks(x16, axis):
     return x.reshape(-1, 16)
 
 
-def _nv_dequant(codes, scales):
+def _nv_dequant(codes, scales, axis=0):
+    if axis == 1:   # scales are token-block major [B,H,Np/16,D]; bring them to the codes' order
+        scales = np.ascontiguousarray(np.swapaxes(scales, 2, 3))
     lo = oracle.e2m1_decode(codes & 15); hi = oracle.e2m1_decode(codes >> 4)
     dec = np.stack([lo, hi], axis=-1).reshape(-1, 16)
     return dec * oracle.e4m3_decode(scales.reshape(-1))[:, None]
@@ -217,8 +221,10 @@ def test_scalesearch_never_worse_and_matches_bruteforce(axis, mode):
     c_max, s_max, ch_max = oracle.quant_nvfp4(qb, oracle.BF16, axis, 0)
     c_s, s_s, ch_s = oracle.quant_nvfp4(qb, oracle.BF16, axis, mode)
     x = _nv_blocks(qb, axis)
-    sse_max = ((_nv_dequant(c_max, s_max) - x) ** 2).sum(axis=1)
-    sse_s = ((_nv_dequant(c_s, s_s) - x) ** 2).sum(axis=1)
+    sse_max = ((_nv_dequant(c_max, s_max, axis) - x) ** 2).sum(axis=1)
+    sse_s = ((_nv_dequant(c_s, s_s, axis) - x) ** 2).sum(axis=1)
+    if axis == 1:
+        ch_s = np.swapaxes(ch_s, 2, 3)
     assert np.all(ch_max == 0)
     assert np.all(sse_s <= sse_max * (1 + 1e-6) + 1e-30)     # fp32 tree vs fp64 sum
     assert np.sum(sse_s) < np.sum(sse_max)                  # the search does find better scales
@@ -235,16 +241,20 @@ def test_scalesearch_on_grid_block_keeps_baseline():
     assert np.array_equal(_nv_dequant(codes, scales).reshape(-1), x.reshape(-1))
 
 
-def test_nvfp4_to_mxfp8_half_step():
+@pytest.mark.parametrize("axis", [0, 1])
+def test_nvfp4_to_mxfp8_half_step(axis):
     w = I.workload("fp4_search", B=1, Hq=1, Hkv=1, N=96)
     q, _, _ = I.make_qkv(w, 2)
-    codes, scales, _ = oracle.quant_nvfp4(I.bits16(q), oracle.BF16, 0, 1)
-    f8, e8 = oracle.nvfp4_to_mxfp8(codes, scales)
-    xhat = _nv_dequant(codes, scales).reshape(-1, 32)
+    codes, scales, _ = oracle.quant_nvfp4(I.bits16(q), oracle.BF16, axis, 1)
+    f8, e8 = oracle.nvfp4_to_mxfp8(codes, scales, 96, 128, axis)
+    if axis == 1:   # E8M0 scales token-block major [B,H,Np/32,D] -> codes' order
+        e8 = np.ascontiguousarray(np.swapaxes(e8, 2, 3))
+    xhat = _nv_dequant(codes, scales, axis).reshape(-1, 32)
     E = e8.reshape(-1).astype(np.int64) - 127
     A = np.abs(xhat).max(axis=1)
     nz = A > 0
     assert np.all((224.0 * 2.0 ** E[nz] < A[nz]) & (A[nz] <= 448.0 * 2.0 ** E[nz]))
+    assert np.all(E[~nz] == -127)
     rec = oracle.e4m3_decode(f8).reshape(-1, 32) * (2.0 ** E)[:, None]
     tol = np.maximum(np.abs(xhat) * 2.0 ** -4, 2.0 ** -10 * 2.0 ** E[:, None])
     assert np.all(np.abs(rec - xhat) <= tol)
