@@ -16,9 +16,9 @@
 //       read permuted so that lane half h holds keys 32h .. 32h+31 of the tile in register
 //       order (key = 32h + 16b + r for accumulator b, register r).
 //   softmax: s = float(acc) * (s_q s_k sm_scale log2 e); row max over the lane and one
-//       v_permlane32_swap; fp32 online softmax in base 2.  The running max moves (and O, l
-//       are rescaled) only when a row's tile max exceeds it by more than `tau` (0 for FP8 P,
-//       which must stay <= 448).
+//       v_permlane32_swap; fp32 online softmax in base 2 with the exact running max (P is
+//       rounded to bf16 / FP8 relative to it, as the per-tile algorithm states; O and l are
+//       rescaled whenever some row of the wave raises its max).
 //   O^T (D x 32) += V^T . P^T on v_mfma_f32_32x32x16_bf16 with V^T fragments read from the
 //       row-major LDS tile by ds_read_b64_tr_b16 (each 16-lane group transposes a 4-key x
 //       16-channel block), or on the scaled FP8 MFMA (32x32x64) with V stored channel-major.
@@ -55,8 +55,8 @@ struct Params {
   const uint8_t* mask; const uint16_t* qhi; const uint16_t* khi;
   void* out;
   int64_t Hq, Hkv, N, Np, nQB, nKB, nPairs, total_wg;
-  float sm_log2;   // sm_scale * log2(e)
-  float tau;       // lazy-rescale threshold (log2 units)
+  float sm_log2;     // sm_scale * log2(e), rounded to fp32
+  float sm_log2_lo;  // sm_scale * log2(e) - sm_log2 (the FP8-P path carries the product exactly)
 };
 
 // LDS: two K tiles (int8 [64][D]) and two V tiles (bf16 [64][D] row-major, or FP8 V^T
@@ -236,9 +236,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 #pragma unroll
   for (int c = 0; c < NCC; ++c) o[c] = v16f{};
   float m_run = -__builtin_inff(), l_run = 0.0f;
+  float m_lo = 0.0f;            // FP8 P: the running max is the pair m_run + m_lo
   v16i acc[2];                  // S of the tile the next VALU phase works on
   bool hi = false;              // that tile runs on bf16 (Thrift)
   float dq = 0.0f;              // its dequantization factor (log2 units)
+  float dq_lo = 0.0f;           // FP8 P: dq + dq_lo = s_q s_k sm_scale log2(e) to ~2^-40
   uint32_t pk[PV8 ? 8 : 16];    // P of the tile the next MFMA phase works on (bf16 pairs / FP8 quads)
 
   DmaPlan<D, PV8> dma;
@@ -263,7 +265,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   };
   auto qk_mfma = [&](int t) {
     hi = THRIFT && mrow[uni(t)] != 0;
-    dq = __builtin_fmaxf(hi ? p.sm_log2 : qscale * k_scales[uni(bkv * p.nKB + t)] * p.sm_log2, 1.17549435e-38f);
+    if (PV8) {   // exact two-float product of the block scales and sm_scale * log2(e)
+      const float ksc = k_scales[uni(bkv * p.nKB + t)];
+      const float kh = qscale * ksc, kl = __builtin_fmaf(qscale, ksc, -kh);
+      dq = kh * p.sm_log2;
+      dq_lo = __builtin_fmaf(kh, p.sm_log2, -dq) + __builtin_fmaf(kh, p.sm_log2_lo, kl * p.sm_log2);
+    } else {
+      dq = __builtin_fmaxf(hi ? p.sm_log2 : qscale * k_scales[uni(bkv * p.nKB + t)] * p.sm_log2, 1.17549435e-38f);
+    }
     const int64_t key0 = (int64_t)t * KT;
     if (!hi) {
       acc[0] = v16i{}; acc[1] = v16i{};
@@ -291,19 +300,89 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   auto valu_phase = [&](int t) {
     if (!active(t)) return;
     const int64_t key0 = (int64_t)t * KT;
+    const bool edge = (key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0);   // causal diagonal or ragged
+    auto masked = [&](int bb, int r) {
+      const int64_t kg = key0 + 32 * lh + 16 * bb + r;
+      return kg >= p.N || (CAUSAL && kg > qrow);
+    };
+    if (PV8) {
+      // FP8 P codes round P * 448, so P is computed to about one fp32 ulp of its exact value:
+      // the exponent is (acc - acc_max) * dq + c with the integer tile max taken out first and
+      // c = tile max - running max + log2(1.75), both maxima carried as exact two-float sums;
+      // the remaining factor 2^8 of 448 is applied exactly by the conversion's scale.
+      constexpr int SENT = -(1 << 30);
+      if (edge) {
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (masked(bb, r)) acc[bb][r] = SENT;
+      }
+      int im = acc[0][0];
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) im = acc[bb][r] > im ? acc[bb][r] : im;
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap((uint32_t)im, (uint32_t)im, false, false);
+        const int i0 = (int)sw[0], i1 = (int)sw[1];
+        im = i0 > i1 ? i0 : i1;
+      }
+      const float fi = (float)im;   // exact: |acc| < 2^24
+      float th = -__builtin_inff(), tl = 0.0f;   // tile row max (log2 units) = th + tl
+      if (im > SENT) {
+        th = fi * dq;
+        tl = __builtin_fmaf(fi, dq, -th) + fi * dq_lo;
+      }
+      const float gt = (th - m_run) + (tl - m_lo);
+      if (__builtin_amdgcn_ballot_w64(gt > 0.0f) != 0) {   // wave-uniform: move the running max
+        const bool up = gt > 0.0f;
+        const float alpha = up ? __builtin_amdgcn_exp2f((m_run - th) + (m_lo - tl)) : 1.0f;   // 0 on the first tile
+        if (up) { m_run = th; m_lo = tl; }
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < NCC; ++c) o[c] *= alpha;
+      }
+      const float c0 = ((th - m_run) + (tl - m_lo)) + 0.807354922057604f;   // + log2(1.75)
+      float lsum = 0.0f;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {   // 1.75 P, kept in the accumulator registers
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)(acc[bb][r] - im), dq, c0));
+          lsum += e;
+          acc[bb][r] = __float_as_int(e);
+        }
+      if (edge) {   // a zero scale leaves masked keys at exp2(c0): clear them
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (masked(bb, r)) { lsum -= __int_as_float(acc[bb][r]); acc[bb][r] = 0; }
+      }
+      l_run += lsum;
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {   // E4M3(1.75 P * 2^8): the scale operand divides by 2^-8
+        const int bb = q4 >> 2, r = 4 * (q4 & 3);
+        const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, __int_as_float(acc[bb][r]),
+                                                                __int_as_float(acc[bb][r + 1]), 0x1p-8f, false);
+        const v2s w2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, __int_as_float(acc[bb][r + 2]),
+                                                                __int_as_float(acc[bb][r + 3]), 0x1p-8f, true);
+        pk[q4] = __builtin_bit_cast(uint32_t, w2);
+      }
+      return;
+    }
     float s[2][16];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[bb][r] = hi ? __int_as_float(acc[bb][r]) : (float)acc[bb][r];
-    if ((key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0)) {   // causal diagonal or ragged tile
+    if (edge) {
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t kg = key0 + 32 * lh + 16 * bb + r;
-          if (kg >= p.N || (CAUSAL && kg > qrow)) s[bb][r] = -__builtin_inff();
-        }
+        for (int r = 0; r < 16; ++r)
+          if (masked(bb, r)) s[bb][r] = -__builtin_inff();
     }
     float mx = s[0][0];
 #pragma unroll
@@ -312,7 +391,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
       for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, s[bb][r]);
     mx = halves_max(mx);
     const float mt = mx * dq;                      // tile row max in scaled units
-    if (__builtin_amdgcn_ballot_w64(mt > m_run + p.tau) != 0) {   // wave-uniform: move the running max
+    if (__builtin_amdgcn_ballot_w64(mt > m_run) != 0) {   // wave-uniform: move the running max
       const float m_new = __builtin_fmaxf(m_run, mt);
       const float alpha = m_run == -__builtin_inff() ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -320,29 +399,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 #pragma unroll
       for (int c = 0; c < NCC; ++c) o[c] *= alpha;
     }
-    const float moff = m_run - (PV8 ? 8.807354922057604f : 0.0f);   // FP8 P carries the factor 448
     float lsum = 0.0f;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        s[bb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], dq, -moff));
+        s[bb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], dq, -m_run));
         lsum += s[bb][r];
       }
     l_run += lsum;
-    if (!PV8) {
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) pk[8 * bb + (r >> 1)] = pack_bf16x2(s[bb][r], s[bb][r + 1]);
-    } else {
-#pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) {
-        const int bb = q4 >> 2, r = 4 * (q4 & 3);
-        const uint32_t wv = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][r], s[bb][r + 1], 0u, false);
-        pk[q4] = __builtin_amdgcn_cvt_pk_fp8_f32(s[bb][r + 2], s[bb][r + 3], wv, true);
-      }
-    }
+      for (int r = 0; r < 16; r += 2) pk[8 * bb + (r >> 1)] = pack_bf16x2(s[bb][r], s[bb][r + 1]);
   };
 
   // ---- MFMA phase: O += P(t) V(t), then S of tile t+1 (group A also issues the tile loads).
@@ -420,7 +489,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 
   // ---- epilogue: O / l (and the FP8 V channel scales); lane (li, lh) holds row qrow,
   //      channels 32cc + 8(r/4) + 4lh + (r%4).
-  const float l_tot = halves_sum(l_run);
+  // (FP8 P: l sums 1.75 P and O sums E4M3(448 P) V, so O / l carries an extra 256)
+  const float l_tot = halves_sum(l_run) * (PV8 ? 256.0f : 1.0f);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_ok) {
 #pragma unroll
@@ -485,8 +555,11 @@ hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st) {
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;
   p.nPairs = (p.nQB + 1) / 2;
   p.total_wg = a.B * a.Hq * p.nPairs;
-  p.sm_log2 = a.sm_scale * LOG2E;
-  p.tau = pv_fp8 ? 0.0f : 8.0f;
+  {
+    const double l2 = (double)a.sm_scale * 1.4426950408889634074;
+    p.sm_log2 = (float)l2;
+    p.sm_log2_lo = (float)(l2 - (double)p.sm_log2);
+  }
   const bool thrift = a.mask != nullptr;
   const bool causal = a.causal != 0;
   if (a.D == 64) {

@@ -297,15 +297,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
       // one E8M0 block = this lane's 32 keys; its largest P is exp2 of the lane max
       const float amax = __builtin_amdgcn_exp2f(__builtin_fmaf(mlane, dq, -moff));
       const int e = mx_exp_e2m1(amax);
-      const float f = __uint_as_float((uint32_t)(127 - e) << 23);   // 2^-e, e in [-127, -2]
+      // the conversion divides by 2^(exponent of its scale operand): codes E2M1(P * 2^-e)
+      // (an all-zero block, e = -127, converts with 2^-126: its codes are 0 either way)
+      const float f = __uint_as_float((uint32_t)(127 + (e < -126 ? -126 : e)) << 23);
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {   // nibble 8wd + j = key 32lh + 16(wd/2) + 8(wd%2) + j
         const int bb = wd >> 1, r0 = 8 * (wd & 1);
         uint32_t x = 0;
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0] * f, s[bb][r0 + 1] * f, 1.0f, 0);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0 + 2] * f, s[bb][r0 + 3] * f, 1.0f, 1);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0 + 4] * f, s[bb][r0 + 5] * f, 1.0f, 2);
-        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0 + 6] * f, s[bb][r0 + 7] * f, 1.0f, 3);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0], s[bb][r0 + 1], f, 0);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0 + 2], s[bb][r0 + 3], f, 1);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0 + 4], s[bb][r0 + 5], f, 2);
+        x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[bb][r0 + 6], s[bb][r0 + 7], f, 3);
         pk[wd] = x;
       }
       psc = (uint32_t)(e + 127);

@@ -1,0 +1,72 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The HIP path runs the whole pass on the full tensors.  The oracle quantizes the same full
+tensors (codes, scales and Thrift masks are compared bit for bit everywhere) and attends
+for sampled (head, Q block) pairs only: the first head's first and middle Q blocks and the
+last head's last Q block, whose outputs together are held to the attention tolerance."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from bit_quantized_attention_03_amd import inputs as I
+from tests.parity import check_out, oracle_pass, u8
+
+pytestmark = pytest.mark.gpu
+
+FULL = [
+    ("llm_int8", False, "int8"),
+    ("llm_int8", True, "int8"),
+    ("video_fp8", False, "int8_fp8pv"),
+    ("fp4_search", False, "mxfp4"),
+    ("fp4_search", False, "nvfp4_search"),
+    ("thrift_long", True, "thrift"),
+]
+
+
+@pytest.mark.parametrize("name,causal,variant", FULL)
+def test_full_size_sampled_parity(name, causal, variant):
+    from bit_quantized_attention_03_amd import sage
+    w = I.workload(name)
+    print(f"[case] full size {name} causal={causal} variant={variant}", flush=True)
+    q, k, v = I.make_qkv(w, seed=0)
+    B, Hq, N, D = q.shape
+    res = sage.forward(q.cuda(), k.cuda(), v.cuda(), causal=causal, variant=variant)
+    torch.cuda.synchronize()
+    out = res.out.cpu().numpy()
+
+    nQB = (N + 127) // 128
+    samples = [(0, 0), (0, nQB // 2), (B * Hq - 1, nQB - 1)]
+    bh0, qb0 = samples[0]
+    orc = oracle_pass(q, k, v, causal, variant, bh=(bh0, bh0 + 1), qb=(qb0, qb0 + 1))
+
+    # every quantized operand, bit for bit, over the full tensors
+    assert np.array_equal(res.mean.cpu().numpy().reshape(orc["mean"].shape), orc["mean"])
+    assert np.array_equal(I.bits16(res.k_smoothed.cpu()).reshape(orc["ks"].shape), orc["ks"])
+    for side, qt in (("q", res.q), ("k", res.k), ("v", res.v)):
+        key = f"{side}_codes"
+        if key not in orc:
+            continue
+        codes = u8(qt.codes).reshape(-1)[: orc[key].nbytes]
+        assert np.array_equal(codes, orc[key].reshape(-1).view(np.uint8)), f"{side} codes"
+        sc = np.ascontiguousarray(orc[f"{side}_scales"]).reshape(-1)
+        gs = u8(qt.scales.contiguous()).reshape(-1)[: sc.nbytes]          # raw bytes of the scale buffer
+        assert np.array_equal(gs, sc.view(np.uint8)), f"{side} scales"
+    if variant == "thrift":
+        assert np.array_equal(res.mask.cpu().numpy(), orc["mask"])
+
+    # the bar applies to the output as a whole: max|O_gpu - O_oracle| <= 2e-3 max|O_oracle| over
+    # all sampled rows together (the per-block figures are printed for inspection)
+    gs, os_ = [], []
+    for i, (bh, qb) in enumerate(samples):
+        ref = orc["out"] if i == 0 else oracle.attention(orc["ops"], B, Hq, w.Hkv, N, D, causal, 1.0 / math.sqrt(D),
+                                                         bh=(bh, bh + 1), qb=(qb, qb + 1))
+        b, h = divmod(bh, Hq)
+        rows = slice(128 * qb, min(N, 128 * qb + 128))
+        g, o = out[b, h, rows], ref[b, h, rows]
+        print(f"  head {bh} Q block {qb}: max err {np.max(np.abs(g - o)):.3e}, max|O| {np.max(np.abs(o)):.3e}")
+        gs.append(g); os_.append(o)
+    rel, cos = check_out(np.concatenate(gs), np.concatenate(os_), f"{name} {variant} sampled rows")
+    print(f"  sampled rows: rel_err_vs_oracle = {rel:.2e}, cosine {cos:.7f}")
