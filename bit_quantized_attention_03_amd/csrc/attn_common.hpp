@@ -15,7 +15,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // Workgroup barrier without a memory fence.  Ordering is explicit in the kernels: tile loads
 // are complete (wait_vmem) before the barrier that publishes them, and an LDS buffer is
 // overwritten only after the barrier following the matrix instructions that consumed it.
-__device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_s_barrier(); }
+__device__ __forceinline__ void phase_barrier() {
+  __asm__ volatile("" ::: "memory");   // LDS may change across a phase boundary (direct loads land
+  __builtin_amdgcn_s_barrier();       // unseen by the compiler): no LDS access moves across it
+  __asm__ volatile("" ::: "memory");
+}
 
 // v_permlane32_swap on (x, x) returns, in an order that depends on the lane half, this
 // lane's value and the value of lane l ^ 32; max and sum of the pair agree in both halves.

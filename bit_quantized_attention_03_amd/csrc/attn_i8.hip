@@ -31,16 +31,20 @@
 // (Both groups run the same straight-line program, offset by one barrier, so the phase code
 // exists once and register pressure is that of one wave's program.)
 // Group A also moves the tiles: at the start of its VALU phase 2t+3 it issues direct
-// global->LDS loads (global_load_lds_dwordx4) of K(t+2) and V(t+1) and waits for them at the
-// end of that phase (a VALU phase reads no LDS, so nothing in it waits on those writes).  K(s)
-// is read in phases 2s, 2s+1 and V(t) in 2t+2, 2t+3, so two buffers of each are enough.
-// Tiles never pass through registers.
+// global->LDS loads (global_load_lds_dwordx4) of K(t+3) and V(t+2), and at the end of its
+// next VALU phase (2t+5) waits for them, leaving that phase's own loads in flight; they are
+// first read in phase 2t+6.  K(s) is read in phases 2s, 2s+1 and V(t) in 2t+2, 2t+3, so the
+// loads land in the buffers of K(t) and V(t-1): three of each, used round-robin (the loop is
+// unrolled by three so every buffer is a compile-time choice).  Tiles never pass through
+// registers.
 //
 // The causal mask is top-left aligned; tiles entirely above a wave's rows are skipped and
 // workgroups are scheduled heaviest first.  Workgroup ids are remapped so consecutive Q-block
 // pairs of one head run on the same XCD and share its L2.
 #include "device.hpp"
 #include "kernels.hpp"
+
+#include <type_traits>
 
 namespace sage {
 namespace {
@@ -59,14 +63,14 @@ struct Params {
   float sm_log2_lo;  // sm_scale * log2(e) - sm_log2 (the FP8-P path carries the product exactly)
 };
 
-// LDS: two K tiles (int8 [64][D]) and two V tiles (bf16 [64][D] row-major, or FP8 V^T
-// [D][64]), all unpadded with XOR-swizzled 16-byte chunks.
+// LDS: three K tiles (int8 [64][D]) and three V tiles (bf16 [64][D] row-major, or FP8 V^T
+// [D][64]), all unpadded with XOR-swizzled 16-byte chunks.  Each tile buffer is a separate
+// static array, so the compiler can tell the reads of one buffer from the direct loads still
+// in flight into another.
 template <int D, bool PV8>
 struct Smem {
   static constexpr int K_BYTES = KT * D;
   static constexpr int V_BYTES = PV8 ? D * KT : KT * 2 * D;
-  static constexpr int V_BASE = 2 * K_BYTES;
-  static constexpr int TOTAL = 2 * K_BYTES + 2 * V_BYTES;
 };
 
 // K: chunk c of row r at chunk position c ^ (r & (D/16 - 1)) of its row: the 32 rows one MFMA
@@ -85,11 +89,18 @@ __device__ __forceinline__ int v_off(int row, int byte) {   // byte offset withi
 __device__ __forceinline__ int v8_off(int row, int c) { return row * KT + 16 * (c ^ ((row >> 2) & 3)); }
 
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// vmcnt(n), n < 16: wait until at most n vector memory operations of this wave are in flight
+template <int n>
+__device__ __forceinline__ void wait_vmem_n() { __builtin_amdgcn_s_waitcnt(0x0F70 | n); }
 // Workgroup barrier without a memory fence.  The loop's ordering needs are explicit: tile loads
 // are complete (wait_vmem) before the barrier that publishes them, and an LDS buffer is
 // overwritten only after the barrier following the matrix instructions that consumed its reads.
 // (__syncthreads would also drain the tile loads still in flight at every phase boundary.)
-__device__ __forceinline__ void phase_barrier() { __builtin_amdgcn_s_barrier(); }
+__device__ __forceinline__ void phase_barrier() {
+  __asm__ volatile("" ::: "memory");   // LDS may change across a phase boundary (direct loads land
+  __builtin_amdgcn_s_barrier();       // unseen by the compiler): no LDS access moves across it
+  __asm__ volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ int tile_key(int b, int m) {   // accumulator row m of half b -> key in tile
   return ((m >> 2) & 1) * 32 + 16 * b + (m >> 3) * 4 + (m & 3);
@@ -173,7 +184,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
                                                               const uint8_t* __restrict__ blk_mask) {
   using S = Smem<D, PV8>;
   constexpr int NCC = D / 32;    // 32-channel output chunks
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[S::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[S::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kb2[S::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vb0[S::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vb1[S::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t vb2[S::V_BYTES];
 
   // ---- workgroup -> (b, h, pair of Q blocks); XCD-aware: consecutive work items on one XCD
   int64_t wg = blockIdx.x;
@@ -195,7 +211,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   const bool blk_ok = qb < p.nQB;
 
   // tiles of this group, and of the workgroup (the longer of the two groups)
-  auto tiles_of = [&](int64_t q) -> int {
+  auto tiles_of = [&](int64_t q) __attribute__((always_inline)) -> int {
     if (q >= p.nQB) return 0;
     if (!CAUSAL) return (int)p.nKB;
     const int64_t last = (q * QB + QB - 1) / KT + 1;
@@ -204,9 +220,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   const int nTg = tiles_of(qb);
   const int nT = tiles_of(2 * pr + 1) > tiles_of(2 * pr) ? tiles_of(2 * pr + 1) : tiles_of(2 * pr);
   const uint8_t* mrow = THRIFT && blk_ok ? blk_mask + (bh * p.nQB + qb) * p.nKB : nullptr;
-  auto active = [&](int t) { return t >= 0 && t < nTg && (!CAUSAL || (int64_t)t * KT <= qrow0 + 31); };
-  auto kbuf = [&](int t) { return smem + (t & 1) * S::K_BYTES; };
-  auto vbuf = [&](int t) { return smem + S::V_BASE + (t & 1) * S::V_BYTES; };
+  auto active = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < nTg && (!CAUSAL || (int64_t)t * KT <= qrow0 + 31); };
+  // buffer J % 3 of K and of V (J a compile-time constant)
+  auto kbuf = [](auto jc) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int J = decltype(jc)::value % 3;
+    if constexpr (J == 0) return kb0; else if constexpr (J == 1) return kb1; else return kb2;
+  };
+  auto vbuf = [](auto jc) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int J = decltype(jc)::value % 3;
+    if constexpr (J == 0) return vb0; else if constexpr (J == 1) return vb1; else return vb2;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
 
   // ---- per-lane LDS read offsets (loop invariant; tile and chunk terms become immediates)
   int kro[D / 32], vro[D / 32];
@@ -246,7 +272,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   DmaPlan<D, PV8> dma;
   if (grp == 0) {
     dma.init(a, lane, p.Np);
-    dma.k_tile(p, bkv, 0, kbuf(0), a);
+    dma.k_tile(p, bkv, 0, kbuf(I0{}), a);
+    if (nT > 1) dma.k_tile(p, bkv, 1, kbuf(I1{}), a);
+    if (nT > 0) dma.v_tile(p, bkv, 0, vbuf(I0{}), a);
   }
   wait_vmem();
   __syncthreads();
@@ -254,16 +282,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   // ---- S of tile t for this wave.  The int8 K fragments are read from LDS by qk_load and
   //      consumed by qk_mfma, so the reads can be issued ahead of other matrix work.
   v4i kf[D / 32][2];
-  auto uni = [](int64_t x) { return (int64_t)__builtin_amdgcn_readfirstlane((int)x); };   // scalar loads below
-  auto qk_load = [&](int t) {
+  auto uni = [](int64_t x) __attribute__((always_inline)) { return (int64_t)__builtin_amdgcn_readfirstlane((int)x); };   // scalar loads below
+  auto qk_load = [&](int t, const uint8_t* kb) __attribute__((always_inline)) {
     if (THRIFT && mrow[uni(t)] != 0) return;
-    const uint8_t* kb = kbuf(t);
 #pragma unroll
     for (int kc = 0; kc < D / 32; ++kc)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) kf[kc][bb] = *(const v4i*)(kb + kro[kc] + 16 * D * bb);
   };
-  auto qk_mfma = [&](int t) {
+  auto qk_mfma = [&](int t) __attribute__((always_inline)) {
     hi = THRIFT && mrow[uni(t)] != 0;
     if (PV8) {   // exact two-float product of the block scales and sm_scale * log2(e)
       const float ksc = k_scales[uni(bkv * p.nKB + t)];
@@ -297,11 +324,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   };
 
   // ---- VALU phase: softmax of tile t -> P in pk
-  auto valu_phase = [&](int t) {
+  auto valu_phase = [&](int t) __attribute__((always_inline)) {
     if (!active(t)) return;
     const int64_t key0 = (int64_t)t * KT;
     const bool edge = (key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0);   // causal diagonal or ragged
-    auto masked = [&](int bb, int r) {
+    auto masked = [&](int bb, int r) __attribute__((always_inline)) {
       const int64_t kg = key0 + 32 * lh + 16 * bb + r;
       return kg >= p.N || (CAUSAL && kg > qrow);
     };
@@ -416,7 +443,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 
   // ---- MFMA phase: O += P(t) V(t), then S of tile t+1 (group A also issues the tile loads).
   //      LDS fragment reads run one k-group ahead of the matrix instructions that use them.
-  auto v_frag = [&](const uint8_t* vs, int kg, int cc) -> v8bf {
+  auto v_frag = [&](const uint8_t* vs, int kg, int cc) __attribute__((always_inline)) -> v8bf {
     const uint8_t* a0 = vs + vro[cc] + 8 * kg * 2 * D;
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0));
     const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0 + 4 * 2 * D));
@@ -429,11 +456,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
     }
     return __builtin_bit_cast(v8bf, raw);
   };
-  auto mfma_phase = [&](int t) {
+  auto mfma_phase = [&](int t, const uint8_t* vs, const uint8_t* kbn) __attribute__((always_inline)) {
     const bool next = active(t + 1);
-    if (next) qk_load(t + 1);
+    if (next) qk_load(t + 1, kbn);
     if (active(t)) {
-      const uint8_t* vs = vbuf(t);
       if (!PV8) {
         v8bf vf[2][NCC];
 #pragma unroll
@@ -473,17 +499,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   //      phase of tile t+1, barrier); group B starts it one barrier late and group A ends with
   //      one extra barrier, so B runs exactly one phase behind A and both pass the same number
   //      of barriers.  Group A waits for its tile loads at the end of its VALU phases.
-  if (grp == 1) phase_barrier();
-  for (int t = -1; t < nT; ++t) {
-    mfma_phase(t);
+  constexpr int KR = DmaPlan<D, PV8>::K_ROUNDS, VR = DmaPlan<D, PV8>::V_ROUNDS;
+  static_assert(KR + VR < 16, "vmcnt immediate");
+  // one step: MFMA phase of tile t, barrier, VALU phase of tile t+1, barrier; jc = t mod 3
+  auto step = [&](int t, auto jc) __attribute__((always_inline)) {
+    constexpr int J = decltype(jc)::value;
+    mfma_phase(t, vbuf(std::integral_constant<int, J>{}), kbuf(std::integral_constant<int, J + 1>{}));
     phase_barrier();
-    if (grp == 0) {   // tile loads overlap this wave's softmax (no LDS reads in the VALU phase)
-      if (t + 2 < nT) dma.k_tile(p, bkv, t + 2, kbuf(t + 2), a);
-      if (t + 1 < nT) dma.v_tile(p, bkv, t + 1, vbuf(t + 1), a);
-    }
+    const bool ld_k = grp == 0 && t + 3 < nT, ld_v = grp == 0 && t + 2 < nT;   // ld_k implies ld_v
+    if (ld_k) dma.k_tile(p, bkv, t + 3, kbuf(std::integral_constant<int, J>{}), a);
+    if (ld_v) dma.v_tile(p, bkv, t + 2, vbuf(std::integral_constant<int, J + 2>{}), a);
     valu_phase(t + 1);
-    if (grp == 0) wait_vmem();
+    if (grp == 0) {   // the previous step's loads are complete; this step's may still fly
+      if (ld_k) wait_vmem_n<KR + VR>();
+      else if (ld_v) wait_vmem_n<VR>();
+      else wait_vmem();
+    }
     phase_barrier();
+  };
+  if (grp == 1) phase_barrier();
+  step(-1, I2{});
+  for (int t = 0; t < nT; t += 3) {
+    step(t, I0{});
+    if (t + 1 < nT) step(t + 1, I1{});
+    if (t + 2 < nT) step(t + 2, I2{});
   }
   if (grp == 0) phase_barrier();
 
@@ -515,15 +554,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 
 template <int D, bool CAUSAL, bool PV8, bool THRIFT, bool VF16, bool OUT_BF16>
 hipError_t launch_cfg(const Params& p, hipStream_t st) {
-  using S = Smem<D, PV8>;
   auto kern = attn_i8_kernel<D, CAUSAL, PV8, THRIFT, VF16, OUT_BF16>;
-  static bool attr_set = false;   // the attribute is per function; setting it twice is harmless
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, S::TOTAL);
-    attr_set = true;
-  }
   if (p.total_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(NTHREADS), S::TOTAL, st, p, p.ks, p.qs, p.mask);
+  hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(NTHREADS), 0, st, p, p.ks, p.qs, p.mask);
   return hipGetLastError();
 }
 

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   const int64_t qrow = qrow0 + li;
   const bool row_ok = qrow < p.N;
 
-  auto tiles_of = [&](int64_t q) -> int {
+  auto tiles_of = [&](int64_t q) __attribute__((always_inline)) -> int {
     if (q >= p.nQB) return 0;
     if (!CAUSAL) return (int)p.nKB;
     const int64_t last = (q * QB + QB - 1) / KT + 1;
@@ -156,9 +156,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   };
   const int nTg = tiles_of(qb);
   const int nT = tiles_of(2 * pr + 1) > tiles_of(2 * pr) ? tiles_of(2 * pr + 1) : tiles_of(2 * pr);
-  auto active = [&](int t) { return t >= 0 && t < nTg && (!CAUSAL || (int64_t)t * KT <= qrow0 + 31); };
-  auto kst = [&](int t) { return smem + (t & 1) * L::K_STAGE; };
-  auto vst = [&](int t) { return smem + L::V_BASE + (t & 1) * L::V_STAGE; };
+  auto active = [&](int t) __attribute__((always_inline)) { return t >= 0 && t < nTg && (!CAUSAL || (int64_t)t * KT <= qrow0 + 31); };
+  auto kst = [&](int t) __attribute__((always_inline)) { return smem + (t & 1) * L::K_STAGE; };
+  auto vst = [&](int t) __attribute__((always_inline)) { return smem + L::V_BASE + (t & 1) * L::V_STAGE; };
 
   // ---- per-lane LDS offsets (loop invariant)
   int kro[2][FP4 ? NKK : 2 * NKK];   // K fragment chunks of block b
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   // ---- S of tile t: K fragments and scales from LDS (qk_load), then the matrix products
   v8i kf[2][NKK];
   uint32_t ksc[2];
-  auto qk_load = [&](int t) {
+  auto qk_load = [&](int t) __attribute__((always_inline)) {
     const uint8_t* ks = kst(t);
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
       ksc[bb] = *(const uint32_t*)(ks + ksro[bb]) >> (8 * lh);
     }
   };
-  auto qk_mfma = [&](int t) {
+  auto qk_mfma = [&](int t) __attribute__((always_inline)) {
     (void)t;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   };
 
   // ---- VALU phase: softmax of tile t, P quantized into pk / psc
-  auto valu_phase = [&](int t) {
+  auto valu_phase = [&](int t) __attribute__((always_inline)) {
     if (!active(t)) return;
     const int64_t key0 = (int64_t)t * KT;
     float s[2][16];
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   };
 
   // ---- MFMA phase: O += P(t) V(t), then S of tile t+1
-  auto mfma_phase = [&](int t) {
+  auto mfma_phase = [&](int t) __attribute__((always_inline)) {
     const bool next = active(t + 1);
     if (next) qk_load(t + 1);
     if (active(t)) {
