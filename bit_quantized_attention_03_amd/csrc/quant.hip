@@ -1,7 +1,7 @@
 // Block quantizers.
 //  * INT8 per block (SageAttention, Technical approach: Q and K in 8 bits): s = amax / 127,
-//    code = clamp(round_half_even(x * (1/s)), -127, 127).  Two passes over the block (the
-//    second read hits L2), 3 bytes of HBM per 16-bit element.
+//    code = clamp(round_half_even(x * (1/s)), -127, 127).  The block is held in registers
+//    between the reduction and the encoding: 3 bytes of HBM per 16-bit element.
 //  * E4M3 per channel for V: amax over all tokens (atomic max on the bit pattern of a
 //    non-negative float), then codes written channel-major through an LDS transpose.
 //  * MX-FP4 (SageAttention3's microscaled FP4): E8M0 per 32 elements, e = smallest integer
@@ -16,11 +16,15 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+#include <type_traits>
+
 namespace sage {
 namespace {
 
 // ------------------------------------------------------------------ INT8 per block
-template <bool F16>
+// One workgroup per block of T tokens x D channels; the block (T * D / 8 16-byte chunks)
+// stays in registers between the amax reduction and the encoding, so HBM is read once.
+template <bool F16, int CPT>   // CPT = 16-byte chunks per thread (T * D / 8 / 256)
 __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int T,
                                                          int8_t* __restrict__ codes, float* __restrict__ scales) {
   const int64_t nblk = (N + T - 1) / T;
@@ -29,9 +33,60 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   const int rows = (int)((N - t0) < T ? (N - t0) : T);
   const int nchunk = rows * D / 8;
   const uint16_t* base = x + (bh * N + t0) * D;
+  v4i raw[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    raw[i] = c < nchunk ? *(const v4i*)(base + (int64_t)c * 8) : v4i{0, 0, 0, 0};
+  }
   float amax = 0.0f;
-  for (int c = threadIdx.x; c < nchunk; c += 256) {
-    v4i raw = *(const v4i*)(base + (int64_t)c * 8);
+#pragma unroll
+  for (int i = 0; i < CPT; ++i)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t u = (uint32_t)raw[i][w];
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u & 0xffffu))));
+      amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u >> 16))));
+    }
+  __shared__ float red[4];
+  amax = wave_max(amax);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
+  const float s = amax / 127.0f;
+  const float r = s > 0.0f ? 1.0f / s : 0.0f;
+  if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
+  int8_t* out = codes + (bh * N + t0) * D;
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c >= nchunk) continue;
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      uint16_t h = (uint16_t)((uint32_t)raw[i][e >> 1] >> (16 * (e & 1)));
+      float q = __builtin_rintf(in16_to_f32<F16>(h) * r);
+      q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+      packed[e >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (e & 3));
+    }
+    *(v2i*)(out + (int64_t)c * 8) = v2i{(int)packed[0], (int)packed[1]};
+  }
+}
+
+// Blocks too large for registers (over 4096 chunks): amax pass, then an encoding pass whose
+// reads hit L2.
+template <bool F16>
+__global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __restrict__ x, int64_t N, int D, int T,
+                                                          int8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int64_t nblk = (N + T - 1) / T;
+  const int64_t blk = blockIdx.x, bh = blockIdx.y;
+  const int64_t t0 = blk * T;
+  const int rows = (int)((N - t0) < T ? (N - t0) : T);
+  const int64_t nchunk = (int64_t)rows * D / 8;
+  const uint16_t* base = x + (bh * N + t0) * D;
+  float amax = 0.0f;
+  for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
+    v4i raw = *(const v4i*)(base + c * 8);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t u = (uint32_t)raw[w];
@@ -48,8 +103,8 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   const float r = s > 0.0f ? 1.0f / s : 0.0f;
   if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
   int8_t* out = codes + (bh * N + t0) * D;
-  for (int c = threadIdx.x; c < nchunk; c += 256) {
-    v4i raw = *(const v4i*)(base + (int64_t)c * 8);
+  for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
+    v4i raw = *(const v4i*)(base + c * 8);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -58,7 +113,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
       q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
       packed[e >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (e & 3));
     }
-    *(v2i*)(out + (int64_t)c * 8) = v2i{(int)packed[0], (int)packed[1]};
+    *(v2i*)(out + c * 8) = v2i{(int)packed[0], (int)packed[1]};
   }
 }
 
@@ -135,18 +190,40 @@ __global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* 
 }
 
 // ------------------------------------------------------------------ FP4 (MX and NV)
+// fp32(1 / E4M3(c)) for every positive finite code, from the compiler's correctly rounded
+// constant division (the same value a run-time IEEE division gives).
+struct RecipTable {
+  float v[128];
+};
+constexpr float e4m3_value(int c) {   // exact: (8 + m) * 2^(e - 10), or m * 2^-9 when e = 0
+  const int e = (c >> 3) & 15, m = c & 7;
+  float x = e == 0 ? (float)m : (float)(8 + m);
+  int sh = e == 0 ? -9 : e - 10;
+  for (; sh > 0; --sh) x *= 2.0f;
+  for (; sh < 0; ++sh) x *= 0.5f;
+  return x;
+}
+constexpr RecipTable make_recip() {
+  RecipTable t{};
+  for (int c = 1; c < 128; ++c) t.v[c] = 1.0f / e4m3_value(c);
+  return t;
+}
+__constant__ RecipTable kRecipE4M3 = make_recip();
+
 // Squared error of an NVFP4 candidate scale code over 16 values; codes written to c[0..1].
+// x_i = E2M1(v_i * fp32(1/s)), xhat_i = x_i * s (exact), e_i = v_i - xhat_i, summed as the
+// balanced index-order tree of e_i * e_i.
 __device__ __forceinline__ float nv_candidate(const float* v, uint32_t scode, uint32_t* c) {
   const float s = e4m3_to_f32(scode);
-  const float r = 1.0f / s;
+  const float r = kRecipE4M3.v[scode & 127u];
   float se[16];
   c[0] = c[1] = 0u;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
-    uint32_t two = f32x2_to_e2m1(v[i] * r, v[i + 1] * r);
+    const uint32_t two = f32x2_to_e2m1(v[i] * r, v[i + 1] * r);
     c[i >> 3] |= two << (4 * (i & 7));
-    float x0 = e2m1_to_f32(two & 15u) * s, x1 = e2m1_to_f32(two >> 4) * s;
-    float e0 = v[i] - x0, e1 = v[i + 1] - x1;
+    const auto xd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(two, 1.0f, 0);   // both E2M1 values of the byte
+    const float e0 = v[i] - xd[0] * s, e1 = v[i + 1] - xd[1] * s;
     se[i] = e0 * e0;
     se[i + 1] = e1 * e1;
   }
@@ -158,6 +235,9 @@ __device__ __forceinline__ float nv_candidate(const float* v, uint32_t scode, ui
 }
 
 // NVFP4 scale choice for one 16-value group (mode 0 max-scaling, 1 grid search, 2 offsets).
+// The grid codes E4M3(amax/6 * g_k) never decrease with k, so only the distinct ones that
+// differ from the baseline are evaluated, baseline first and then in ascending order: a
+// repeated code repeats the same error and could never be strictly smaller.
 __device__ __forceinline__ uint32_t nv_quant16(const float* v, int mode, uint32_t* codes) {
   float amax = 0.0f;
 #pragma unroll
@@ -168,13 +248,21 @@ __device__ __forceinline__ uint32_t nv_quant16(const float* v, int mode, uint32_
   uint32_t best_c = c0;
   float best = nv_candidate(v, c0, codes);
   if (mode == 1) {
+    uint32_t lo = 0, mask = 0;   // grid codes as a bit mask over [lo, lo + 31]
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const float g = (float)(0.85 + k * 0.3 / 7.0);
       uint32_t ck = f32_to_e4m3(smax * g);
       if (ck == 0) ck = 1;
+      if (k == 0) lo = ck;
+      if (ck != c0 && ck - lo < 32) mask |= 1u << (ck - lo);
+    }
+    // (the grid spans a factor 1.35, at most ~5 E4M3 codes, so the 32-bit window suffices)
+    for (uint32_t j = 0; j < 32 && (mask >> j) != 0; ++j) {
+      if (((mask >> j) & 1u) == 0) continue;
+      const uint32_t ck = lo + j;
       uint32_t cc[2];
-      float sse = nv_candidate(v, ck, cc);
+      const float sse = nv_candidate(v, ck, cc);
       if (sse < best) { best = sse; best_c = ck; codes[0] = cc[0]; codes[1] = cc[1]; }
     }
   } else if (mode == 2) {
@@ -297,11 +385,18 @@ __global__ __launch_bounds__(256) void nv_to_mx8_kernel(const uint8_t* __restric
   const float s0 = e4m3_to_f32(scales[nv0]), s1 = e4m3_to_f32(scales[nv1]);
   float xh[32];
   float A = 0.0f;
+  auto dec2 = [&](int i, decltype(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(0u, 1.0f, 0)) xd) {
+    xh[i] = xd[0] * (i < 16 ? s0 : s1);
+    xh[i + 1] = xd[1] * (i < 16 ? s0 : s1);
+    A = __builtin_fmaxf(A, __builtin_fmaxf(__builtin_fabsf(xh[i]), __builtin_fabsf(xh[i + 1])));
+  };
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    uint32_t c = ((uint32_t)raw[i >> 3] >> (4 * (i & 7))) & 15u;
-    xh[i] = e2m1_to_f32(c) * (i < 16 ? s0 : s1);
-    A = __builtin_fmaxf(A, __builtin_fabsf(xh[i]));
+  for (int w = 0; w < 4; ++w) {   // one conversion decodes the two E2M1 codes of a byte
+    const uint32_t u = (uint32_t)raw[w];
+    dec2(8 * w, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 0));
+    dec2(8 * w + 2, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 1));
+    dec2(8 * w + 4, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 2));
+    dec2(8 * w + 6, __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 3));
   }
   const int E = mx_exp_e4m3(A);
   e8[mx] = (uint8_t)(E + 127);
@@ -333,8 +428,19 @@ hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, 
   const int64_t nblk = (N + T - 1) / T;
   if (nblk == 0 || BH == 0) return hipSuccess;
   dim3 g((unsigned)nblk, (unsigned)BH);
-  if (is_f16) quant_int8_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
-  else quant_int8_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+  const int64_t chunks = (int64_t)T * D / 8;   // 16-byte chunks of a full block
+  auto go = [&](auto cpt) {
+    constexpr int C = decltype(cpt)::value;
+    if (is_f16) quant_int8_kernel<true, C><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+    else quant_int8_kernel<false, C><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+  };
+  if (chunks <= 256) go(std::integral_constant<int, 1>{});
+  else if (chunks <= 512) go(std::integral_constant<int, 2>{});
+  else if (chunks <= 1024) go(std::integral_constant<int, 4>{});
+  else if (chunks <= 2048) go(std::integral_constant<int, 8>{});
+  else if (chunks <= 4096) go(std::integral_constant<int, 16>{});
+  else if (is_f16) quant_int8_twopass<true><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+  else quant_int8_twopass<false><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
   return hipGetLastError();
 }
 

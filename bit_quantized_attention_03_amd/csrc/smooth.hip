@@ -4,7 +4,8 @@
 //
 // HBM-bound, 6 bytes per element for 16-bit K (read K twice, write K_s once):
 //   1. smooth_partial: fp32 running sum over each run of 64 tokens, in token order, for 8
-//      channels per thread (one 16-byte load per token row) -> partials [BH, runs, D].
+//      channels per thread (one 16-byte load per token row, 16 rows in flight) -> partials
+//      [BH, runs, D].
 //   2. smooth_mean:    per (bh, channel) running sum of the partials in run order, / N.
 //   3. smooth_apply:   K_s = round_to_dtype(fp32(k - mean)), 8 elements per thread.
 // The fixed summation order makes the mean reproducible bit for bit.
@@ -29,14 +30,22 @@ __global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict
   const int rows = (int)((N - t0) < RUN ? (N - t0) : RUN);
   const uint16_t* p = k + (bh * N + t0) * D + c8 * 8;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = 0; t < rows; ++t) {
-    v4i raw = *(const v4i*)(p + (int64_t)t * D);
+  auto add_row = [&](v4i raw) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       uint16_t h = (uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1)));
       s[e] = s[e] + in16_to_f32<F16>(h);
     }
+  };
+  int t = 0;
+  for (; t + 16 <= rows; t += 16) {   // 16 row loads in flight, then the adds in token order
+    v4i raw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raw[j] = *(const v4i*)(p + (int64_t)(t + j) * D);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) add_row(raw[j]);
   }
+  for (; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * D));
   float* o = part + (bh * nrun + run) * D + c8 * 8;
   *(v4f*)o = v4f{s[0], s[1], s[2], s[3]};
   *(v4f*)(o + 4) = v4f{s[4], s[5], s[6], s[7]};
@@ -50,7 +59,15 @@ __global__ __launch_bounds__(256) void smooth_mean(const float* __restrict__ par
   const int64_t bh = gid / D, c = gid % D;
   const float* p = part + bh * nrun * D + c;
   float total = 0.0f;
-  for (int64_t r = 0; r < nrun; ++r) total = total + p[r * D];
+  int64_t r = 0;
+  for (; r + 16 <= nrun; r += 16) {   // loads in flight, sums in run order
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = p[(r + j) * D];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) total = total + v[j];
+  }
+  for (; r < nrun; ++r) total = total + p[r * D];
   mean[gid] = N > 0 ? total / (float)N : 0.0f;
 }
 

@@ -77,6 +77,19 @@ def test_smooth_and_int8_bit_exact(name, ov):
                               s_o.view(np.uint32))
 
 
+@pytest.mark.parametrize("T", [1, 100, 4096])
+def test_int8_block_sizes_bit_exact(T):
+    # register-held blocks of every size class, and a block too large for registers
+    sage = _sage()
+    w = I.workload("llm_int8", B=1, Hq=2, Hkv=2, N=4500)
+    q, _, _ = I.make_qkv(w, seed=11)
+    qt = sage.quantize(q.cuda(), sage.INT8, (T, w.D))
+    c_o, s_o = oracle.quant_int8(np16(q), 0, T)
+    assert np.array_equal(qt.codes.cpu().numpy().view(np.int8).reshape(c_o.shape), c_o)
+    assert np.array_equal(qt.scales.cpu().view(torch.float32).numpy().reshape(s_o.shape).view(np.uint32),
+                          s_o.view(np.uint32))
+
+
 def test_fp8_channel_bit_exact():
     sage = _sage()
     for ov in (dict(B=1, Hq=2, Hkv=2, N=300), dict(B=1, Hq=1, Hkv=1, N=1024)):
