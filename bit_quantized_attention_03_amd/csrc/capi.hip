@@ -88,8 +88,9 @@ int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* 
   }
 }
 
-int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
-                         sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream) {
+namespace {
+int quantize_impl(const void* x, sage_fmt in_dt, sage_shape xs, const float* mean, sage_fmt fmt, sage_block block,
+                  sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream) {
   if (!x || !codes_out || !scales_out || !shape_ok(xs)) return SAGE_EINVAL;
   if (!is16(in_dt)) return SAGE_ENOTSUP;
   if (xs.D % 8 != 0) return SAGE_EINVAL;
@@ -106,15 +107,31 @@ int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt 
   const bool f16 = in_dt == SAGE_FP16;
   switch (fmt) {
     case SAGE_INT8:
-      return launched(launch_quant_int8(x, f16, BH, xs.N, (int)xs.D, block.tokens, (int8_t*)codes_out,
+      return launched(launch_quant_int8(x, f16, BH, xs.N, (int)xs.D, block.tokens, mean, (int8_t*)codes_out,
                                         (float*)scales_out, stream));
     case SAGE_E4M3:
       return launched(launch_quant_fp8_channel(x, f16, BH, xs.N, (int)xs.D, (uint8_t*)codes_out, (float*)scales_out,
                                                stream));
     default:
       return launched(launch_quant_fp4(x, f16, BH, xs.N, (int)xs.D, fmt == SAGE_NVFP4, block.channels == 1 ? 1 : 0,
-                                       (int)mode, (uint8_t*)codes_out, (uint8_t*)scales_out, stream));
+                                       (int)mode, mean, (uint8_t*)codes_out, (uint8_t*)scales_out, stream));
   }
+}
+}  // namespace
+
+int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
+                         sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream) {
+  return quantize_impl(x, in_dt, xs, nullptr, fmt, block, mode, codes_out, scales_out, stream);
+}
+
+int sage_quantize_smoothed(const void* k, sage_fmt in_dt, sage_shape ks, const float* mean, sage_fmt fmt,
+                           sage_block block, sage_scale_mode mode, void* codes_out, void* scales_out,
+                           hipStream_t stream) {
+  if (!mean) return SAGE_EINVAL;
+  if (fmt == SAGE_E4M3) return SAGE_ENOTSUP;                                          // a V format
+  if ((fmt == SAGE_MXFP4 || fmt == SAGE_NVFP4) && block.tokens != 1) return SAGE_ENOTSUP;   // along D only
+  if (!aligned16(mean)) return SAGE_EALIGN;
+  return quantize_impl(k, in_dt, ks, mean, fmt, block, mode, codes_out, scales_out, stream);
 }
 
 int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, int along_tokens, void* f8_out,

@@ -21,12 +21,31 @@
 namespace sage {
 namespace {
 
+// K smoothing applied on the fly (sage_quantize_smoothed): eight 16-bit values of channels
+// ch0 .. ch0+7 become round_to_dtype(fp32(x - mean)), the same arithmetic as the smoothing
+// kernel's output, so the quantized result equals quantizing the stored K_s.
+template <bool F16>
+__device__ __forceinline__ v4i smooth_chunk(v4i raw, const float* __restrict__ mu) {
+  const v4f m0 = *(const v4f*)mu, m1 = *(const v4f*)(mu + 4);
+  const float m[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+  v4i o;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t u = (uint32_t)raw[w];
+    const float a = in16_to_f32<F16>((uint16_t)(u & 0xffffu)) - m[2 * w];
+    const float b = in16_to_f32<F16>((uint16_t)(u >> 16)) - m[2 * w + 1];
+    o[w] = (int)((uint32_t)f32_to_in16<F16>(a) | ((uint32_t)f32_to_in16<F16>(b) << 16));
+  }
+  return o;
+}
+
 // ------------------------------------------------------------------ INT8 per block
 // One workgroup per block of T tokens x D channels; the block (T * D / 8 16-byte chunks)
 // stays in registers between the amax reduction and the encoding, so HBM is read once.
-template <bool F16, int CPT>   // CPT = 16-byte chunks per thread (T * D / 8 / 256)
+template <bool F16, int CPT, bool SMOOTH>   // CPT = 16-byte chunks per thread (T * D / 8 / 256)
 __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int T,
-                                                         int8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                         const float* __restrict__ mean, int8_t* __restrict__ codes,
+                                                         float* __restrict__ scales) {
   const int64_t nblk = (N + T - 1) / T;
   const int64_t blk = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = blk * T;
@@ -38,6 +57,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + 256 * i;
     raw[i] = c < nchunk ? *(const v4i*)(base + (int64_t)c * 8) : v4i{0, 0, 0, 0};
+    if (SMOOTH && c < nchunk) raw[i] = smooth_chunk<F16>(raw[i], mean + bh * D + (c * 8) % D);
   }
   float amax = 0.0f;
 #pragma unroll
@@ -75,9 +95,10 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
 
 // Blocks too large for registers (over 4096 chunks): amax pass, then an encoding pass whose
 // reads hit L2.
-template <bool F16>
+template <bool F16, bool SMOOTH>
 __global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __restrict__ x, int64_t N, int D, int T,
-                                                          int8_t* __restrict__ codes, float* __restrict__ scales) {
+                                                          const float* __restrict__ mean, int8_t* __restrict__ codes,
+                                                          float* __restrict__ scales) {
   const int64_t nblk = (N + T - 1) / T;
   const int64_t blk = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = blk * T;
@@ -87,6 +108,7 @@ __global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __rest
   float amax = 0.0f;
   for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
     v4i raw = *(const v4i*)(base + c * 8);
+    if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + bh * D + (c * 8) % D);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       uint32_t u = (uint32_t)raw[w];
@@ -105,6 +127,7 @@ __global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __rest
   int8_t* out = codes + (bh * N + t0) * D;
   for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
     v4i raw = *(const v4i*)(base + c * 8);
+    if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + bh * D + (c * 8) % D);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -294,8 +317,9 @@ __device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* c) {
 }
 
 // Along D: one thread per group (32 values for MX, 16 for NV) of one token row.
-template <bool F16, bool NV>
-__global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int D, int mode,
+template <bool F16, bool NV, bool SMOOTH>
+__global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t N, int D,
+                                                       int mode, const float* __restrict__ mean,
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int G = NV ? 16 : 32;
   const int gpr = D / G;
@@ -306,6 +330,7 @@ __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restric
 #pragma unroll
   for (int q = 0; q < G / 8; ++q) {
     v4i raw = *(const v4i*)(p + q * 8);
+    if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + (gid / gpr / N) * D + (gid % gpr) * G + q * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[q * 8 + e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
   }
@@ -423,24 +448,35 @@ __global__ void convert_kernel(const float* __restrict__ x, int64_t n, int fmt, 
 
 }  // namespace
 
-hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, int8_t* codes,
-                             float* scales, hipStream_t st) {
+hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, const float* mean,
+                             int8_t* codes, float* scales, hipStream_t st) {
   const int64_t nblk = (N + T - 1) / T;
   if (nblk == 0 || BH == 0) return hipSuccess;
   dim3 g((unsigned)nblk, (unsigned)BH);
   const int64_t chunks = (int64_t)T * D / 8;   // 16-byte chunks of a full block
+  const uint16_t* xs = (const uint16_t*)x;
   auto go = [&](auto cpt) {
     constexpr int C = decltype(cpt)::value;
-    if (is_f16) quant_int8_kernel<true, C><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
-    else quant_int8_kernel<false, C><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+    if (mean) {
+      if (is_f16) quant_int8_kernel<true, C, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+      else quant_int8_kernel<false, C, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+    } else {
+      if (is_f16) quant_int8_kernel<true, C, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+      else quant_int8_kernel<false, C, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+    }
   };
   if (chunks <= 256) go(std::integral_constant<int, 1>{});
   else if (chunks <= 512) go(std::integral_constant<int, 2>{});
   else if (chunks <= 1024) go(std::integral_constant<int, 4>{});
   else if (chunks <= 2048) go(std::integral_constant<int, 8>{});
   else if (chunks <= 4096) go(std::integral_constant<int, 16>{});
-  else if (is_f16) quant_int8_twopass<true><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
-  else quant_int8_twopass<false><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, T, codes, scales);
+  else if (mean) {
+    if (is_f16) quant_int8_twopass<true, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+    else quant_int8_twopass<false, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+  } else {
+    if (is_f16) quant_int8_twopass<true, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+    else quant_int8_twopass<false, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+  }
   return hipGetLastError();
 }
 
@@ -464,18 +500,24 @@ hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int6
 }
 
 hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
-                            int mode, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                            int mode, const float* mean, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   const uint16_t* xs = (const uint16_t*)x;
   if (!along_tokens) {
     const int64_t groups = BH * N * (D / (nv ? 16 : 32));
     if (groups == 0) return hipSuccess;
     const unsigned g = (unsigned)((groups + 255) / 256);
+    auto go = [&](auto f16c, auto nvc, auto smc) {
+      fp4_rows_kernel<decltype(f16c)::value, decltype(nvc)::value, decltype(smc)::value>
+          <<<g, 256, 0, st>>>(xs, BH * N, N, D, mode, mean, codes, scales);
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
     if (nv) {
-      if (is_f16) fp4_rows_kernel<true, true><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
-      else fp4_rows_kernel<false, true><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
+      if (mean) { if (is_f16) go(T_{}, T_{}, T_{}); else go(F_{}, T_{}, T_{}); }
+      else { if (is_f16) go(T_{}, T_{}, F_{}); else go(F_{}, T_{}, F_{}); }
     } else {
-      if (is_f16) fp4_rows_kernel<true, false><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
-      else fp4_rows_kernel<false, false><<<g, 256, 0, st>>>(xs, BH * N, D, mode, codes, scales);
+      if (mean) { if (is_f16) go(T_{}, F_{}, T_{}); else go(F_{}, F_{}, T_{}); }
+      else { if (is_f16) go(T_{}, F_{}, F_{}); else go(F_{}, F_{}, F_{}); }
     }
   } else {
     const int64_t nrun = (N + 63) / 64;

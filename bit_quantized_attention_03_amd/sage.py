@@ -55,6 +55,8 @@ def lib():
         L.sage_smooth_k_workspace_bytes.restype = C.c_size_t
         L.sage_smooth_k_workspace_bytes.argtypes = [Shape]
         L.sage_smooth_k.argtypes = [C.c_void_p, C.c_int, Shape, C.c_void_p, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+        L.sage_quantize_smoothed.argtypes = [C.c_void_p, C.c_int, Shape, C.c_void_p, C.c_int, Block, C.c_int, C.c_void_p,
+                                             C.c_void_p, C.c_void_p]
         L.sage_quantize_blocks.argtypes = [C.c_void_p, C.c_int, Shape, C.c_int, Block, C.c_int, C.c_void_p, C.c_void_p,
                                            C.c_void_p]
         L.sage_quantized_bytes.argtypes = [C.c_int, Block, Shape, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
@@ -147,6 +149,18 @@ def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
     return QT(fmt, codes[:cb], scales[:sb], tuple(x.shape))
 
 
+def quantize_smoothed(k: torch.Tensor, mean: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
+    """Quantize K_s = round(k - mean) without storing it (same codes as quantize(K_s, ...))."""
+    _dev(k)
+    cb, sb = quantized_bytes(fmt, block, tuple(k.shape))
+    codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=k.device)
+    scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=k.device)
+    _check("sage_quantize_smoothed", lib().sage_quantize_smoothed(_ptr(k), _TORCH_FMT[k.dtype], _shape(k), _ptr(mean), fmt,
+                                                                  Block(*block), mode, _ptr(codes), _ptr(scales),
+                                                                  _stream()))
+    return QT(fmt, codes[:cb], scales[:sb], tuple(k.shape))
+
+
 def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
     """NVFP4 codes and UE4M3 scales (as sage_quantize_blocks wrote them) -> E4M3 codes with
     E8M0 scales per 32 elements, the operand form of the scaled FP8 matrix product."""
@@ -204,7 +218,7 @@ VARIANTS = ("int8", "int8_fp8pv", "mxfp4", "nvfp4_search", "thrift")
 class Pass:
     """Intermediate tensors of one forward pass (kept for parity checks)."""
     mean: torch.Tensor
-    k_smoothed: torch.Tensor
+    k_smoothed: Optional[torch.Tensor]   # None when K was quantized with smoothing on the fly
     q: QT
     k: QT
     v: QT
@@ -214,14 +228,21 @@ class Pass:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str = "int8",
             sm_scale: float = 0.0, thrift_frac: float = 0.05, search_mode: int = SEARCH,
-            out_dtype: torch.dtype = torch.float32) -> Pass:
-    """K smoothing -> block quantization -> (Thrift selection) -> fused attention."""
+            out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False) -> Pass:
+    """K smoothing -> block quantization -> (Thrift selection) -> fused attention.  K_s is only
+    materialized when Thrift needs it (or keep_smoothed); otherwise K is quantized with the
+    smoothing applied on the fly (identical codes)."""
     B, Hq, N, D = q.shape
-    mean, ks = smooth_k(k)
+    need_ks = variant == "thrift" or keep_smoothed
+    mean, ks = smooth_k(k, want_smoothed=need_ks)
+
+    def quant_k(fmt, block, mode=ABSMAX):
+        return quantize(ks, fmt, block, mode) if ks is not None else quantize_smoothed(k, mean, fmt, block, mode)
+
     mask = None
     if variant in ("int8", "int8_fp8pv", "thrift"):
         qq = quantize(q, INT8, (128, D))
-        kq = quantize(ks, INT8, (64, D))
+        kq = quant_k(INT8, (64, D))
         if variant == "int8_fp8pv":
             vq = quantize(v, E4M3, (0, 1))
             out = attn_fwd(qq, kq, vq, causal, E4M3, sm_scale, out_dtype=out_dtype)
@@ -235,12 +256,12 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
                 out = attn_fwd(qq, kq, vq, causal, BF16, sm_scale, out_dtype=out_dtype)
     elif variant == "mxfp4":
         qq = quantize(q, MXFP4, (1, 32))
-        kq = quantize(ks, MXFP4, (1, 32))
+        kq = quant_k(MXFP4, (1, 32))
         vq = quantize(v, MXFP4, (32, 1))
         out = attn_fwd(qq, kq, vq, causal, MXFP4, sm_scale, out_dtype=out_dtype)
     elif variant == "nvfp4_search":
         qq = nvfp4_to_mxfp8(quantize(q, NVFP4, (1, 16), search_mode), False)
-        kq = nvfp4_to_mxfp8(quantize(ks, NVFP4, (1, 16), search_mode), False)
+        kq = nvfp4_to_mxfp8(quant_k(NVFP4, (1, 16), search_mode), False)
         vq = nvfp4_to_mxfp8(quantize(v, NVFP4, (16, 1), search_mode), True)
         out = attn_fwd(qq, kq, vq, causal, NVFP4, sm_scale, out_dtype=out_dtype)
     else:

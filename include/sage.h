@@ -128,6 +128,18 @@ size_t sage_smooth_k_workspace_bytes(sage_shape ks);
  * Scale mode must be SAGE_SCALE_ABSMAX except for SAGE_NVFP4.                            */
 int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
                          sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream);
+/* Block quantization of smoothed K without storing it — SageAttention (Technical approach:
+ * K smoothing before 8-bit quantization).  Produces exactly the codes and scales
+ * sage_quantize_blocks would produce for K_s = round_to_dtype(fp32(k - mean)), the K_s of
+ * sage_smooth_k, without writing K_s (2 bytes per element less HBM traffic each way).
+ *   k     [B,H,N,D] in in_dt (SAGE_BF16 | SAGE_FP16); mean [B,H,D] fp32 (sage_smooth_k's
+ *         mean_out), 16-byte aligned.
+ *   fmt   SAGE_INT8 (blocks (T, D)), SAGE_MXFP4 (1, 32) or SAGE_NVFP4 (1, 16) along D; other
+ *         formats and token-axis blocks return SAGE_ENOTSUP.  Layouts as sage_quantize_blocks. */
+int sage_quantize_smoothed(const void* k, sage_fmt in_dt, sage_shape ks, const float* mean, sage_fmt fmt,
+                           sage_block block, sage_scale_mode mode, void* codes_out, void* scales_out,
+                           hipStream_t stream);
+
 /* Host-side size query for the outputs of sage_quantize_blocks (host pointers out). */
 int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* codes_bytes, size_t* scale_bytes);
 

@@ -100,6 +100,16 @@ def test_validation_before_launch(L):
     assert L.sage_nvfp4_to_mxfp8(0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 64, 48), 0, 0x1000_0000, 0x1000_0000,
                                  None) == -1
     assert L.sage_nvfp4_to_mxfp8(0x1000_0008, 0x1000_0000, shp, 0, 0x1000_0000, 0x1000_0000, None) == -3
+    # fused smoothing + quantization: mean required, K formats along D only, aligned mean
+    blk = sage.Block(64, 128)
+    assert L.sage_quantize_smoothed(0x1000_0000, sage.BF16, shp, None, sage.INT8, blk, 0, 0x1000_0000, 0x1000_0000,
+                                    None) == -1
+    assert L.sage_quantize_smoothed(0x1000_0000, sage.BF16, shp, 0x1000_0000, sage.E4M3, sage.Block(0, 1), 0,
+                                    0x1000_0000, 0x1000_0000, None) == -2
+    assert L.sage_quantize_smoothed(0x1000_0000, sage.BF16, shp, 0x1000_0000, sage.MXFP4, sage.Block(32, 1), 0,
+                                    0x1000_0000, 0x1000_0000, None) == -2
+    assert L.sage_quantize_smoothed(0x1000_0000, sage.BF16, shp, 0x1000_0004, sage.INT8, blk, 0, 0x1000_0000,
+                                    0x1000_0000, None) == -3
     # smoothing workspace
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
 

@@ -77,6 +77,21 @@ def test_smooth_and_int8_bit_exact(name, ov):
                               s_o.view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt,block,mode", [("INT8", (64, 128), 0), ("INT8", (100, 128), 0), ("INT8", (4096, 128), 0),
+                                            ("MXFP4", (1, 32), 0), ("NVFP4", (1, 16), 1), ("NVFP4", (1, 16), 2)])
+def test_quantize_smoothed_equals_quantize_of_smoothed(fmt, block, mode):
+    # smoothing applied on the fly gives the codes and scales of quantizing the stored K_s
+    sage = _sage()
+    w = I.workload("llm_int8", B=1, Hq=2, Hkv=2, N=4500)
+    _, k, _ = I.make_qkv(w, seed=12)
+    kg = k.cuda()
+    mean, ks = sage.smooth_k(kg)
+    f = getattr(sage, fmt)
+    a = sage.quantize(ks, f, block, mode)
+    b = sage.quantize_smoothed(kg, mean, f, block, mode)
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
 @pytest.mark.parametrize("T", [1, 100, 4096])
 def test_int8_block_sizes_bit_exact(T):
     # register-held blocks of every size class, and a block too large for registers
