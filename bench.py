@@ -36,7 +36,8 @@ VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "int8_fp8pv": "int8
                  "nvfp4_search": "nvfp4->mxfp8"}
 
 
-KERNEL_SOURCES = {"int8": ("attn_i8.hip",), "thrift": ("attn_i8.hip",), "int8_fp8pv": ("attn_i8.hip",),
+KERNEL_SOURCES = {"int8": ("attn_i8.hip", "attn_common.hpp"), "thrift": ("attn_i8.hip", "attn_common.hpp"),
+                  "int8_fp8pv": ("attn_i8.hip", "attn_common.hpp"),
                   "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp")}
 
 

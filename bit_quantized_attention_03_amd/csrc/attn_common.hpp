@@ -32,18 +32,22 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Workgroup -> (b*Hq + h, pair of Q blocks).  Consecutive pairs of one head go to one XCD
-// (workgroups are dealt round-robin over the 8 XCDs), so they share its L2; causal runs
-// take the heaviest pairs first.
+// Workgroup -> (b*Hq + h, pair of Q blocks).  Consecutive work items go to one XCD
+// (workgroups are dealt round-robin over the 8 XCDs), so neighbouring heads share its L2.
+// Causal runs take two heads at a time and walk their pairs from the heaviest down, the two
+// heads interleaved: the long pairs of a group start together and the short ones fill the
+// tail, while each XCD still streams the K/V of only a few heads at once.
 struct WgMap {
   int64_t bh, pair;
 };
 __device__ __forceinline__ WgMap map_workgroup(int64_t total_wg, int64_t n_pairs, bool causal) {
   int64_t wg = blockIdx.x;
   if ((total_wg & 7) == 0) wg = (wg & 7) * (total_wg >> 3) + (wg >> 3);
-  WgMap m{wg / n_pairs, wg % n_pairs};
-  if (causal) m.pair = n_pairs - 1 - m.pair;
-  return m;
+  if (!causal) return WgMap{wg / n_pairs, wg % n_pairs};
+  const int64_t g = wg / (2 * n_pairs), j = wg % (2 * n_pairs);
+  if ((g + 1) * 2 * n_pairs > total_wg)                  // odd head count: the last head alone
+    return WgMap{2 * g, n_pairs - 1 - j};
+  return WgMap{2 * g + (j & 1), n_pairs - 1 - (j >> 1)};
 }
 
 }  // namespace attn

@@ -41,6 +41,7 @@
 // The causal mask is top-left aligned; tiles entirely above a wave's rows are skipped and
 // workgroups are scheduled heaviest first.  Workgroup ids are remapped so consecutive Q-block
 // pairs of one head run on the same XCD and share its L2.
+#include "attn_common.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
 
@@ -191,12 +192,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   __shared__ __attribute__((aligned(16))) uint8_t vb1[S::V_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vb2[S::V_BYTES];
 
-  // ---- workgroup -> (b, h, pair of Q blocks); XCD-aware: consecutive work items on one XCD
-  int64_t wg = blockIdx.x;
-  if ((p.total_wg & 7) == 0) wg = (wg & 7) * (p.total_wg >> 3) + (wg >> 3);
-  const int64_t bh = wg / p.nPairs;
-  int64_t pr = wg % p.nPairs;
-  if (CAUSAL) pr = p.nPairs - 1 - pr;         // heaviest pairs first
+  const attn::WgMap wm = attn::map_workgroup(p.total_wg, p.nPairs, CAUSAL);
+  const int64_t bh = wm.bh, pr = wm.pair;
   const int64_t b = bh / p.Hq, h = bh % p.Hq;
   const int64_t bkv = b * p.Hkv + h / (p.Hq / p.Hkv);
 
