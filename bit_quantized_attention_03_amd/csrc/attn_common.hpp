@@ -34,9 +34,11 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 // Workgroup -> (b*Hq + h, pair of Q blocks).  Consecutive work items go to one XCD
 // (workgroups are dealt round-robin over the 8 XCDs), so neighbouring heads share its L2.
-// Causal runs take two heads at a time and walk their pairs from the heaviest down, the two
-// heads interleaved: the long pairs of a group start together and the short ones fill the
-// tail, while each XCD still streams the K/V of only a few heads at once.
+// Causal runs take four heads at a time and walk their pairs from the heaviest down, the four
+// heads interleaved.  Within an XCD the dispatcher deals workgroups round-robin over its four
+// shader engines and waits when the next one has no free CU, so each run of four consecutive
+// workgroups (one per engine) has the same length: they finish together and free one CU on
+// every engine for the next four.  Heaviest first lets the short pairs fill the tail.
 struct WgMap {
   int64_t bh, pair;
 };
@@ -44,10 +46,11 @@ __device__ __forceinline__ WgMap map_workgroup(int64_t total_wg, int64_t n_pairs
   int64_t wg = blockIdx.x;
   if ((total_wg & 7) == 0) wg = (wg & 7) * (total_wg >> 3) + (wg >> 3);
   if (!causal) return WgMap{wg / n_pairs, wg % n_pairs};
-  const int64_t g = wg / (2 * n_pairs), j = wg % (2 * n_pairs);
-  if ((g + 1) * 2 * n_pairs > total_wg)                  // odd head count: the last head alone
-    return WgMap{2 * g, n_pairs - 1 - j};
-  return WgMap{2 * g + (j & 1), n_pairs - 1 - (j >> 1)};
+  constexpr int64_t G = 4;
+  const int64_t heads = total_wg / n_pairs;
+  const int64_t g = wg / (G * n_pairs), j = wg % (G * n_pairs);
+  const int64_t r = heads - G * g < G ? heads - G * g : G;   // heads in this group
+  return WgMap{G * g + j % r, n_pairs - 1 - j / r};
 }
 
 }  // namespace attn
