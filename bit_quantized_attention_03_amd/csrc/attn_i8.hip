@@ -52,6 +52,10 @@ namespace {
 
 constexpr int QB = 128, KT = 64, NWAVES = 8, NTHREADS = 64 * NWAVES;
 constexpr float LOG2E = 1.4426950408889634f;
+// 1.5 * 2^23 and its bit pattern: an int32 x with |x| < 2^22 added to the pattern gives the
+// float kMagic + x exactly.
+constexpr float kMagic = 12582912.0f;
+constexpr int kMagicBits = 0x4B400000;
 
 struct Params {
   const int8_t* q; const float* qs;
@@ -260,7 +264,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   for (int c = 0; c < NCC; ++c) o[c] = v16f{};
   float m_run = -__builtin_inff(), l_run = 0.0f;
   float m_lo = 0.0f;            // FP8 P: the running max is the pair m_run + m_lo
-  v16i acc[2];                  // S of the tile the next VALU phase works on
+  v16i acc[2];                  // S of the tile the next VALU phase works on (FP8 P: kMagic + S)
+  v16i magic;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
   bool hi = false;              // that tile runs on bf16 (Thrift)
   float dq = 0.0f;              // its dequantization factor (log2 units)
   float dq_lo = 0.0f;           // FP8 P: dq + dq_lo = s_q s_k sm_scale log2(e) to ~2^-40
@@ -299,9 +306,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
     }
     const int64_t key0 = (int64_t)t * KT;
     if (!hi) {
-      acc[0] = v16i{}; acc[1] = v16i{};
+      // FP8 P: the integer sums start at the bit pattern of 1.5 * 2^23, so each result read as
+      // a float is 1.5 * 2^23 + S exactly (|S| <= 128 * 128 * D < 2^22) and S - S_max is one
+      // float subtraction.  (The bf16 path converts S directly: the start value would cost as
+      // many register moves per tile as the conversions it saves.)
 #pragma unroll
-      for (int kc = 0; kc < D / 32; ++kc)
+      for (int bb = 0; bb < 2; ++bb) acc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0][bb], qf[0], PV8 ? magic : v16i{}, 0, 0, 0);
+#pragma unroll
+      for (int kc = 1; kc < D / 32; ++kc)
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb) acc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kc][bb], qf[kc], acc[bb], 0, 0, 0);
     } else {   // Thrift tile: bf16 Q and K_s fragments straight from global memory (L2)
@@ -334,7 +346,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
       // the exponent is (acc - acc_max) * dq + c with the integer tile max taken out first and
       // c = tile max - running max + log2(1.75), both maxima carried as exact two-float sums;
       // the remaining factor 2^8 of 448 is applied exactly by the conversion's scale.
-      constexpr int SENT = -(1 << 30);
+      constexpr int SENT = 0;   // below every kMagic + S
       if (edge) {
 #pragma unroll
         for (int bb = 0; bb < 2; ++bb)
@@ -352,7 +364,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
         const int i0 = (int)sw[0], i1 = (int)sw[1];
         im = i0 > i1 ? i0 : i1;
       }
-      const float fi = (float)im;   // exact: |acc| < 2^24
+      const float fi = __int_as_float(im) - kMagic;   // exact
       float th = -__builtin_inff(), tl = 0.0f;   // tile row max (log2 units) = th + tl
       if (im > SENT) {
         th = fi * dq;
@@ -373,7 +385,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {   // 1.75 P, kept in the accumulator registers
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf((float)(acc[bb][r] - im), dq, c0));
+          // both terms lie in [2^23, 2^24): their difference S - S_max is exact
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(__int_as_float(acc[bb][r]) - __int_as_float(im), dq, c0));
           lsum += e;
           acc[bb][r] = __float_as_int(e);
         }
