@@ -24,7 +24,7 @@
 //       16-channel block), or on the scaled FP8 MFMA (32x32x64) with V stored channel-major.
 //
 // Ping-pong schedule.  Each wave alternates a VALU phase (softmax of tile t) and an MFMA
-// phase (P.V of tile t, then S of tile t+1).  Group B runs one phase behind group A, so on
+// phase (P.V of tile t and S of tile t+1; Thrift issues S first).  Group B runs one phase behind group A, so on
 // every SIMD (one wave of each group) one wave keeps the matrix core busy while the other
 // uses the vector ALU.  Phases are separated by workgroup barriers:
 //     phase 2t+2: A = MFMA(t), B = VALU(t);   phase 2t+3: A = VALU(t+1), B = MFMA(t).
@@ -301,8 +301,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
       const float kh = qscale * ksc, kl = __builtin_fmaf(qscale, ksc, -kh);
       dq = kh * p.sm_log2;
       dq_lo = __builtin_fmaf(kh, p.sm_log2, -dq) + __builtin_fmaf(kh, p.sm_log2_lo, kl * p.sm_log2);
-    } else {
-      dq = __builtin_fmaxf(hi ? p.sm_log2 : qscale * k_scales[uni(bkv * p.nKB + t)] * p.sm_log2, 1.17549435e-38f);
+    } else if (!THRIFT) {
+      dq = __builtin_fmaxf(qscale * k_scales[uni(bkv * p.nKB + t)] * p.sm_log2, 1.17549435e-38f);
     }
     const int64_t key0 = (int64_t)t * KT;
     if (!hi) {
@@ -335,6 +335,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   // ---- VALU phase: softmax of tile t -> P in pk
   auto valu_phase = [&](int t) __attribute__((always_inline)) {
     if (!active(t)) return;
+    // Thrift: the dequantization factor is formed here rather than next to the matrix
+    // instructions, where a scalar load in flight would force every LDS wait to zero.
+    if (THRIFT) dq = __builtin_fmaxf(hi ? p.sm_log2 : qscale * k_scales[uni(bkv * p.nKB + t)] * p.sm_log2, 1.17549435e-38f);
     const int64_t key0 = (int64_t)t * KT;
     const bool edge = (key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0);   // causal diagonal or ragged
     auto masked = [&](int bb, int r) __attribute__((always_inline)) {
@@ -451,13 +454,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
       for (int r = 0; r < 16; r += 2) pk[8 * bb + (r >> 1)] = pack_bf16x2(s[bb][r], s[bb][r + 1]);
   };
 
-  // ---- MFMA phase: O += P(t) V(t), then S of tile t+1 (group A also issues the tile loads).
-  //      LDS fragment reads run one k-group ahead of the matrix instructions that use them.
-  auto v_frag = [&](const uint8_t* vs, int kg, int cc) __attribute__((always_inline)) -> v8bf {
+  // ---- MFMA phase: S of tile t+1 and O += P(t) V(t) (group A also issues the tile loads).
+  //      Thrift: every LDS fragment read is issued well ahead of the matrix instruction that
+  //      consumes it: the K fragments of tile t+1 and the first V k-group, then S(t+1) (whose
+  //      bf16 tiles read Q and K_s from L2 and so start early), then per k-group the read of
+  //      k-group kg + 1 and the P.V products of kg.  Scheduling barriers keep that order:
+  //      left alone, the compiler sinks each read next to its use to save registers and then
+  //      waits for every read in turn.  Plain bf16 P and FP8 P run P.V first with the V reads
+  //      one k-group ahead, then S(t+1): measured faster for them (1.5 % and 3 %).
+  auto v_read = [&](const uint8_t* vs, int kg, int cc) __attribute__((always_inline)) -> v8us {
     const uint8_t* a0 = vs + vro[cc] + 8 * kg * 2 * D;
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0));
     const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(a0 + 4 * 2 * D));
-    v8us raw = __builtin_bit_cast(v8us, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+    return __builtin_bit_cast(v8us, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto v_bf16 = [&](v8us raw) __attribute__((always_inline)) -> v8bf {
     if (VF16) {   // fp16 V is multiplied as bf16 (nearest-even)
       v4i pkd;
 #pragma unroll
@@ -467,26 +478,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
     return __builtin_bit_cast(v8bf, raw);
   };
   auto mfma_phase = [&](int t, const uint8_t* vs, const uint8_t* kbn) __attribute__((always_inline)) {
-    const bool next = active(t + 1);
-    if (next) qk_load(t + 1, kbn);
-    if (active(t)) {
-      if (!PV8) {
-        v8bf vf[2][NCC];
+    const bool an = active(t + 1), at = active(t);
+    if (an) qk_load(t + 1, kbn);
+    if (THRIFT) {
+      v8us vf[2][NCC];
+      if (at) {
 #pragma unroll
-        for (int cc = 0; cc < NCC; ++cc) vf[0][cc] = v_frag(vs, 0, cc);
+        for (int cc = 0; cc < NCC; ++cc) vf[0][cc] = v_read(vs, 0, cc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (an) qk_mfma(t + 1);
+      if (at) {
 #pragma unroll
         for (int kg = 0; kg < 4; ++kg) {
           if (kg + 1 < 4) {
 #pragma unroll
-            for (int cc = 0; cc < NCC; ++cc) vf[(kg + 1) & 1][cc] = v_frag(vs, kg + 1, cc);
+            for (int cc = 0; cc < NCC; ++cc) vf[(kg + 1) & 1][cc] = v_read(vs, kg + 1, cc);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const v8bf pf = __builtin_bit_cast(v8bf, v4i{(int)pk[4 * kg], (int)pk[4 * kg + 1], (int)pk[4 * kg + 2],
+                                                        (int)pk[4 * kg + 3]});
+#pragma unroll
+          for (int cc = 0; cc < NCC; ++cc)
+            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_bf16(vf[kg & 1][cc]), pf, o[cc], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else if (!PV8) {
+      if (at) {
+        v8us vf[2][NCC];
+#pragma unroll
+        for (int cc = 0; cc < NCC; ++cc) vf[0][cc] = v_read(vs, 0, cc);
+#pragma unroll
+        for (int kg = 0; kg < 4; ++kg) {
+          if (kg + 1 < 4) {
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) vf[(kg + 1) & 1][cc] = v_read(vs, kg + 1, cc);
           }
           const v8bf pf = __builtin_bit_cast(v8bf, v4i{(int)pk[4 * kg], (int)pk[4 * kg + 1], (int)pk[4 * kg + 2],
                                                         (int)pk[4 * kg + 3]});
 #pragma unroll
           for (int cc = 0; cc < NCC; ++cc)
-            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[kg & 1][cc], pf, o[cc], 0, 0, 0);
+            o[cc] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_bf16(vf[kg & 1][cc]), pf, o[cc], 0, 0, 0);
         }
-      } else {
+      }
+      if (an) qk_mfma(t + 1);
+    } else {
+      if (at) {
         const v8i pf = v8i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
         v8i vf[NCC];
 #pragma unroll
@@ -501,8 +539,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
         for (int cc = 0; cc < NCC; ++cc)
           o[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[cc], pf, o[cc], 0, 0, 0, 127, 0, 127);
       }
+      if (an) qk_mfma(t + 1);
     }
-    if (next) qk_mfma(t + 1);
   };
 
   // ---- the schedule.  Both groups run the same program (MFMA phase of tile t, barrier, VALU
