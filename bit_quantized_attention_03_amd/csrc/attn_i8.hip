@@ -552,11 +552,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   // one step: MFMA phase of tile t, barrier, VALU phase of tile t+1, barrier; jc = t mod 3
   auto step = [&](int t, auto jc) __attribute__((always_inline)) {
     constexpr int J = decltype(jc)::value;
+    // Group A issues the tile loads at the start of its VALU phase; the FP8-P variant issues them
+    // one phase earlier, at the start of its MFMA phase (measured faster there, slower for bf16
+    // P): K(t) and V(t-1), whose buffers they fill, were last read (by group B) in the phase
+    // before either.
+    const bool ld_k = grp == 0 && t + 3 < nT, ld_v = grp == 0 && t + 2 < nT;   // ld_k implies ld_v
+    auto issue_loads = [&]() __attribute__((always_inline)) {
+      if (ld_k) dma.k_tile(p, bkv, t + 3, kbuf(std::integral_constant<int, J>{}), a);
+      if (ld_v) dma.v_tile(p, bkv, t + 2, vbuf(std::integral_constant<int, J + 2>{}), a);
+    };
+    if (PV8) issue_loads();
     mfma_phase(t, vbuf(std::integral_constant<int, J>{}), kbuf(std::integral_constant<int, J + 1>{}));
     phase_barrier();
-    const bool ld_k = grp == 0 && t + 3 < nT, ld_v = grp == 0 && t + 2 < nT;   // ld_k implies ld_v
-    if (ld_k) dma.k_tile(p, bkv, t + 3, kbuf(std::integral_constant<int, J>{}), a);
-    if (ld_v) dma.v_tile(p, bkv, t + 2, vbuf(std::integral_constant<int, J + 2>{}), a);
+    if (!PV8) issue_loads();
     valu_phase(t + 1);
     if (grp == 0) {   // the previous step's loads are complete; this step's may still fly
       if (ld_k) wait_vmem_n<KR + VR>();
