@@ -515,6 +515,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 #pragma unroll
             for (int cc = 0; cc < NCC; ++cc) vf[(kg + 1) & 1][cc] = v_read(vs, kg + 1, cc);
           }
+          __builtin_amdgcn_sched_barrier(0);
           const v8bf pf = __builtin_bit_cast(v8bf, v4i{(int)pk[4 * kg], (int)pk[4 * kg + 1], (int)pk[4 * kg + 2],
                                                         (int)pk[4 * kg + 3]});
 #pragma unroll
