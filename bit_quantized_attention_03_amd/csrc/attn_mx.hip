@@ -374,12 +374,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   // ---- the schedule (as in the INT8 kernel): group B one barrier behind group A
   if (grp == 1) phase_barrier();
   for (int t = -1; t < nT; ++t) {
-    mfma_phase(t);
-    phase_barrier();
+    // group A issues the next tiles at the start of its MFMA phase (its vector slots are idle
+    // there): the stages of K(t) and V(t-1) they fill were last read, by group B, in the phase
+    // before, and the loads get two phases to land
     if (grp == 0) {
       if (t + 2 < nT) dma.k_tile(p, bkv, t + 2, kst(t + 2), a, lane);
       if (t + 1 < nT) dma.v_tile(p, bkv, t + 1, vst(t + 1), a, lane);
     }
+    mfma_phase(t);
+    phase_barrier();
     valu_phase(t + 1);
     if (grp == 0) wait_vmem();
     phase_barrier();
