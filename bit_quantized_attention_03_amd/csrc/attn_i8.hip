@@ -264,10 +264,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
   for (int c = 0; c < NCC; ++c) o[c] = v16f{};
   float m_run = -__builtin_inff(), l_run = 0.0f;
   float m_lo = 0.0f;            // FP8 P: the running max is the pair m_run + m_lo
-  v16i acc[2];                  // S of the tile the next VALU phase works on (FP8 P: kMagic + S)
-  v16i magic;
+  v16i acc[2];                  // S of the tile the next VALU phase works on (kMagic + S; Thrift: S)
+  v16i magic;   // opaque to the compiler, so it stays in registers instead of being rebuilt per tile
 #pragma unroll
-  for (int r = 0; r < 16; ++r) magic[r] = kMagicBits;
+  for (int r = 0; r < 16; ++r) {
+    int m;
+    __asm__ volatile("v_mov_b32 %0, %1" : "=v"(m) : "s"(kMagicBits));
+    magic[r] = m;
+  }
   bool hi = false;              // that tile runs on bf16 (Thrift)
   float dq = 0.0f;              // its dequantization factor (log2 units)
   float dq_lo = 0.0f;           // FP8 P: dq + dq_lo = s_q s_k sm_scale log2(e) to ~2^-40
@@ -306,12 +310,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
     }
     const int64_t key0 = (int64_t)t * KT;
     if (!hi) {
-      // FP8 P: the integer sums start at the bit pattern of 1.5 * 2^23, so each result read as
-      // a float is 1.5 * 2^23 + S exactly (|S| <= 128 * 128 * D < 2^22) and S - S_max is one
-      // float subtraction.  (The bf16 path converts S directly: the start value would cost as
-      // many register moves per tile as the conversions it saves.)
+      // The integer sums start at the bit pattern of 1.5 * 2^23 (held in registers), so each
+      // result read as a float is 1.5 * 2^23 + S exactly (|S| <= 128 * 128 * D < 2^22): one
+      // full-rate subtraction recovers S (FP8 P: S - S_max), where a conversion runs at half
+      // rate.  Thrift keeps a zero start: its bf16 tiles return floats in the same registers.
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) acc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0][bb], qf[0], PV8 ? magic : v16i{}, 0, 0, 0);
+      for (int bb = 0; bb < 2; ++bb) acc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0][bb], qf[0], (PV8 || !THRIFT) ? magic : v16i{}, 0, 0, 0);
 #pragma unroll
       for (int kc = 1; kc < D / 32; ++kc)
 #pragma unroll
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[bb][r] = hi ? __int_as_float(acc[bb][r]) : (float)acc[bb][r];
+      for (int r = 0; r < 16; ++r) s[bb][r] = THRIFT ? (hi ? __int_as_float(acc[bb][r]) : (float)acc[bb][r]) : __int_as_float(acc[bb][r]) - kMagic;
     if (edge) {
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
