@@ -25,8 +25,7 @@ namespace {
 // ch0 .. ch0+7 become round_to_dtype(fp32(x - mean)), the same arithmetic as the smoothing
 // kernel's output, so the quantized result equals quantizing the stored K_s.
 template <bool F16>
-__device__ __forceinline__ v4i smooth_chunk(v4i raw, const float* __restrict__ mu) {
-  const v4f m0 = *(const v4f*)mu, m1 = *(const v4f*)(mu + 4);
+__device__ __forceinline__ v4i smooth_vals(v4i raw, const v4f m0, const v4f m1) {
   const float m[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
   v4i o;
 #pragma unroll
@@ -37,6 +36,10 @@ __device__ __forceinline__ v4i smooth_chunk(v4i raw, const float* __restrict__ m
     o[w] = (int)((uint32_t)f32_to_in16<F16>(a) | ((uint32_t)f32_to_in16<F16>(b) << 16));
   }
   return o;
+}
+template <bool F16>
+__device__ __forceinline__ v4i smooth_chunk(v4i raw, const float* __restrict__ mu) {
+  return smooth_vals<F16>(raw, *(const v4f*)mu, *(const v4f*)(mu + 4));
 }
 
 // ------------------------------------------------------------------ INT8 per block
@@ -57,7 +60,21 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + 256 * i;
     raw[i] = c < nchunk ? *(const v4i*)(base + (int64_t)c * 8) : v4i{0, 0, 0, 0};
-    if (SMOOTH && c < nchunk) raw[i] = smooth_chunk<F16>(raw[i], mean + bh * D + (c * 8) % D);
+  }
+  if (SMOOTH) {
+    if ((2048 % D) == 0) {   // chunks tid + 256 i all start at channel 8 tid mod D: one mean slice
+      const float* mu = mean + bh * D + (threadIdx.x * 8) % D;
+      const v4f m0 = *(const v4f*)mu, m1 = *(const v4f*)(mu + 4);
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+        if (threadIdx.x + 256 * i < nchunk) raw[i] = smooth_vals<F16>(raw[i], m0, m1);
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = threadIdx.x + 256 * i;
+        if (c < nchunk) raw[i] = smooth_chunk<F16>(raw[i], mean + bh * D + (c * 8) % D);
+      }
+    }
   }
   float amax = 0.0f;
 #pragma unroll

@@ -4,8 +4,8 @@
 //
 // HBM-bound, 6 bytes per element for 16-bit K (read K twice, write K_s once):
 //   1. smooth_partial: fp32 running sum over each run of 64 tokens, in token order, for 8
-//      channels per thread (one 16-byte load per token row, 16 rows in flight) -> partials
-//      [BH, runs, D].
+//      channels per thread (one 16-byte load per token row; batches of 16 rows, the next
+//      batch in flight while the current one is added) -> partials [BH, runs, D].
 //   2. smooth_mean:    per (bh, channel) running sum of the partials in run order, / N.
 //   3. smooth_apply:   K_s = round_to_dtype(fp32(k - mean)), 8 elements per thread.
 // The fixed summation order makes the mean reproducible bit for bit.
@@ -37,15 +37,23 @@ __global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict
       s[e] = s[e] + in16_to_f32<F16>(h);
     }
   };
-  int t = 0;
-  for (; t + 16 <= rows; t += 16) {   // 16 row loads in flight, then the adds in token order
-    v4i raw[16];
+  if (rows == RUN) {   // a full run: four batches of 16 rows, the next batch in flight while
+                       // the current one is added (in token order)
+    v4i raw[2][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) raw[j] = *(const v4i*)(p + (int64_t)(t + j) * D);
+    for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * D);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) add_row(raw[j]);
+    for (int b = 0; b < RUN / 16; ++b) {
+      if (b + 1 < RUN / 16) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * D);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) add_row(raw[b & 1][j]);
+    }
+  } else {
+    for (int t = 0; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * D));
   }
-  for (; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * D));
   float* o = part + (bh * nrun + run) * D + c8 * 8;
   *(v4f*)o = v4f{s[0], s[1], s[2], s[3]};
   *(v4f*)(o + 4) = v4f{s[4], s[5], s[6], s[7]};
