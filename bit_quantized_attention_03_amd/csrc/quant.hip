@@ -166,25 +166,59 @@ __global__ void fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 template <bool F16>
 __global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __restrict__ x, int64_t BH, int64_t N, int D,
                                                            uint32_t* __restrict__ amax_bits) {
-  // thread: (bh, run of 64 tokens, 8 channels)
+  // thread: (bh, run of 64 tokens, 8 channels); lanes of one wave cover D/8 channel groups of
+  // consecutive runs
   const int64_t nrun = (N + 63) / 64;
   const int cg = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= BH * nrun * cg) return;
+  const bool valid = gid < BH * nrun * cg;
   const int c8 = (int)(gid % cg);
   const int64_t run = (gid / cg) % nrun, bh = gid / cg / nrun;
-  const int64_t t0 = run * 64;
-  const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
-  const uint16_t* p = x + (bh * N + t0) * D + c8 * 8;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = 0; t < rows; ++t) {
-    v4i raw = *(const v4i*)(p + (int64_t)t * D);
+  auto take = [&](v4i raw) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))))));
-  }
+  };
+  if (valid) {
+    const int64_t t0 = run * 64;
+    const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
+    const uint16_t* p = x + (bh * N + t0) * D + c8 * 8;
+    if (rows == 64) {   // four batches of 16 rows, the next one in flight while the current is taken
+      v4i raw[2][16];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) atomicMax(amax_bits + bh * D + c8 * 8 + e, __float_as_uint(m[e]));
+      for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * D);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b + 1 < 4) {
+#pragma unroll
+          for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * D);
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) take(raw[b & 1][j]);
+      }
+    } else {
+      for (int t = 0; t < rows; ++t) take(*(const v4i*)(p + (int64_t)t * D));
+    }
+  }
+  // Lanes l, l + cg, l + 2cg, ... hold the same channels of consecutive runs; when the whole
+  // wave is valid and in one head, fold them (max is order-free) and let the first cg lanes
+  // issue the atomics.
+  const int lane = threadIdx.x & 63;
+  const int64_t bh0 = __shfl(bh, 0), bh63 = __shfl(bh, 63);
+  const bool fold = (cg & (cg - 1)) == 0 && cg < 64 && __all(valid) && bh0 == bh63;
+  if (fold) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      for (int sft = cg; sft < 64; sft <<= 1) m[e] = __builtin_fmaxf(m[e], __shfl_xor(m[e], sft));
+    if (lane < cg) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) atomicMax(amax_bits + bh * D + c8 * 8 + e, __float_as_uint(m[e]));
+    }
+  } else if (valid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) atomicMax(amax_bits + bh * D + c8 * 8 + e, __float_as_uint(m[e]));
+  }
 }
 
 __global__ void channel_scale_kernel(uint32_t* sc, int64_t n) {
