@@ -213,6 +213,10 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
   if (ks.B != qs.B || ks.N != qs.N || ks.D != qs.D || qs.H % ks.H != 0 || qs.D % 8 != 0) return SAGE_EINVAL;
   if (dt != SAGE_BF16 || q_block != QBLK || k_block != KBLK) return SAGE_ENOTSUP;
   if (!(frac >= 0.0 && frac <= 1.0) || (causal != 0 && causal != 1)) return SAGE_EINVAL;
+  {   // the selection indexes a head's (Q block, K block) pairs with 32-bit integers
+    const int64_t nqb = (qs.N + QBLK - 1) / QBLK, nkb = (qs.N + KBLK - 1) / KBLK;
+    if (nqb * nkb > INT32_MAX) return SAGE_EINVAL;
+  }
   if (!aligned16(q) || !aligned16(k_smoothed)) return SAGE_EALIGN;
   const size_t need = thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
   if (!workspace || workspace_bytes < need) return SAGE_EWORKSPACE;

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
                                                              int causal, int64_t n_sel, uint8_t* __restrict__ mask) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wave_tot[SEL_THREADS / 64];
-  __shared__ uint32_t sh_digit, sh_remaining;
+  __shared__ uint32_t sh_digit, sh_remaining, sh_eq;
   const int64_t bhq = blockIdx.x;
   const float* sc = scores + bhq * nQB * nKB;
   uint8_t* mk = mask + bhq * nQB * nKB;
@@ -103,11 +103,24 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < npair; i += SEL_THREADS) {
-      const int64_t qb = i / nKB, kb = i % nKB;
-      if (!pair_valid(qb, kb, causal)) continue;
-      const uint32_t key = order_key(sc[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    // eight scores per thread in flight (the scores sit in L2; one load per step would leave
+    // each step waiting for its load)
+    for (int64_t base = 0; base < npair; base += 8 * SEL_THREADS) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t i = base + j * SEL_THREADS + tid;
+        v[j] = i < npair ? sc[i] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t i = base + j * SEL_THREADS + tid;
+        if (i >= npair) continue;
+        const uint32_t qb = (uint32_t)i / (uint32_t)nKB, kb = (uint32_t)i - qb * (uint32_t)nKB;
+        if (!pair_valid(qb, kb, causal)) continue;
+        const uint32_t key = order_key(v[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     if (tid == 0) {
@@ -119,6 +132,7 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
       }
       sh_digit = (uint32_t)d;
       sh_remaining = remaining - above;
+      sh_eq = hist[d];   // after the last pass: how many keys equal the threshold key
     }
     __syncthreads();
     prefix |= sh_digit << shift;
@@ -128,6 +142,25 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
   }
   // prefix = key of the n_sel-th largest; `remaining` keys equal to it are taken, lowest index first.
   const uint32_t T = prefix;
+  if (remaining == sh_eq) {   // every key equal to T is taken: no ordering needed
+    for (int64_t base = 0; base < npair; base += 8 * SEL_THREADS) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t i = base + j * SEL_THREADS + tid;
+        v[j] = i < npair ? sc[i] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t i = base + j * SEL_THREADS + tid;
+        if (i >= npair) continue;
+        const uint32_t qb = (uint32_t)i / (uint32_t)nKB;
+        const bool valid = pair_valid(qb, (uint32_t)i - qb * (uint32_t)nKB, causal);
+        mk[i] = (uint8_t)(valid && order_key(v[j]) >= T);
+      }
+    }
+    return;
+  }
   uint32_t taken_eq = 0;
   const int lane = tid & 63, wv = tid >> 6;
   for (int64_t base = 0; base < npair; base += SEL_THREADS) {
@@ -135,7 +168,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(const float* __rest
     bool valid = false;
     uint32_t key = 0;
     if (i < npair) {
-      valid = pair_valid(i / nKB, i % nKB, causal);
+      const uint32_t qb = (uint32_t)i / (uint32_t)nKB;
+      valid = pair_valid(qb, (uint32_t)i - qb * (uint32_t)nKB, causal);
       key = valid ? order_key(sc[i]) : 0u;
     }
     const bool eq = valid && key == T;

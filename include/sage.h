@@ -181,7 +181,8 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
  * causal-valid pairs (k_block*kb <= q_block*qb + q_block - 1 when causal), the
  * min(n_valid, ceil(frac * n_valid)) highest scores are selected (ties: lower qb*nKB+kb).
  *   q [B,Hq,N,D], k_smoothed [B,Hkv,N,D] in dt (SAGE_BF16);  mask_out [B,Hq,nQB,nKB] u8.
- *   q_block = 128 and k_block = 64 are supported.  0 <= frac <= 1.                        */
+ *   q_block = 128 and k_block = 64 are supported.  0 <= frac <= 1.  A head's pair count
+ *   nQB * nKB must not exceed 2^31 - 1 (N up to about 4.2 million tokens), else SAGE_EINVAL. */
 int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sage_shape qs, sage_shape ks,
                          int q_block, int k_block, double frac, int causal, uint8_t* mask_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream);
