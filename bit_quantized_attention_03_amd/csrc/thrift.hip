@@ -29,11 +29,19 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int rows = (int)((N - t0) < T ? (N - t0) : T);
   const uint16_t* p = x + (bh * N + t0) * D + c8 * 8;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = 0; t < rows; ++t) {
-    v4i raw = *(const v4i*)(p + (int64_t)t * D);
+  auto add_row = [&](v4i raw) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) s[e] = s[e] + bf16_to_f32((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
+  };
+  int t = 0;
+  for (; t + 16 <= rows; t += 16) {   // 16 row loads in flight, then the adds in token order
+    v4i raw[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raw[j] = *(const v4i*)(p + (int64_t)(t + j) * D);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) add_row(raw[j]);
   }
+  for (; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * D));
   v4i o;
 #pragma unroll
   for (int w = 0; w < 4; ++w) o[w] = (int)pack_bf16x2(s[2 * w] / (float)rows, s[2 * w + 1] / (float)rows);
