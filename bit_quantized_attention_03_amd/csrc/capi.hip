@@ -13,7 +13,9 @@ namespace {
 constexpr int QBLK = 128, KBLK = 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-bool shape_ok(const sage_shape& s) { return s.B >= 0 && s.H >= 1 && s.N >= 0 && s.D >= 1 && s.B <= (1 << 20) && s.N <= (1ll << 31); }
+bool shape_ok(const sage_shape& s) {
+  return s.B >= 0 && s.H >= 1 && s.N >= 0 && s.D >= 1 && s.B <= (1 << 20) && s.H <= 65535 && s.B * s.H <= 65535 && s.N <= (1ll << 31);
+}
 bool is16(sage_fmt f) { return f == SAGE_BF16 || f == SAGE_FP16; }
 int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int launched(hipError_t e) { return e == hipSuccess ? SAGE_OK : (e == hipErrorNotSupported ? SAGE_ENOTSUP : SAGE_EHIP); }
@@ -211,7 +213,7 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
                          size_t workspace_bytes, hipStream_t stream) {
   if (!q || !k_smoothed || !mask_out || !shape_ok(qs) || !shape_ok(ks)) return SAGE_EINVAL;
   if (ks.B != qs.B || ks.N != qs.N || ks.D != qs.D || qs.H % ks.H != 0 || qs.D % 8 != 0) return SAGE_EINVAL;
-  if (dt != SAGE_BF16 || q_block != QBLK || k_block != KBLK) return SAGE_ENOTSUP;
+  if (dt != SAGE_BF16 || q_block != QBLK || k_block != KBLK || qs.D > 128) return SAGE_ENOTSUP;
   if (!(frac >= 0.0 && frac <= 1.0) || (causal != 0 && causal != 1)) return SAGE_EINVAL;
   {   // the selection indexes a head's (Q block, K block) pairs with 32-bit integers
     const int64_t nqb = (qs.N + QBLK - 1) / QBLK, nkb = (qs.N + KBLK - 1) / KBLK;

@@ -54,6 +54,9 @@ typedef enum {
   SAGE_SCALE_SEARCH_OFFSETS = 2  /* ScaleSearch over UE4M3 bit offsets f in [-2, 6] */
 } sage_scale_mode;
 
+/* Logical [B, H, N, D] of a tensor.  Every entry point that takes one returns SAGE_EINVAL
+ * unless B >= 0, H >= 1, N >= 0, D >= 1, B <= 2^20, B * H <= 65535 (heads index a launch
+ * dimension) and N <= 2^31.                                                                */
 typedef struct { int64_t B, H, N, D; } sage_shape;
 
 /* Block of a quantizer.  Supported (tokens, channels):
@@ -181,6 +184,7 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
  * causal-valid pairs (k_block*kb <= q_block*qb + q_block - 1 when causal), the
  * min(n_valid, ceil(frac * n_valid)) highest scores are selected (ties: lower qb*nKB+kb).
  *   q [B,Hq,N,D], k_smoothed [B,Hkv,N,D] in dt (SAGE_BF16);  mask_out [B,Hq,nQB,nKB] u8.
+ *   D a multiple of 8 (else SAGE_EINVAL) and at most 128 (else SAGE_ENOTSUP).
  *   q_block = 128 and k_block = 64 are supported.  0 <= frac <= 1.  A head's pair count
  *   nQB * nKB must not exceed 2^31 - 1 (N up to about 4.2 million tokens), else SAGE_EINVAL. */
 int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sage_shape qs, sage_shape ks,

@@ -85,6 +85,13 @@ def test_validation_before_launch(L):
                                   None) == -4
     assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, shp, shp, 128, 64, 1.5, 1, 0x1000_0000,
                                   0x1000_0000, 1 << 30, None) == -1
+    s256 = sage.Shape(1, 1, 128, 256)                                  # head dimension above 128
+    assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, s256, s256, 128, 64, 0.05, 1, 0x1000_0000,
+                                  0x1000_0000, 1 << 30, None) == -2
+    wide = sage.Shape(300, 300, 128, 128)                              # B * H above 65535
+    assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, wide, wide, 128, 64, 0.05, 1, 0x1000_0000,
+                                  0x1000_0000, 1 << 30, None) == -1
+    assert L.thrift_workspace_bytes(wide, wide, 128, 64) == 0
     # microscaled attention: D = 128 only, dword-aligned scales
     m64 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 128, 64))
     p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)

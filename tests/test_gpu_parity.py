@@ -157,6 +157,41 @@ def test_thrift_mask_bit_exact(causal):
         assert np.array_equal(m.cpu().numpy(), m_o), frac
 
 
+def _tiled(x, period):
+    """x's first `period` tokens repeated along the token axis to x's length."""
+    n = x.shape[2]
+    reps = (n + period - 1) // period
+    return x[:, :, :period].repeat(1, 1, reps, 1)[:, :, :n].contiguous()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N,pattern", [(4500, "random"), (4500, "row_ties"), (4500, "grid_ties"),
+                                       (4500, "zero_scores"), (33000, "random"), (33000, "grid_ties")])
+def test_thrift_mask_multi_chunk(causal, N, pattern):
+    """N = 4500: 36 Q blocks (selection chunks of 16 Q blocks: three, the last ragged) x 71 K
+    blocks (the last ragged).  N = 33000: 516 K blocks, so a chunk holds more pairs than the
+    kernels keep in registers and its scores are streamed.  row_ties: K repeats every 64
+    tokens, so a Q block's scores tie over its full K blocks.  grid_ties: Q repeats every 128
+    tokens too, so the ties span every chunk.  zero_scores: constant K, smoothed to zero.
+    frac 1.0 is decided by the first byte."""
+    sage = _sage()
+    w = I.workload("thrift_long", B=1, Hq=2 if N < 10000 else 1, Hkv=1, N=N)
+    q, k, _ = I.make_qkv(w, seed=11)
+    if pattern in ("row_ties", "grid_ties"):
+        k = _tiled(k, 64)
+    if pattern == "grid_ties":
+        q = _tiled(q, 128)
+    if pattern == "zero_scores":
+        k = _tiled(k, 1)
+    print(f"[case] thrift multi-chunk N={N} {pattern} causal={causal}", flush=True)
+    qg, kg = _cuda(q, k)
+    _, ks = sage.smooth_k(kg)
+    for frac in (0.0, 0.05, 0.37, 1.0):
+        m = sage.thrift_select(qg, ks, frac, causal)
+        m_o, _ = oracle.thrift_select(np16(q), np16(ks), 0, 128, 64, frac, causal)
+        assert np.array_equal(m.cpu().numpy(), m_o), frac
+
+
 # ------------------------------------------------------------------------------ attention
 ATT_CASES = [
     ("tiny_int8", {}, False, "int8"),
