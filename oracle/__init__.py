@@ -126,11 +126,21 @@ def smooth_k(k16: np.ndarray, dt: int):
     return mean, ks
 
 
-def quant_int8(x16: np.ndarray, dt: int, block_tokens: int):
+def hadamard_rows(x16: np.ndarray, dt: int) -> np.ndarray:
+    """fp32 rows of x times the normalized Sylvester Hadamard matrix (fast-transform stage
+    order, then one multiply by fp32(1/sqrt(D)))."""
+    x16 = _c(x16, np.uint16); D = x16.shape[-1]
+    out = np.empty(x16.shape, np.float32)
+    _load().orc_hadamard_rows(_p(x16), C.c_int(dt), _i(x16.size // D), _i(D), _p(out))
+    return out
+
+
+def quant_int8(x16: np.ndarray, dt: int, block_tokens: int, hadamard: bool = False):
     x16 = _c(x16, np.uint16); B, H, N, D = x16.shape
     nblk = (N + block_tokens - 1) // block_tokens
     codes = np.empty((B, H, N, D), np.int8); scales = np.empty((B, H, nblk), np.float32)
-    _load().orc_quant_int8(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), _i(block_tokens), _p(codes), _p(scales))
+    _load().orc_quant_int8(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), _i(block_tokens), C.c_int(int(hadamard)),
+                           _p(codes), _p(scales))
     return codes, scales
 
 
@@ -144,17 +154,20 @@ def quant_fp8_channel(v16: np.ndarray, dt: int):
     return codes, scales
 
 
-def quant_mxfp4(x16: np.ndarray, dt: int, axis: int):
+def quant_mxfp4(x16: np.ndarray, dt: int, axis: int, hadamard: bool = False):
     x16 = _c(x16, np.uint16); B, H, N, D = x16.shape
     Np = (N + 63) // 64 * 64
     rows, length = (N, D) if axis == 0 else (D, Np)
     codes = np.empty((B, H, rows, length // 2), np.uint8)
     scales = np.empty((B, H, rows, length // 32) if axis == 0 else (B, H, Np // 32, D), np.uint8)
-    _load().orc_quant_mxfp4(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), _p(codes), _p(scales))
+    if hadamard and axis != 0:
+        raise ValueError("the Hadamard transform runs along D (axis 0)")
+    _load().orc_quant_mxfp4(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), C.c_int(int(hadamard)),
+                            _p(codes), _p(scales))
     return codes, scales
 
 
-def quant_nvfp4(x16: np.ndarray, dt: int, axis: int, mode: int):
+def quant_nvfp4(x16: np.ndarray, dt: int, axis: int, mode: int, hadamard: bool = False):
     """mode 0 = max-scaling, 1 = ScaleSearch on the 0.85..1.15 grid, 2 = the page's bit offsets [-2, 6].
     Returns (codes, ue4m3 scales, index of the winning candidate per block)."""
     x16 = _c(x16, np.uint16); B, H, N, D = x16.shape
@@ -164,8 +177,10 @@ def quant_nvfp4(x16: np.ndarray, dt: int, axis: int, mode: int):
     sshape = (B, H, rows, length // 16) if axis == 0 else (B, H, Np // 16, D)
     scales = np.empty(sshape, np.uint8)
     chosen = np.empty(sshape, np.uint8)
+    if hadamard and axis != 0:
+        raise ValueError("the Hadamard transform runs along D (axis 0)")
     _load().orc_quant_nvfp4(_p(x16), C.c_int(dt), _i(B), _i(H), _i(N), _i(D), C.c_int(axis), C.c_int(mode),
-                            _p(codes), _p(scales), _p(chosen))
+                            C.c_int(int(hadamard)), _p(codes), _p(scales), _p(chosen))
     return codes, scales, chosen
 
 

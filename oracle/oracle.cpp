@@ -240,13 +240,56 @@ void orc_smooth_k(const uint16_t* k, int dt, int64_t B, int64_t H, int64_t N, in
       }
 }
 
+// ----- Hadamard incoherence processing ("Search Your Block Floating Point Scales!", Method ›
+// ScaleSearchAttention: a Hadamard transform of Q and K, after QuIP#, spreads outliers
+// before FP4 quantization).  Reading taken: each row of D channels (D a power of two) is
+// multiplied by the normalized Sylvester Hadamard matrix H_D / sqrt(D), which is orthogonal,
+// so Q'K'^T = QK^T.  Arithmetic, in fp32: the fast transform's stages h = 1, 2, 4, ..., D/2,
+// each replacing every pair (v[j], v[j+h]) with j mod 2h < h by (v[j] + v[j+h],
+// v[j] - v[j+h]), then one multiply by fp32(1 / sqrt(D)).  The result equals H_D v exactly
+// in real arithmetic; the fp32 roundings are those of this stage order.
+void hadamard_row(float* v, int64_t D) {
+  for (int64_t h = 1; h < D; h *= 2)
+    for (int64_t i = 0; i < D; i += 2 * h)
+      for (int64_t j = i; j < i + h; ++j) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+  const float c = (float)(1.0 / std::sqrt((double)D));
+  for (int64_t j = 0; j < D; ++j) v[j] = v[j] * c;
+}
+
+// Decoded values of a [B, H, N, D] tensor of 16-bit patterns, or of their row transforms.
+struct Values {
+  const uint16_t* x16;
+  int dt;
+  std::vector<float> rot;   // non-empty: the Hadamard-transformed rows
+  Values(const uint16_t* x, int dtype, int64_t rows, int64_t D, int hadamard) : x16(x), dt(dtype) {
+    if (!hadamard) return;
+    rot.resize((size_t)(rows * D));
+    for (int64_t r = 0; r < rows; ++r) {
+      for (int64_t c = 0; c < D; ++c) rot[r * D + c] = in_value(x, r * D + c, dt);
+      hadamard_row(&rot[r * D], D);
+    }
+  }
+  float operator[](int64_t i) const { return rot.empty() ? in_value(x16, i, dt) : rot[i]; }
+};
+
+void orc_hadamard_rows(const uint16_t* x, int dt, int64_t rows, int64_t D, float* out) {
+  Values v(x, dt, rows, D, 1);
+  std::memcpy(out, v.rot.data(), sizeof(float) * rows * D);
+}
+
 // ----- INT8 per-block quantization (SageAttention: Q and K in 8 bits) -----
 // A block is `block_tokens` consecutive tokens x all D channels of one (b, h); the last
 // block may be short.  Symmetric absmax rule: s = fp32(amax / 127), r = fp32(1 / s),
 // code = clamp(round_half_even(fp32(x * r)), -127, 127); an all-zero block has s = 0 and
-// codes 0.  Scales are [B, H, ceil(N / block_tokens)] fp32.
-void orc_quant_int8(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, int64_t D,
-                    int64_t block_tokens, int8_t* codes, float* scales) {
+// codes 0.  Scales are [B, H, ceil(N / block_tokens)] fp32.  hadamard: quantize the
+// transformed rows (hadamard_row) instead of x.
+void orc_quant_int8(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N, int64_t D,
+                    int64_t block_tokens, int hadamard, int8_t* codes, float* scales) {
+  const Values x(x16, dt, B * H * N, D, hadamard);
   int64_t nblk = (N + block_tokens - 1) / block_tokens;
   for (int64_t b = 0; b < B; ++b)
     for (int64_t h = 0; h < H; ++h)
@@ -254,14 +297,14 @@ void orc_quant_int8(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, 
         int64_t t0 = blk * block_tokens, t1 = std::min(N, t0 + block_tokens);
         float amax = 0.0f;
         for (int64_t t = t0; t < t1; ++t)
-          for (int64_t c = 0; c < D; ++c) amax = std::max(amax, std::fabs(in_value(x, idx4(b, h, t, c, H, N, D), dt)));
+          for (int64_t c = 0; c < D; ++c) amax = std::max(amax, std::fabs(x[idx4(b, h, t, c, H, N, D)]));
         float s = amax / 127.0f;
         scales[(b * H + h) * nblk + blk] = s;
         float r = s > 0.0f ? 1.0f / s : 0.0f;
         for (int64_t t = t0; t < t1; ++t)
           for (int64_t c = 0; c < D; ++c) {
             int64_t i = idx4(b, h, t, c, H, N, D);
-            float q = std::nearbyint(in_value(x, i, dt) * r);
+            float q = std::nearbyint(x[i] * r);
             codes[i] = (int8_t)std::max(-127.0f, std::min(127.0f, q));
           }
       }
@@ -304,8 +347,9 @@ inline int64_t scale_index(int64_t bh, int64_t r, int64_t g, int64_t rows, int64
 // axis 1: codes [B,H,D,Np/2] with Np = N rounded up to 64 (the padding tokens are zeros),
 //         scales [B,H,Np/32,D] (token block major: the scales of 64 consecutive tokens
 //         are 2*D consecutive bytes).
-void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis,
-                     uint8_t* codes, uint8_t* scales) {
+void orc_quant_mxfp4(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis,
+                     int hadamard, uint8_t* codes, uint8_t* scales) {
+  const Values x(x16, dt, B * H * N, D, hadamard && axis == 0);
   const int64_t G = 32;
   int64_t Np = (N + 63) / 64 * 64;
   int64_t rows = axis == 0 ? N : D;        // rows of the output layout
@@ -318,7 +362,7 @@ void orc_quant_mxfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
           double amax = 0.0;
           for (int64_t j = 0; j < G; ++j) {
             int64_t t = axis == 0 ? r : g0 + j, c = axis == 0 ? g0 + j : r;
-            vals[j] = t < N ? in_value(x, idx4(b, h, t, c, H, N, D), dt) : 0.0f;
+            vals[j] = t < N ? x[idx4(b, h, t, c, H, N, D)] : 0.0f;
             amax = std::max(amax, std::fabs((double)vals[j]));
           }
           int e = mx_exponent(amax, 6.0);
@@ -367,8 +411,10 @@ float nv_block_sse(const float* x, float s, uint8_t* codes_out) {
   return se[0];
 }
 
-void orc_quant_nvfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis, int mode,
-                     uint8_t* codes, uint8_t* scales, uint8_t* chosen /* nullable: index of winning candidate */) {
+void orc_quant_nvfp4(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis, int mode,
+                     int hadamard, uint8_t* codes, uint8_t* scales,
+                     uint8_t* chosen /* nullable: index of winning candidate */) {
+  const Values x(x16, dt, B * H * N, D, hadamard && axis == 0);
   const int64_t G = 16;
   int64_t Np = (N + 63) / 64 * 64;
   int64_t rows = axis == 0 ? N : D;
@@ -383,7 +429,7 @@ void orc_quant_nvfp4(const uint16_t* x, int dt, int64_t B, int64_t H, int64_t N,
           float amax = 0.0f;
           for (int64_t j = 0; j < G; ++j) {
             int64_t t = axis == 0 ? r : g0 + j, c = axis == 0 ? g0 + j : r;
-            vals[j] = t < N ? in_value(x, idx4(b, h, t, c, H, N, D), dt) : 0.0f;
+            vals[j] = t < N ? x[idx4(b, h, t, c, H, N, D)] : 0.0f;
             amax = std::max(amax, std::fabs(vals[j]));
           }
           float smax = amax / 6.0f;
