@@ -99,6 +99,14 @@ int quantize_impl(const void* x, sage_fmt in_dt, sage_shape xs, const float* mea
   size_t cb, sb;
   int st = sage_quantized_bytes(fmt, block, xs, &cb, &sb);
   if (st != SAGE_OK) return st;
+  const bool had = (mode & SAGE_ROTATE_HADAMARD) != 0;
+  mode = (sage_scale_mode)(mode & ~SAGE_ROTATE_HADAMARD);
+  if (had) {   // along D only, D in {64, 128}; INT8 blocks that stay in registers
+    if (xs.D != 64 && xs.D != 128) return SAGE_ENOTSUP;
+    if (fmt == SAGE_E4M3) return SAGE_ENOTSUP;
+    if ((fmt == SAGE_MXFP4 || fmt == SAGE_NVFP4) && block.channels == 1) return SAGE_ENOTSUP;
+    if (fmt == SAGE_INT8 && (int64_t)block.tokens * xs.D > 32768) return SAGE_ENOTSUP;
+  }
   if (mode != SAGE_SCALE_ABSMAX && fmt != SAGE_NVFP4) return SAGE_EINVAL;
   if (mode != SAGE_SCALE_ABSMAX && mode != SAGE_SCALE_SEARCH && mode != SAGE_SCALE_SEARCH_OFFSETS) return SAGE_EINVAL;
   if (!aligned16(x) || !aligned16(codes_out) || !aligned16(scales_out)) return SAGE_EALIGN;
@@ -110,13 +118,13 @@ int quantize_impl(const void* x, sage_fmt in_dt, sage_shape xs, const float* mea
   switch (fmt) {
     case SAGE_INT8:
       return launched(launch_quant_int8(x, f16, BH, xs.N, (int)xs.D, block.tokens, mean, (int8_t*)codes_out,
-                                        (float*)scales_out, stream));
+                                        (float*)scales_out, stream, had));
     case SAGE_E4M3:
       return launched(launch_quant_fp8_channel(x, f16, BH, xs.N, (int)xs.D, (uint8_t*)codes_out, (float*)scales_out,
                                                stream));
     default:
       return launched(launch_quant_fp4(x, f16, BH, xs.N, (int)xs.D, fmt == SAGE_NVFP4, block.channels == 1 ? 1 : 0,
-                                       (int)mode, mean, (uint8_t*)codes_out, (uint8_t*)scales_out, stream));
+                                       (int)mode, mean, (uint8_t*)codes_out, (uint8_t*)scales_out, stream, had));
   }
 }
 }  // namespace

@@ -13,13 +13,15 @@ hipError_t launch_smooth_k(const void* k, bool is_f16, int64_t BH, int64_t N, in
 // Block quantizers.
 // mean (nullable, [BH, D] fp32): quantize round_to_dtype(x - mean) instead of x (K smoothing
 // applied on the fly, bit-identical to quantizing the smoothing kernel's K_s).
+// hadamard: rows along D times the normalized Hadamard matrix first (D in {64, 128}; INT8
+// blocks of at most 4096 16-byte chunks; FP4 along D only), else hipErrorNotSupported.
 hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, const float* mean,
-                             int8_t* codes, float* scales, hipStream_t st);
+                             int8_t* codes, float* scales, hipStream_t st, bool hadamard = false);
 hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int64_t N, int D, uint8_t* codes_t,
                                     float* scales, hipStream_t st);
 hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
                             int mode, const float* mean /* nullable; along D only */, uint8_t* codes, uint8_t* scales,
-                            hipStream_t st);
+                            hipStream_t st, bool hadamard = false);
 // rows x len elements along the block axis; D_tok = 0 along D, else the channel count of a
 // token-axis (V) layout whose scales are token-group major.
 hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len, int D_tok,

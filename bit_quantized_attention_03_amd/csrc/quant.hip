@@ -12,10 +12,14 @@
 //    strictly smaller wins, the max-scaling candidate first).  This one is ALU-bound: about
 //    nine candidates x ten operations per element.
 //  * NVFP4 -> MXFP8 for the FP8 matrix-core path.
+//  * Optional Hadamard incoherence processing of the rows along D ("Search Your Block
+//    Floating Point Scales!", Method > ScaleSearchAttention) inside the along-D quantizers:
+//    each row times the normalized Sylvester Hadamard matrix, so Q'K'^T = QK^T.
 // Compiled with -ffp-contract=off: every expression rounds as written.
 #include "device.hpp"
 #include "kernels.hpp"
 
+#include <cmath>
 #include <type_traits>
 
 namespace sage {
@@ -42,13 +46,43 @@ __device__ __forceinline__ v4i smooth_chunk(v4i raw, const float* __restrict__ m
   return smooth_vals<F16>(raw, *(const v4f*)mu, *(const v4f*)(mu + 4));
 }
 
+// ------------------------------------------------------------------ Hadamard along D
+// The fast Walsh-Hadamard transform of a row of D values in fp32: stages h = 1, 2, ...,
+// D/2, each replacing the pair (v[j], v[j+h]) (j mod 2h < h) by (v[j] + v[j+h],
+// v[j] - v[j+h]); then one multiply by fp32(1/sqrt(D)).  A thread holds n consecutive values
+// of the row and the row's threads sit in consecutive lanes, so the stages h < n run inside
+// the thread and the stage h = n m pairs lane L with lane L ^ m.  Every add and subtract is
+// the same fp32 operation on the same operands as in the plain stage-by-stage transform.
+template <int n>
+__device__ __forceinline__ void fwht_in_thread(float* v) {
+#pragma unroll
+  for (int h = 1; h < n; h *= 2)
+#pragma unroll
+    for (int i = 0; i < n; i += 2 * h)
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+}
+
+// Stage pairing this lane with lane ^ m; `upper`: this lane holds the second element of
+// each pair (its lane bit m is set).
+__device__ __forceinline__ float fwht_across(float mine, int m, bool upper) {
+  const float other = __shfl_xor(mine, m);
+  return upper ? other - mine : mine + other;
+}
+
 // ------------------------------------------------------------------ INT8 per block
 // One workgroup per block of T tokens x D channels; the block (T * D / 8 16-byte chunks)
 // stays in registers between the amax reduction and the encoding, so HBM is read once.
-template <bool F16, int CPT, bool SMOOTH>   // CPT = 16-byte chunks per thread (T * D / 8 / 256)
+// HAD: the rows are Hadamard-transformed first (D in {64, 128}: a row is D/8 chunks, held by
+// D/8 consecutive lanes); the block is then held as fp32.
+template <bool F16, int CPT, bool SMOOTH, bool HAD = false>   // CPT = 16-byte chunks per thread (T * D / 8 / 256)
 __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int T,
                                                          const float* __restrict__ mean, int8_t* __restrict__ codes,
-                                                         float* __restrict__ scales) {
+                                                         float* __restrict__ scales, float hscale = 0.0f) {
   const int64_t nblk = (N + T - 1) / T;
   const int64_t blk = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = blk * T;
@@ -76,15 +110,38 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
       }
     }
   }
+  float hv[HAD ? CPT : 1][8];   // HAD: the transformed block
   float amax = 0.0f;
+  if (HAD) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i)
+    for (int i = 0; i < CPT; ++i) {
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint32_t u = (uint32_t)raw[i][w];
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u & 0xffffu))));
-      amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u >> 16))));
+      for (int e = 0; e < 8; ++e) hv[i][e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[i][e >> 1] >> (16 * (e & 1))));
+      fwht_in_thread<8>(hv[i]);
     }
+    for (int m = 1; m < D / 8; m *= 2)   // chunk k of a row sits in lane (row's first lane) + k
+#pragma unroll
+      for (int i = 0; i < CPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) hv[i][e] = fwht_across(hv[i][e], m, (lane & m) != 0);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hv[i][e] = hv[i][e] * hscale;
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[i][e]));
+      }
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t u = (uint32_t)raw[i][w];
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u & 0xffffu))));
+        amax = __builtin_fmaxf(amax, __builtin_fabsf(in16_to_f32<F16>((uint16_t)(u >> 16))));
+      }
+  }
   __shared__ float red[4];
   amax = wave_max(amax);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
@@ -101,8 +158,8 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      uint16_t h = (uint16_t)((uint32_t)raw[i][e >> 1] >> (16 * (e & 1)));
-      float q = __builtin_rintf(in16_to_f32<F16>(h) * r);
+      const float xv = HAD ? hv[i][e] : in16_to_f32<F16>((uint16_t)((uint32_t)raw[i][e >> 1] >> (16 * (e & 1))));
+      float q = __builtin_rintf(xv * r);
       q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
       packed[e >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (e & 3));
     }
@@ -367,11 +424,14 @@ __device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* c) {
   return (uint32_t)(e + 127);
 }
 
-// Along D: one thread per group (32 values for MX, 16 for NV) of one token row.
-template <bool F16, bool NV, bool SMOOTH>
+// Along D: one thread per group (32 values for MX, 16 for NV) of one token row.  HAD: the
+// row is Hadamard-transformed first; its D / G groups sit in consecutive lanes, and whole
+// rows leave together at the bound check, so every lane a stage pairs with is active.
+template <bool F16, bool NV, bool SMOOTH, bool HAD = false>
 __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t N, int D,
                                                        int mode, const float* __restrict__ mean,
-                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                       float hscale = 0.0f) {
   constexpr int G = NV ? 16 : 32;
   const int gpr = D / G;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -384,6 +444,15 @@ __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restric
     if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + (gid / gpr / N) * D + (gid % gpr) * G + q * 8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[q * 8 + e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
+  }
+  if (HAD) {
+    const int lane = threadIdx.x & 63;
+    fwht_in_thread<G>(v);
+    for (int m = 1; m < gpr; m *= 2)
+#pragma unroll
+      for (int j = 0; j < G; ++j) v[j] = fwht_across(v[j], m, (lane & m) != 0);
+#pragma unroll
+    for (int j = 0; j < G; ++j) v[j] = v[j] * hscale;
   }
   if (NV) {
     uint32_t c[2];
@@ -499,13 +568,35 @@ __global__ void convert_kernel(const float* __restrict__ x, int64_t n, int fmt, 
 
 }  // namespace
 
+float hadamard_scale(int D) { return (float)(1.0 / std::sqrt((double)D)); }
+
 hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, const float* mean,
-                             int8_t* codes, float* scales, hipStream_t st) {
+                             int8_t* codes, float* scales, hipStream_t st, bool hadamard) {
   const int64_t nblk = (N + T - 1) / T;
   if (nblk == 0 || BH == 0) return hipSuccess;
   dim3 g((unsigned)nblk, (unsigned)BH);
   const int64_t chunks = (int64_t)T * D / 8;   // 16-byte chunks of a full block
   const uint16_t* xs = (const uint16_t*)x;
+  if (hadamard) {   // D in {64, 128}, chunks <= 4096 (checked at the boundary)
+    const float hs = hadamard_scale(D);
+    auto goh = [&](auto cpt) {
+      constexpr int C = decltype(cpt)::value;
+      if (mean) {
+        if (is_f16) quant_int8_kernel<true, C, true, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
+        else quant_int8_kernel<false, C, true, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
+      } else {
+        if (is_f16) quant_int8_kernel<true, C, false, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
+        else quant_int8_kernel<false, C, false, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
+      }
+    };
+    if (chunks <= 256) goh(std::integral_constant<int, 1>{});
+    else if (chunks <= 512) goh(std::integral_constant<int, 2>{});
+    else if (chunks <= 1024) goh(std::integral_constant<int, 4>{});
+    else if (chunks <= 2048) goh(std::integral_constant<int, 8>{});
+    else if (chunks <= 4096) goh(std::integral_constant<int, 16>{});
+    else return hipErrorNotSupported;
+    return hipGetLastError();
+  }
   auto go = [&](auto cpt) {
     constexpr int C = decltype(cpt)::value;
     if (mean) {
@@ -551,15 +642,19 @@ hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int6
 }
 
 hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
-                            int mode, const float* mean, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                            int mode, const float* mean, uint8_t* codes, uint8_t* scales, hipStream_t st,
+                            bool hadamard) {
   const uint16_t* xs = (const uint16_t*)x;
+  if (hadamard && along_tokens) return hipErrorNotSupported;
   if (!along_tokens) {
     const int64_t groups = BH * N * (D / (nv ? 16 : 32));
     if (groups == 0) return hipSuccess;
     const unsigned g = (unsigned)((groups + 255) / 256);
+    const float hs = hadamard ? hadamard_scale(D) : 0.0f;
     auto go = [&](auto f16c, auto nvc, auto smc) {
-      fp4_rows_kernel<decltype(f16c)::value, decltype(nvc)::value, decltype(smc)::value>
-          <<<g, 256, 0, st>>>(xs, BH * N, N, D, mode, mean, codes, scales);
+      constexpr bool F16 = decltype(f16c)::value, NV = decltype(nvc)::value, SM = decltype(smc)::value;
+      if (hadamard) fp4_rows_kernel<F16, NV, SM, true><<<g, 256, 0, st>>>(xs, BH * N, N, D, mode, mean, codes, scales, hs);
+      else fp4_rows_kernel<F16, NV, SM, false><<<g, 256, 0, st>>>(xs, BH * N, N, D, mode, mean, codes, scales);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libsage.so")
 
 BF16, FP16, FP32, INT8, E4M3, MXFP4, NVFP4, MXFP8 = range(8)
 ABSMAX, SEARCH, SEARCH_OFFSETS = 0, 1, 2
+ROTATE_HADAMARD = 0x100   # flag OR'ed into a scale mode: rows along D Hadamard-transformed first
 _TORCH_FMT = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
 
 
@@ -138,9 +139,11 @@ class QT:
         return QTensorC(self.fmt, _ptr(self.codes), _ptr(self.scales), Shape(*self.shape))
 
 
-def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
-    """Block quantization (layouts as in sage.h); returns a QT with flat code/scale buffers."""
+def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX, hadamard: bool = False) -> QT:
+    """Block quantization (layouts as in sage.h); returns a QT with flat code/scale buffers.
+    hadamard: quantize the rows along D times the normalized Hadamard matrix (Q and K only)."""
     _dev(x)
+    mode = mode | (ROTATE_HADAMARD if hadamard else 0)
     cb, sb = quantized_bytes(fmt, block, tuple(x.shape))
     codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)
     scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)
@@ -149,9 +152,11 @@ def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
     return QT(fmt, codes[:cb], scales[:sb], tuple(x.shape))
 
 
-def quantize_smoothed(k: torch.Tensor, mean: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX) -> QT:
+def quantize_smoothed(k: torch.Tensor, mean: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX,
+                      hadamard: bool = False) -> QT:
     """Quantize K_s = round(k - mean) without storing it (same codes as quantize(K_s, ...))."""
     _dev(k)
+    mode = mode | (ROTATE_HADAMARD if hadamard else 0)
     cb, sb = quantized_bytes(fmt, block, tuple(k.shape))
     codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=k.device)
     scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=k.device)
@@ -228,20 +233,23 @@ class Pass:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str = "int8",
             sm_scale: float = 0.0, thrift_frac: float = 0.05, search_mode: int = SEARCH,
-            out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False) -> Pass:
+            out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False, hadamard: bool = False) -> Pass:
     """K smoothing -> block quantization -> (Thrift selection) -> fused attention.  K_s is only
     materialized when Thrift needs it (or keep_smoothed); otherwise K is quantized with the
-    smoothing applied on the fly (identical codes)."""
+    smoothing applied on the fly (identical codes).  hadamard: Q and K_s are quantized after
+    the orthogonal Hadamard transform of their rows (QK^T unchanged; V and Thrift's bf16
+    tiles take the original rows)."""
     B, Hq, N, D = q.shape
     need_ks = variant == "thrift" or keep_smoothed
     mean, ks = smooth_k(k, want_smoothed=need_ks)
 
     def quant_k(fmt, block, mode=ABSMAX):
-        return quantize(ks, fmt, block, mode) if ks is not None else quantize_smoothed(k, mean, fmt, block, mode)
+        return (quantize(ks, fmt, block, mode, hadamard) if ks is not None
+                else quantize_smoothed(k, mean, fmt, block, mode, hadamard))
 
     mask = None
     if variant in ("int8", "int8_fp8pv", "thrift"):
-        qq = quantize(q, INT8, (128, D))
+        qq = quantize(q, INT8, (128, D), hadamard=hadamard)
         kq = quant_k(INT8, (64, D))
         if variant == "int8_fp8pv":
             vq = quantize(v, E4M3, (0, 1))
@@ -255,12 +263,12 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
             else:
                 out = attn_fwd(qq, kq, vq, causal, BF16, sm_scale, out_dtype=out_dtype)
     elif variant == "mxfp4":
-        qq = quantize(q, MXFP4, (1, 32))
+        qq = quantize(q, MXFP4, (1, 32), hadamard=hadamard)
         kq = quant_k(MXFP4, (1, 32))
         vq = quantize(v, MXFP4, (32, 1))
         out = attn_fwd(qq, kq, vq, causal, MXFP4, sm_scale, out_dtype=out_dtype)
     elif variant == "nvfp4_search":
-        qq = nvfp4_to_mxfp8(quantize(q, NVFP4, (1, 16), search_mode), False)
+        qq = nvfp4_to_mxfp8(quantize(q, NVFP4, (1, 16), search_mode, hadamard), False)
         kq = nvfp4_to_mxfp8(quant_k(NVFP4, (1, 16), search_mode), False)
         vq = nvfp4_to_mxfp8(quantize(v, NVFP4, (16, 1), search_mode), True)
         out = attn_fwd(qq, kq, vq, causal, NVFP4, sm_scale, out_dtype=out_dtype)

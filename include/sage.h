@@ -51,7 +51,8 @@ typedef enum {
 typedef enum {
   SAGE_SCALE_ABSMAX = 0,         /* max-scaling: the block maximum fits the format's range */
   SAGE_SCALE_SEARCH = 1,         /* ScaleSearch over max-scale x {0.85 .. 1.15} (8 steps) */
-  SAGE_SCALE_SEARCH_OFFSETS = 2  /* ScaleSearch over UE4M3 bit offsets f in [-2, 6] */
+  SAGE_SCALE_SEARCH_OFFSETS = 2, /* ScaleSearch over UE4M3 bit offsets f in [-2, 6] */
+  SAGE_ROTATE_HADAMARD = 0x100   /* flag, OR'ed into a mode: Hadamard rows first (see below) */
 } sage_scale_mode;
 
 /* Logical [B, H, N, D] of a tensor.  Every entry point that takes one returns SAGE_EINVAL
@@ -128,7 +129,16 @@ size_t sage_smooth_k_workspace_bytes(sage_shape ks);
  *          fp32 as the balanced index-order pairwise tree; the first strictly smaller sum
  *          wins (c0 first).  Layout as MXFP4 with one scale byte per 16 elements
  *          (along tokens: scales [B,H,Np/16,D]).
- * Scale mode must be SAGE_SCALE_ABSMAX except for SAGE_NVFP4.                            */
+ * Scale mode must be SAGE_SCALE_ABSMAX except for SAGE_NVFP4.
+ * SAGE_ROTATE_HADAMARD ("Search Your Block Floating Point Scales!", Method >
+ * ScaleSearchAttention: incoherence processing of Q and K): each row of D channels is
+ * first replaced by fp32(fwht(x) * fp32(1/sqrt(D))), where fwht runs the fast
+ * Walsh-Hadamard stages h = 1, 2, .., D/2 in fp32, each turning (v[j], v[j+h]) with
+ * j mod 2h < h into (v[j] + v[j+h], v[j] - v[j+h]) (the Sylvester-ordered Hadamard matrix);
+ * the block rules above then apply to those values.  The matrix is orthogonal, so quantizing
+ * both Q and K this way leaves QK^T unchanged up to quantization, and sage_attn_fwd needs no
+ * change.  Along D only (INT8 blocks of T * D <= 32768 elements, SAGE_MXFP4 / SAGE_NVFP4
+ * along D) with D in {64, 128}; otherwise SAGE_ENOTSUP.                                    */
 int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
                          sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream);
 /* Block quantization of smoothed K without storing it — SageAttention (Technical approach:

@@ -40,8 +40,9 @@ def check_out(gpu: np.ndarray, orc: np.ndarray, what: str = ""):
 
 
 def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str,
-                bh=None, qb=None, frac: float = 0.05, search_mode: int = 1, threads=None):
-    """The whole quantize-and-attend pass on the oracle, from the same 16-bit inputs."""
+                bh=None, qb=None, frac: float = 0.05, search_mode: int = 1, threads=None, hadamard: bool = False):
+    """The whole quantize-and-attend pass on the oracle, from the same 16-bit inputs.
+    hadamard: Q and K_s are quantized after the Hadamard transform of their rows."""
     dt = I.dtype_code(q.dtype)
     qb16, kb16, vb16 = np16(q), np16(k), np16(v)
     B, Hq, N, D = q.shape
@@ -49,8 +50,8 @@ def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
     mean, ks = oracle.smooth_k(kb16, dt)
     res = {"mean": mean, "ks": ks}
     if variant in ("int8", "int8_fp8pv", "thrift"):
-        qc, qs = oracle.quant_int8(qb16, dt, 128)
-        kc, kss = oracle.quant_int8(ks, dt, 64)
+        qc, qs = oracle.quant_int8(qb16, dt, 128, hadamard)
+        kc, kss = oracle.quant_int8(ks, dt, 64, hadamard)
         res.update(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=kss)
         if variant == "int8_fp8pv":
             vc, vs = oracle.quant_fp8_channel(vb16, dt)
@@ -66,15 +67,15 @@ def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
                                       k_i8=kc, k_s=kss, v_hi=vb16, v_dt=dt, q_hi=qb16, k_hi=ks, hi_dt=dt,
                                       thrift_mask=mask)
     elif variant == "mxfp4":
-        qc, qe = oracle.quant_mxfp4(qb16, dt, 0)
-        kc, ke = oracle.quant_mxfp4(ks, dt, 0)
+        qc, qe = oracle.quant_mxfp4(qb16, dt, 0, hadamard)
+        kc, ke = oracle.quant_mxfp4(ks, dt, 0, hadamard)
         vc, ve = oracle.quant_mxfp4(vb16, dt, 1)
         res.update(q_codes=qc, q_scales=qe, k_codes=kc, k_scales=ke, v_codes=vc, v_scales=ve)
         ops = oracle.AttnOperands(qk_fmt=oracle.QK_MXFP4, p_fmt=oracle.P_MXFP4, v_fmt=oracle.V_MXFP4, q_lp=qc,
                                   q_e8=qe, k_lp=kc, k_e8=ke, v_lp=vc, v_e8=ve)
     elif variant == "nvfp4_search":
-        qc, qsc, _ = oracle.quant_nvfp4(qb16, dt, 0, search_mode)
-        kc, ksc, _ = oracle.quant_nvfp4(ks, dt, 0, search_mode)
+        qc, qsc, _ = oracle.quant_nvfp4(qb16, dt, 0, search_mode, hadamard)
+        kc, ksc, _ = oracle.quant_nvfp4(ks, dt, 0, search_mode, hadamard)
         vc, vsc, _ = oracle.quant_nvfp4(vb16, dt, 1, search_mode)
         res.update(q_nv=(qc, qsc), k_nv=(kc, ksc), v_nv=(vc, vsc))
         q8, qe = oracle.nvfp4_to_mxfp8(qc, qsc, N, D, 0)

@@ -117,6 +117,19 @@ def test_validation_before_launch(L):
                                     0x1000_0000, 0x1000_0000, None) == -2
     assert L.sage_quantize_smoothed(0x1000_0000, sage.BF16, shp, 0x1000_0004, sage.INT8, blk, 0, 0x1000_0000,
                                     0x1000_0000, None) == -3
+    # Hadamard rows: along D only, D in {64, 128}, INT8 blocks of at most 32768 elements
+    H = 0x100
+    s96 = sage.Shape(1, 1, 128, 96)
+    assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, s96, sage.INT8, sage.Block(128, 96), H, 0x2000_0000,
+                                  0x3000_0000, None) == -2
+    assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.E4M3, sage.Block(0, 1), H, 0x2000_0000,
+                                  0x3000_0000, None) == -2
+    assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.NVFP4, sage.Block(16, 1), H, 0x2000_0000,
+                                  0x3000_0000, None) == -2
+    assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.INT8, sage.Block(512, 128), H, 0x2000_0000,
+                                  0x3000_0000, None) == -2
+    assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.MXFP4, sage.Block(1, 32), H | 1, 0x2000_0000,
+                                  0x3000_0000, None) == -1                 # search modes are NVFP4's
     # smoothing workspace
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
 

@@ -192,6 +192,80 @@ def test_thrift_mask_multi_chunk(causal, N, pattern):
         assert np.array_equal(m.cpu().numpy(), m_o), frac
 
 
+# ------------------------------------------------------------------------------ Hadamard
+HAD_QUANT = [   # (format, block, mode, D, dtype, smoothed)
+    ("INT8", 128, 0, 128, torch.bfloat16, False),
+    ("INT8", 64, 0, 128, torch.bfloat16, True),
+    ("INT8", 256, 0, 128, torch.float16, False),    # 4096 chunks: the largest register-held block
+    ("INT8", 128, 0, 64, torch.bfloat16, False),
+    ("INT8", 64, 0, 64, torch.float16, True),
+    ("MXFP4", 32, 0, 128, torch.bfloat16, False),
+    ("MXFP4", 32, 0, 128, torch.bfloat16, True),
+    ("MXFP4", 32, 0, 64, torch.float16, False),
+    ("NVFP4", 16, 0, 128, torch.bfloat16, False),
+    ("NVFP4", 16, 1, 128, torch.bfloat16, True),
+    ("NVFP4", 16, 2, 128, torch.bfloat16, False),
+    ("NVFP4", 16, 2, 64, torch.float16, True),
+]
+
+
+@pytest.mark.parametrize("fmt,blk,mode,D,dtype,smoothed", HAD_QUANT)
+def test_hadamard_quantizers_bit_exact(fmt, blk, mode, D, dtype, smoothed):
+    """Rows along D Hadamard-transformed inside the quantizer: codes and scales equal the
+    oracle's bit for bit (N = 333: ragged blocks; fp16 and bf16; K smoothing fused)."""
+    sage = _sage()
+    w = I.workload("fp4_search", B=1, Hq=2, Hkv=2, N=333, D=D, dtype=dtype)
+    q, k, _ = I.make_qkv(w, seed=21)
+    dt = I.dtype_code(dtype)
+    print(f"[case] hadamard {fmt} block {blk} mode {mode} D={D} {dtype} smoothed={smoothed}", flush=True)
+    f = getattr(sage, fmt)
+    block = (blk, D) if fmt == "INT8" else (1, blk)
+    if smoothed:
+        kg = k.cuda()
+        mean, _ = sage.smooth_k(kg, want_smoothed=False)
+        qt = sage.quantize_smoothed(kg, mean, f, block, mode, hadamard=True)
+        _, xo = oracle.smooth_k(np16(k), dt)
+    else:
+        qt = sage.quantize(q.cuda(), f, block, mode, hadamard=True)
+        xo = np16(q)
+    if fmt == "INT8":
+        c_o, s_o = oracle.quant_int8(xo, dt, blk, hadamard=True)
+        assert np.array_equal(qt.codes.cpu().numpy().view(np.int8).reshape(c_o.shape), c_o)
+        assert np.array_equal(qt.scales.cpu().view(torch.float32).numpy().reshape(s_o.shape).view(np.uint32),
+                              s_o.view(np.uint32))
+        return
+    if fmt == "MXFP4":
+        c_o, s_o = oracle.quant_mxfp4(xo, dt, 0, hadamard=True)
+    else:
+        c_o, s_o, _ = oracle.quant_nvfp4(xo, dt, 0, mode, hadamard=True)
+    assert np.array_equal(u8(qt.scales).reshape(s_o.shape), s_o)
+    assert np.array_equal(u8(qt.codes).reshape(c_o.shape), c_o)
+
+
+HAD_ATT = [
+    ("llm_int8", dict(B=1, Hq=2, Hkv=2, N=333), False, "int8"),
+    ("llm_int8", dict(B=1, Hq=2, Hkv=2, N=512), True, "int8"),
+    ("thrift_long", dict(B=1, Hq=4, Hkv=2, N=700), True, "thrift"),
+    ("video_fp8", dict(B=1, Hq=2, Hkv=2, N=300), False, "int8_fp8pv"),
+    ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=333), False, "mxfp4"),
+    ("fp4_search", dict(B=1, Hq=4, Hkv=2, N=512), True, "nvfp4_search"),
+]
+
+
+@pytest.mark.parametrize("name,ov,causal,variant", HAD_ATT)
+def test_hadamard_attention_parity(name, ov, causal, variant):
+    sage = _sage()
+    w = I.workload(name, **ov)
+    q, k, v = I.make_qkv(w, seed=0)
+    print(f"[case] hadamard {name} {ov} causal={causal} variant={variant}", flush=True)
+    res = sage.forward(*_cuda(q, k, v), causal=causal, variant=variant, hadamard=True)
+    torch.cuda.synchronize()
+    orc = oracle_pass(q, k, v, causal, variant, hadamard=True)
+    rel, cos = check_out(res.out.cpu().numpy(), orc["out"], f"hadamard {name} {variant} causal={causal}")
+    ref = fp64_reference(q, k, v, causal)
+    print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
+
+
 # ------------------------------------------------------------------------------ attention
 ATT_CASES = [
     ("tiny_int8", {}, False, "int8"),
