@@ -68,7 +68,7 @@ def load_traffic(workload: str, causal: bool, variant: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float):
+def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float, hadamard: bool = False):
     """The oracle as it stands, on whole (b, h) heads of the same workload (CPU tensors q, k,
     v), until ~budget_s."""
     import oracle
@@ -87,7 +87,7 @@ def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float):
         hk = h // g
         qs, ks_, vs = (q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, hk:hk + 1].contiguous(),
                        v[b:b + 1, hk:hk + 1].contiguous())
-        oracle_pass(qs, ks_, vs, causal, variant, threads=threads)
+        oracle_pass(qs, ks_, vs, causal, variant, threads=threads, hadamard=hadamard)
         ops += 4.0 * w.N * w.N * w.D / (2.0 if causal else 1.0)
         done.append(f"({b},{h})")
         if time.perf_counter() - t0 > budget_s:
@@ -152,6 +152,8 @@ def main():
     ap.add_argument("--causal", action="store_true", help="causal mask (the thrift workload is always causal)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--hadamard", action="store_true",
+                    help="Hadamard incoherence processing of Q and K_s inside their quantizers")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the known-size conversion kernel (for counter calibration)")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
@@ -192,12 +194,15 @@ def main():
         # smoothing applied on the fly (same codes, no K_s round trip through HBM)
         mean, ks = sage.smooth_k(k, want_smoothed=variant == "thrift")
 
+        had = args.hadamard
+
         def quant_k(fmt, block, mode=sage.ABSMAX):
-            return sage.quantize(ks, fmt, block, mode) if ks is not None else sage.quantize_smoothed(k, mean, fmt, block, mode)
+            return (sage.quantize(ks, fmt, block, mode, had) if ks is not None
+                    else sage.quantize_smoothed(k, mean, fmt, block, mode, had))
 
         mask = None
         if variant in ("int8", "thrift", "int8_fp8pv"):
-            qq = sage.quantize(q, sage.INT8, (128, D))
+            qq = sage.quantize(q, sage.INT8, (128, D), hadamard=had)
             kq = quant_k(sage.INT8, (64, D))
             if variant == "int8_fp8pv":
                 vq, pf = sage.quantize(v, sage.E4M3, (0, 1)), sage.E4M3
@@ -206,10 +211,10 @@ def main():
                 if variant == "thrift":
                     mask = sage.thrift_select(q, ks, 0.05, causal)
         elif variant == "mxfp4":
-            qq, kq = sage.quantize(q, sage.MXFP4, (1, 32)), quant_k(sage.MXFP4, (1, 32))
+            qq, kq = sage.quantize(q, sage.MXFP4, (1, 32), hadamard=had), quant_k(sage.MXFP4, (1, 32))
             vq, pf = sage.quantize(v, sage.MXFP4, (32, 1)), sage.MXFP4
         else:
-            qq = sage.nvfp4_to_mxfp8(sage.quantize(q, sage.NVFP4, (1, 16), sage.SEARCH), False)
+            qq = sage.nvfp4_to_mxfp8(sage.quantize(q, sage.NVFP4, (1, 16), sage.SEARCH, had), False)
             kq = sage.nvfp4_to_mxfp8(quant_k(sage.NVFP4, (1, 16), sage.SEARCH), False)
             vq = sage.nvfp4_to_mxfp8(sage.quantize(v, sage.NVFP4, (16, 1), sage.SEARCH), True)
             pf = sage.NVFP4
@@ -255,14 +260,15 @@ def main():
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": w.Hkv, "N": N, "D": D, "causal": causal,
                    "variant": variant, "input_dtype": str(w.dtype).replace("torch.", ""),
                    "step": ("smooth_k + quantize + thrift_select + attn_fwd" if variant == "thrift" else
-                            "smooth_k (mean) + quantize (Q, V; K with the smoothing fused) + attn_fwd")},
+                            "smooth_k (mean) + quantize (Q, V; K with the smoothing fused) + attn_fwd")
+                   + (" (Q, K_s Hadamard-transformed in their quantizers)" if args.hadamard else "")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_fwd", "kernel_ms": round(attn_ms, 4),
                      "qk_pv_peak": round(mixed, 1), "qk_pv_frac": round(achieved / mixed, 4)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, variant, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, variant, args.cpu_seconds, args.hadamard)
     print(json.dumps(rec))
 
 

@@ -67,11 +67,45 @@ __device__ __forceinline__ void fwht_in_thread(float* v) {
       }
 }
 
-// Stage pairing this lane with lane ^ m; `upper`: this lane holds the second element of
-// each pair (its lane bit m is set).
-__device__ __forceinline__ float fwht_across(float mine, int m, bool upper) {
-  const float other = __shfl_xor(mine, m);
-  return upper ? other - mine : mine + other;
+// The value of lane ^ m (m in {1, 2, 4, 8}; the lanes of a row of 16 exchange) through DPP:
+// xor 1 and xor 2 are quad permutations, xor 8 rotates the row by 8, xor 4 is the half-row
+// mirror (i -> 7 - i within 8) followed by the reversed quad (i -> 3 - i within 4).
+template <int m>
+__device__ __forceinline__ float lane_xor(float v) {
+  int x = __builtin_bit_cast(int, v);
+  if constexpr (m == 1) x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  else if constexpr (m == 2) x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  else if constexpr (m == 8) x = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);  // row_ror:8
+  else {
+    static_assert(m == 4, "lanes of one row of 16");
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);   // row_half_mirror
+    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);    // quad_perm [3,2,1,0]
+  }
+  return __builtin_bit_cast(float, x);
+}
+
+// The stages h = n m, m = 1, 2, .., LPR/2, for `cnt` values per lane, where a row's values
+// sit n per lane in LPR consecutive lanes.  The lower lane of a pair forms mine + other, the
+// upper one other - mine, written other + (-mine): the same IEEE result.  VIA_LDS: the
+// partner's value comes through the LDS crossbar (ds_bpermute) instead of DPP, which keeps
+// the exchange off the vector ALU (for kernels bound by it).
+template <int LPR, bool VIA_LDS = false>
+__device__ __forceinline__ void fwht_across_lanes(float* v, int cnt) {
+  const int lane = threadIdx.x & 63;
+  auto stage = [&](auto mc) __attribute__((always_inline)) {
+    constexpr int m = decltype(mc)::value;
+    const uint32_t sign = (lane & m) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int j = 0; j < cnt; ++j) {
+      const float other = VIA_LDS ? __shfl_xor(v[j], m) : lane_xor<m>(v[j]);
+      v[j] = other + __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, v[j]) ^ sign);
+    }
+  };
+  if constexpr (LPR > 1) stage(std::integral_constant<int, 1>{});
+  if constexpr (LPR > 2) stage(std::integral_constant<int, 2>{});
+  if constexpr (LPR > 4) stage(std::integral_constant<int, 4>{});
+  if constexpr (LPR > 8) stage(std::integral_constant<int, 8>{});
+  static_assert(LPR <= 16, "a row spans at most 16 lanes");
 }
 
 // ------------------------------------------------------------------ INT8 per block
@@ -113,18 +147,15 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   float hv[HAD ? CPT : 1][8];   // HAD: the transformed block
   float amax = 0.0f;
   if (HAD) {
-    const int lane = threadIdx.x & 63;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) hv[i][e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[i][e >> 1] >> (16 * (e & 1))));
       fwht_in_thread<8>(hv[i]);
     }
-    for (int m = 1; m < D / 8; m *= 2)   // chunk k of a row sits in lane (row's first lane) + k
-#pragma unroll
-      for (int i = 0; i < CPT; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hv[i][e] = fwht_across(hv[i][e], m, (lane & m) != 0);
+    // chunk k of a row sits in lane (row's first lane) + k: D / 8 lanes per row
+    if (D == 128) fwht_across_lanes<16>(&hv[0][0], CPT * 8);
+    else fwht_across_lanes<8>(&hv[0][0], CPT * 8);
 #pragma unroll
     for (int i = 0; i < CPT; ++i)
 #pragma unroll
@@ -445,12 +476,11 @@ __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restric
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[q * 8 + e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
   }
-  if (HAD) {
-    const int lane = threadIdx.x & 63;
+  if (HAD) {   // D in {64, 128}: gpr = D / G lanes per row; NVFP4's search is VALU-bound
     fwht_in_thread<G>(v);
-    for (int m = 1; m < gpr; m *= 2)
-#pragma unroll
-      for (int j = 0; j < G; ++j) v[j] = fwht_across(v[j], m, (lane & m) != 0);
+    if (gpr == 8) fwht_across_lanes<8, NV>(v, G);
+    else if (gpr == 4) fwht_across_lanes<4, NV>(v, G);
+    else fwht_across_lanes<2, NV>(v, G);
 #pragma unroll
     for (int j = 0; j < G; ++j) v[j] = v[j] * hscale;
   }
