@@ -30,13 +30,15 @@ HBM_GBS = 8000.0
 
 DEFAULT_VARIANT = {"tiny_int8": "int8", "llm_int8": "int8", "video_fp8": "int8_fp8pv", "fp4_search": "mxfp4",
                    "thrift_long": "thrift"}
-VARIANT_PEAK = {"int8": "int8", "thrift": "int8", "int8_fp8pv": "int8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
-PV_PEAK = {"int8": "bf16", "thrift": "bf16", "int8_fp8pv": "fp8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
-VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "int8_fp8pv": "int8+fp8", "mxfp4": "mxfp4",
+VARIANT_PEAK = {"int8": "int8", "thrift": "int8", "sink": "int8", "int8_fp8pv": "int8", "mxfp4": "fp4",
+                "nvfp4_search": "fp8"}
+PV_PEAK = {"int8": "bf16", "thrift": "bf16", "sink": "bf16", "int8_fp8pv": "fp8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
+VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "sink": "int8+bf16", "int8_fp8pv": "int8+fp8", "mxfp4": "mxfp4",
                  "nvfp4_search": "nvfp4->mxfp8"}
 
 
 KERNEL_SOURCES = {"int8": ("attn_i8.hip", "attn_common.hpp"), "thrift": ("attn_i8.hip", "attn_common.hpp"),
+                  "sink": ("attn_i8.hip", "attn_common.hpp"),
                   "int8_fp8pv": ("attn_i8.hip", "attn_common.hpp"),
                   "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp")}
 
@@ -192,7 +194,7 @@ def main():
     def step(record: bool):
         # K_s is stored only where Thrift's bf16 tiles read it; otherwise K is quantized with the
         # smoothing applied on the fly (same codes, no K_s round trip through HBM)
-        mean, ks = sage.smooth_k(k, want_smoothed=variant == "thrift")
+        mean, ks = sage.smooth_k(k, want_smoothed=variant in ("thrift", "sink"))
 
         had = args.hadamard
 
@@ -201,7 +203,7 @@ def main():
                     else sage.quantize_smoothed(k, mean, fmt, block, mode, had))
 
         mask = None
-        if variant in ("int8", "thrift", "int8_fp8pv"):
+        if variant in ("int8", "thrift", "sink", "int8_fp8pv"):
             qq = sage.quantize(q, sage.INT8, (128, D), hadamard=had)
             kq = quant_k(sage.INT8, (64, D))
             if variant == "int8_fp8pv":
@@ -210,6 +212,8 @@ def main():
                 vq, pf = sage.QT(sage.BF16 if v.dtype == torch.bfloat16 else sage.FP16, v, None, tuple(v.shape)), sage.BF16
                 if variant == "thrift":
                     mask = sage.thrift_select(q, ks, 0.05, causal)
+                elif variant == "sink":
+                    mask = sage.sink_select(q, 1, 1, causal)
         elif variant == "mxfp4":
             qq, kq = sage.quantize(q, sage.MXFP4, (1, 32), hadamard=had), quant_k(sage.MXFP4, (1, 32))
             vq, pf = sage.quantize(v, sage.MXFP4, (32, 1)), sage.MXFP4
@@ -260,6 +264,8 @@ def main():
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": w.Hkv, "N": N, "D": D, "causal": causal,
                    "variant": variant, "input_dtype": str(w.dtype).replace("torch.", ""),
                    "step": ("smooth_k + quantize + thrift_select + attn_fwd" if variant == "thrift" else
+                            "smooth_k + quantize + sink_select (first and last valid K block in bf16) + attn_fwd"
+                            if variant == "sink" else
                             "smooth_k (mean) + quantize (Q, V; K with the smoothing fused) + attn_fwd")
                    + (" (Q, K_s Hadamard-transformed in their quantizers)" if args.hadamard else "")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",

@@ -236,6 +236,14 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
                                        (int)qs.D, frac, causal, mask_out, workspace, stream));
 }
 
+int sage_sink_blocks(sage_shape qs, int q_block, int k_block, int n_first, int n_last, int causal, uint8_t* mask_out,
+                     hipStream_t stream) {
+  if (!mask_out || !shape_ok(qs)) return SAGE_EINVAL;
+  if (q_block != QBLK || k_block != KBLK) return SAGE_ENOTSUP;
+  if (n_first < 0 || n_last < 0 || (causal != 0 && causal != 1)) return SAGE_EINVAL;
+  return launched(launch_sink_mask(qs.B * qs.H, qs.N, n_first, n_last, causal, mask_out, stream));
+}
+
 int sage_convert_f32(const float* x, int64_t n, sage_fmt fmt, void* out, hipStream_t stream) {
   if (!x || !out || n < 0) return SAGE_EINVAL;
   if (fmt != SAGE_BF16 && fmt != SAGE_FP16 && fmt != SAGE_E4M3 && fmt != SAGE_MXFP4 && fmt != SAGE_NVFP4)

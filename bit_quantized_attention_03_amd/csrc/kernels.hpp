@@ -32,6 +32,8 @@ hipError_t launch_convert_f32(const float* x, int64_t n, int fmt, void* out, hip
 hipError_t launch_thrift_select(const uint16_t* q, const uint16_t* ks, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                 int D, double frac, int causal, uint8_t* mask, void* ws, hipStream_t st);
 size_t thrift_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int D);
+// Static sink-and-recent block mask [BH, nQB, nKB] (blocks of 128 Q rows and 64 keys).
+hipError_t launch_sink_mask(int64_t BH, int64_t N, int n_first, int n_last, int causal, uint8_t* mask, hipStream_t st);
 
 // Attention kernels.
 struct AttnArgs {

@@ -355,7 +355,31 @@ __global__ __launch_bounds__(256) void mask_kernel(const float* __restrict__ sco
   }
 }
 
+// Sink-aware static selection ("Search Your Block Floating Point Scales!", Method >
+// ScaleSearchAttention: the first and the last blocks of the KV cache stay at full
+// precision).  For Q block qb, with kl its last causal-valid K block (nKB - 1 when not
+// causal), K blocks kb <= kl with kb < n_first or kb > kl - n_last are marked.
+__global__ __launch_bounds__(256) void sink_mask_kernel(int64_t total, int64_t nQB, int64_t nKB, int n_first,
+                                                        int n_last, int causal, uint8_t* __restrict__ mask) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t kb = i % nKB, qb = (i / nKB) % nQB;
+  int64_t kl = nKB - 1;
+  if (causal) {
+    const int64_t lim = (QBLK * qb + QBLK - 1) / KBLK;
+    kl = lim < kl ? lim : kl;
+  }
+  mask[i] = (uint8_t)(kb <= kl && (kb < n_first || kb > kl - n_last));
+}
+
 }  // namespace
+
+hipError_t launch_sink_mask(int64_t BH, int64_t N, int n_first, int n_last, int causal, uint8_t* mask, hipStream_t st) {
+  const int64_t nQB = (N + QBLK - 1) / QBLK, nKB = (N + KBLK - 1) / KBLK, total = BH * nQB * nKB;
+  if (total == 0) return hipSuccess;
+  sink_mask_kernel<<<(unsigned)((total + 255) / 256), 256, 0, st>>>(total, nQB, nKB, n_first, n_last, causal, mask);
+  return hipGetLastError();
+}
 
 size_t thrift_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int D) {
   const int64_t nQB = (N + QBLK - 1) / QBLK, nKB = (N + KBLK - 1) / KBLK;

@@ -69,6 +69,7 @@ def lib():
         L.thrift_workspace_bytes.restype = C.c_size_t
         L.thrift_workspace_bytes.argtypes = [Shape, Shape, C.c_int, C.c_int]
         L.sage_convert_f32.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
+        L.sage_sink_blocks.argtypes = [Shape, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib
 
@@ -208,6 +209,18 @@ def thrift_select(q: torch.Tensor, k_smoothed: torch.Tensor, frac: float, causal
     return mask
 
 
+def sink_select(q: torch.Tensor, n_first: int, n_last: int, causal: bool,
+                q_block: int = 128, k_block: int = 64) -> torch.Tensor:
+    """Static mask [B,Hq,nQB,nKB] u8: each Q block's first n_first and last n_last valid K blocks."""
+    _dev(q)
+    B, Hq, N, D = q.shape
+    nQB, nKB = (N + q_block - 1) // q_block, (N + k_block - 1) // k_block
+    mask = torch.empty((B, Hq, nQB, nKB), dtype=torch.uint8, device=q.device)
+    _check("sage_sink_blocks", lib().sage_sink_blocks(_shape(q), q_block, k_block, int(n_first), int(n_last),
+                                                      int(causal), _ptr(mask), _stream()))
+    return mask
+
+
 def convert_f32(x: torch.Tensor, fmt: int) -> torch.Tensor:
     _dev(x)
     out = torch.empty(x.numel(), dtype=torch.int16 if fmt in (BF16, FP16) else torch.uint8, device=x.device)
@@ -216,7 +229,7 @@ def convert_f32(x: torch.Tensor, fmt: int) -> torch.Tensor:
 
 
 # ------------------------------------------------------------------------------------ whole pass
-VARIANTS = ("int8", "int8_fp8pv", "mxfp4", "nvfp4_search", "thrift")
+VARIANTS = ("int8", "int8_fp8pv", "mxfp4", "nvfp4_search", "thrift", "sink")
 
 
 @dataclass
@@ -233,14 +246,16 @@ class Pass:
 
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str = "int8",
             sm_scale: float = 0.0, thrift_frac: float = 0.05, search_mode: int = SEARCH,
-            out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False, hadamard: bool = False) -> Pass:
+            out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False, hadamard: bool = False,
+            sink_first: int = 1, sink_last: int = 1) -> Pass:
     """K smoothing -> block quantization -> (Thrift selection) -> fused attention.  K_s is only
     materialized when Thrift needs it (or keep_smoothed); otherwise K is quantized with the
     smoothing applied on the fly (identical codes).  hadamard: Q and K_s are quantized after
     the orthogonal Hadamard transform of their rows (QK^T unchanged; V and Thrift's bf16
-    tiles take the original rows)."""
+    tiles take the original rows).  variant "sink": INT8 tiles except each Q block's first
+    sink_first and last sink_last valid K blocks, which run in bf16 (a static Thrift mask)."""
     B, Hq, N, D = q.shape
-    need_ks = variant == "thrift" or keep_smoothed
+    need_ks = variant in ("thrift", "sink") or keep_smoothed
     mean, ks = smooth_k(k, want_smoothed=need_ks)
 
     def quant_k(fmt, block, mode=ABSMAX):
@@ -248,7 +263,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
                 else quantize_smoothed(k, mean, fmt, block, mode, hadamard))
 
     mask = None
-    if variant in ("int8", "int8_fp8pv", "thrift"):
+    if variant in ("int8", "int8_fp8pv", "thrift", "sink"):
         qq = quantize(q, INT8, (128, D), hadamard=hadamard)
         kq = quant_k(INT8, (64, D))
         if variant == "int8_fp8pv":
@@ -256,8 +271,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
             out = attn_fwd(qq, kq, vq, causal, E4M3, sm_scale, out_dtype=out_dtype)
         else:
             vq = QT(_TORCH_FMT[v.dtype], v, None, tuple(v.shape))
-            if variant == "thrift":
-                mask = thrift_select(q, ks, thrift_frac, causal)
+            if variant in ("thrift", "sink"):
+                mask = (thrift_select(q, ks, thrift_frac, causal) if variant == "thrift"
+                        else sink_select(q, sink_first, sink_last, causal))
                 out = attn_fwd(qq, kq, vq, causal, BF16, sm_scale, block_mask=mask, q_hi=q, k_hi=ks,
                                out_dtype=out_dtype)
             else:

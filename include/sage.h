@@ -202,6 +202,18 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
                          size_t workspace_bytes, hipStream_t stream);
 size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_block);
 
+/* Sink-aware static block selection — "Search Your Block Floating Point Scales!" (Method >
+ * ScaleSearchAttention: the first and the last blocks of the KV cache are kept at full
+ * precision, the middle ones low-bit).  For every (b, q-head) and Q block qb, with kl its
+ * last causal-valid K block (k_block*kl <= q_block*qb + q_block - 1 when causal, else the
+ * last K block), mask_out[b,h,qb,kb] = 1 for kb <= kl with kb < n_first or kb > kl - n_last.
+ * With causal masking the last valid blocks are the diagonal ones: each query's most recent
+ * keys.  The mask feeds sage_attn_fwd's block_mask (bf16 tiles), as Thrift's does.
+ *   qs: the [B,Hq,N,D] shape of q;  mask_out [B,Hq,nQB,nKB] u8 (device).  q_block = 128 and
+ *   k_block = 64 are supported (else SAGE_ENOTSUP); n_first, n_last >= 0 (else SAGE_EINVAL). */
+int sage_sink_blocks(sage_shape qs, int q_block, int k_block, int n_first, int n_last, int causal, uint8_t* mask_out,
+                     hipStream_t stream);
+
 /* Format conversion as the quantizers perform it, for verification: n fp32 values (device)
  * to fmt codes (device): SAGE_BF16 / SAGE_FP16 (uint16 each), SAGE_E4M3 (byte each,
  * saturating), SAGE_MXFP4 / SAGE_NVFP4 (an E2M1 code per byte, saturating).               */

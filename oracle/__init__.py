@@ -208,6 +208,24 @@ def thrift_select(q16: np.ndarray, ks16: np.ndarray, dt: int, q_block: int, k_bl
     return mask, scores
 
 
+def sink_mask(B: int, Hq: int, N: int, q_block: int, k_block: int, n_first: int, n_last: int, causal: bool):
+    """Sink-aware static selection ("Search Your Block Floating Point Scales!", Method ›
+    ScaleSearchAttention: the first and last KV-cache blocks stay at full precision).  Per Q
+    block qb, the valid K blocks are 0..kl, kl = the last one a causal row of the block sees
+    (the last K block when not causal); marked: the first n_first and the last n_last of them."""
+    nQB = (N + q_block - 1) // q_block
+    nKB = (N + k_block - 1) // k_block
+    mask = np.zeros((B, Hq, nQB, nKB), np.uint8)
+    for qb in range(nQB):
+        # the causal-valid rule of the Thrift selection: a K block is valid for Q block qb if
+        # its first key is at or before the Q block's last row
+        valid = [kb for kb in range(nKB) if not causal or k_block * kb <= q_block * qb + q_block - 1]
+        chosen = set(valid[:n_first]) | set(valid[len(valid) - n_last:] if n_last > 0 else [])
+        for kb in chosen:
+            mask[:, :, qb, kb] = 1
+    return mask
+
+
 class _AttnArgs(C.Structure):
     _fields_ = [
         ("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("N", C.c_int64), ("D", C.c_int64),

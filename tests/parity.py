@@ -40,7 +40,8 @@ def check_out(gpu: np.ndarray, orc: np.ndarray, what: str = ""):
 
 
 def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str,
-                bh=None, qb=None, frac: float = 0.05, search_mode: int = 1, threads=None, hadamard: bool = False):
+                bh=None, qb=None, frac: float = 0.05, search_mode: int = 1, threads=None, hadamard: bool = False,
+                sink=(1, 1)):
     """The whole quantize-and-attend pass on the oracle, from the same 16-bit inputs.
     hadamard: Q and K_s are quantized after the Hadamard transform of their rows."""
     dt = I.dtype_code(q.dtype)
@@ -49,7 +50,7 @@ def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
     Hkv = k.shape[1]
     mean, ks = oracle.smooth_k(kb16, dt)
     res = {"mean": mean, "ks": ks}
-    if variant in ("int8", "int8_fp8pv", "thrift"):
+    if variant in ("int8", "int8_fp8pv", "thrift", "sink"):
         qc, qs = oracle.quant_int8(qb16, dt, 128, hadamard)
         kc, kss = oracle.quant_int8(ks, dt, 64, hadamard)
         res.update(q_codes=qc, q_scales=qs, k_codes=kc, k_scales=kss)
@@ -62,6 +63,9 @@ def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
             mask = None
             if variant == "thrift":
                 mask, _ = oracle.thrift_select(qb16, ks, dt, 128, 64, frac, causal)
+                res["mask"] = mask
+            elif variant == "sink":
+                mask = oracle.sink_mask(B, Hq, N, 128, 64, sink[0], sink[1], causal)
                 res["mask"] = mask
             ops = oracle.AttnOperands(qk_fmt=oracle.QK_INT8, p_fmt=oracle.P_BF16, v_fmt=oracle.V_HI, q_i8=qc, q_s=qs,
                                       k_i8=kc, k_s=kss, v_hi=vb16, v_dt=dt, q_hi=qb16, k_hi=ks, hi_dt=dt,

@@ -130,6 +130,11 @@ def test_validation_before_launch(L):
                                   0x3000_0000, None) == -2
     assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.MXFP4, sage.Block(1, 32), H | 1, 0x2000_0000,
                                   0x3000_0000, None) == -1                 # search modes are NVFP4's
+    # sink mask: 128 / 64 blocks, non-negative counts, a destination
+    assert L.sage_sink_blocks(shp, 128, 64, -1, 1, 1, 0x1000_0000, None) == -1
+    assert L.sage_sink_blocks(shp, 64, 64, 1, 1, 1, 0x1000_0000, None) == -2
+    assert L.sage_sink_blocks(shp, 128, 64, 1, 1, 2, 0x1000_0000, None) == -1
+    assert L.sage_sink_blocks(shp, 128, 64, 1, 1, 1, None, None) == -1
     # smoothing workspace
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
 

@@ -23,6 +23,7 @@ FULL = [
     ("fp4_search", False, "mxfp4"),
     ("fp4_search", False, "nvfp4_search"),
     ("thrift_long", True, "thrift"),
+    ("thrift_long", True, "sink"),
 ]
 
 
@@ -56,7 +57,7 @@ def test_full_size_sampled_parity(name, causal, variant):
         sc = np.ascontiguousarray(orc[f"{side}_scales"]).reshape(-1)
         gs = u8(qt.scales.contiguous()).reshape(-1)[: sc.nbytes]          # raw bytes of the scale buffer
         assert np.array_equal(gs, sc.view(np.uint8)), f"{side} scales"
-    if variant == "thrift":
+    if variant in ("thrift", "sink"):
         assert np.array_equal(res.mask.cpu().numpy(), orc["mask"])
 
     # the bar applies to the output as a whole: max|O_gpu - O_oracle| <= 2e-3 max|O_oracle| over

@@ -266,6 +266,15 @@ def test_hadamard_attention_parity(name, ov, causal, variant):
     print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
 
 
+@pytest.mark.parametrize("N,causal", [(1000, True), (1000, False), (4500, True), (333, False)])
+def test_sink_mask_bit_exact(N, causal):
+    sage = _sage()
+    q = torch.zeros((2, 3, N, 64), dtype=torch.bfloat16, device="cuda")
+    for nf, nl in ((1, 1), (2, 3), (0, 4), (5, 0), (0, 0), (1000, 1000)):
+        m = sage.sink_select(q, nf, nl, causal)
+        assert np.array_equal(m.cpu().numpy(), oracle.sink_mask(2, 3, N, 128, 64, nf, nl, causal)), (nf, nl)
+
+
 # ------------------------------------------------------------------------------ attention
 ATT_CASES = [
     ("tiny_int8", {}, False, "int8"),
@@ -284,6 +293,8 @@ ATT_CASES = [
     ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=333), False, "nvfp4_search"),
     ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=512), True, "nvfp4_search"),
     ("fp4_search", dict(B=2, Hq=4, Hkv=2, N=640), False, "nvfp4_search"),  # GQA
+    ("thrift_long", dict(B=1, Hq=4, Hkv=2, N=1100), True, "sink"),
+    ("thrift_long", dict(B=1, Hq=2, Hkv=1, N=640), False, "sink"),
 ]
 
 
@@ -296,7 +307,7 @@ def test_attention_parity(name, ov, causal, variant):
     res = sage.forward(*_cuda(q, k, v), causal=causal, variant=variant)
     torch.cuda.synchronize()
     orc = oracle_pass(q, k, v, causal, variant)
-    if variant == "thrift":
+    if variant in ("thrift", "sink"):
         assert np.array_equal(res.mask.cpu().numpy(), orc["mask"])
     rel, cos = check_out(res.out.cpu().numpy(), orc["out"], f"{name} {variant} causal={causal}")
     ref = fp64_reference(q, k, v, causal)

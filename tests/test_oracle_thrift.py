@@ -94,3 +94,31 @@ def test_mixed_precision_moves_toward_reference(thrift_small):
     e_int8 = np.abs(oracle.attention(_int8_ops(q, ks, v, None), B, Hq, Hkv, N, D, True, sm) - ref).mean()
     e_mix = np.abs(oracle.attention(_int8_ops(q, ks, v, m), B, Hq, Hkv, N, D, True, sm) - ref).mean()
     assert e_mix < e_int8
+
+
+# ---------------------------------------------------------------- sink-aware static selection
+def test_sink_mask_hand_example():
+    """N = 384: 3 Q blocks of 128, 6 K blocks of 64.  Causal: Q block qb sees K blocks
+    0..2qb+1.  Written out from the definition (first n_first and last n_last valid blocks)."""
+    m = oracle.sink_mask(1, 1, 384, 128, 64, 1, 1, True)[0, 0]
+    assert m.tolist() == [[1, 1, 0, 0, 0, 0], [1, 0, 0, 1, 0, 0], [1, 0, 0, 0, 0, 1]]
+    m = oracle.sink_mask(1, 1, 384, 128, 64, 1, 2, True)[0, 0]
+    assert m.tolist() == [[1, 1, 0, 0, 0, 0], [1, 0, 1, 1, 0, 0], [1, 0, 0, 0, 1, 1]]
+    m = oracle.sink_mask(1, 1, 384, 128, 64, 2, 1, False)[0, 0]
+    assert m.tolist() == [[1, 1, 0, 0, 0, 1]] * 3
+    m = oracle.sink_mask(1, 1, 384, 128, 64, 0, 0, True)[0, 0]
+    assert m.sum() == 0
+
+
+@pytest.mark.parametrize("N,causal", [(1000, True), (1000, False), (4500, True), (64, True)])
+def test_sink_mask_counts_closed_form(N, causal):
+    nQB, nKB = (N + 127) // 128, (N + 63) // 64
+    for nf, nl in ((1, 1), (2, 3), (0, 4), (5, 0), (100, 100)):
+        m = oracle.sink_mask(2, 3, N, 128, 64, nf, nl, causal)
+        assert np.array_equal(m[0, 0], m[1, 2])           # the same for every head
+        for qb in range(nQB):
+            kl = min(nKB - 1, (128 * qb + 127) // 64) if causal else nKB - 1
+            row = m[0, 0, qb]
+            assert row[kl + 1:].sum() == 0                  # nothing past the last valid block
+            assert row.sum() == min(kl + 1, nf + nl)        # no double count until the ranges meet
+            assert row[:min(nf, kl + 1)].all() and row[max(0, kl + 1 - nl):kl + 1].all()
