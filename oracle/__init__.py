@@ -226,6 +226,42 @@ def sink_mask(B: int, Hq: int, N: int, q_block: int, k_block: int, n_first: int,
     return mask
 
 
+def nvfp4_rows_value(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """fp64 values of NVFP4 rows along D: codes [..., D/2] (even element in the low nibble),
+    UE4M3 scales [..., D/16]; value = E2M1(code) * UE4M3(scale of its 16-element group)."""
+    codes = np.asarray(codes, np.uint8); scales = np.asarray(scales, np.uint8)
+    lo = e2m1_decode(codes & 15); hi = e2m1_decode(codes >> 4)
+    vals = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    return vals * np.repeat(e4m3_decode(scales), 16, axis=-1)
+
+
+def decode_attention(q16: np.ndarray, dt: int, k_codes, k_scales, v_codes, v_scales, causal: bool,
+                     sm_scale: float) -> np.ndarray:
+    """Decode-shaped attention on a KV cache held in NVFP4 ("Search Your Block Floating Point
+    Scales!", Method › ScaleSearchAttention: the KV cache stored in 4 bits).  q [B,Hq,Nq,D]
+    16-bit; K and V as NVFP4 rows along D, [B,Hkv,Nk,D/2] codes and [B,Hkv,Nk,D/16] scales.
+    Query i stands at position Nk - Nq + i (the newest tokens); with causal masking it sees
+    keys j <= Nk - Nq + i.  Textbook fp64 softmax(q K^T sm_scale) V on the cache's values;
+    q-head h reads KV head h // (Hq / Hkv)."""
+    q = decode16(np.asarray(q16, np.uint16), dt).astype(np.float64)
+    K = nvfp4_rows_value(k_codes, k_scales)
+    V = nvfp4_rows_value(v_codes, v_scales)
+    B, Hq, Nq, D = q.shape
+    Hkv, Nk = K.shape[1], K.shape[2]
+    G = Hq // Hkv
+    out = np.empty((B, Hq, Nq, D), np.float64)
+    pos = Nk - Nq + np.arange(Nq)
+    for b in range(B):
+        for h in range(Hq):
+            S = (q[b, h] @ K[b, h // G].T) * sm_scale
+            if causal:
+                S = np.where(np.arange(Nk)[None, :] <= pos[:, None], S, -np.inf)
+            S = S - S.max(axis=1, keepdims=True)
+            P = np.exp(S)
+            out[b, h] = (P @ V[b, h // G]) / P.sum(axis=1, keepdims=True)
+    return out
+
+
 class _AttnArgs(C.Structure):
     _fields_ = [
         ("B", C.c_int64), ("Hq", C.c_int64), ("Hkv", C.c_int64), ("N", C.c_int64), ("D", C.c_int64),
