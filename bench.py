@@ -29,7 +29,7 @@ PEAK = {"int8": 5000.0, "fp8": 5000.0, "bf16": 2500.0, "fp4": 10100.0}
 HBM_GBS = 8000.0
 
 DEFAULT_VARIANT = {"tiny_int8": "int8", "llm_int8": "int8", "video_fp8": "int8_fp8pv", "fp4_search": "mxfp4",
-                   "thrift_long": "thrift"}
+                   "thrift_long": "thrift", "decode_nvfp4": "decode"}
 VARIANT_PEAK = {"int8": "int8", "thrift": "int8", "sink": "int8", "int8_fp8pv": "int8", "mxfp4": "fp4",
                 "nvfp4_search": "fp8"}
 PV_PEAK = {"int8": "bf16", "thrift": "bf16", "sink": "bf16", "int8_fp8pv": "fp8", "mxfp4": "fp4", "nvfp4_search": "fp8"}
@@ -98,6 +98,98 @@ def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float, hadama
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": f"{len(done)} whole (b,h) heads {' '.join(done)} of {w.name} at N={w.N}, D={w.D}"
                       f"{' causal' if causal else ''}: smoothing + quantization + tiled attention, {t:.1f} s"}
+
+
+def decode_cpu_baseline(w, q, kc, ks, vc, vs, budget_s: float):
+    """The oracle's decode attention, whole sequences at a time, until ~budget_s."""
+    import numpy as np
+    import torch
+    import oracle
+    cshape, sshape = (w.B, w.Hkv, w.N, 64), (w.B, w.Hkv, w.N, 8)
+    kc, ks, vc, vs = kc.reshape(cshape), ks.reshape(sshape), vc.reshape(cshape), vs.reshape(sshape)
+    q16 = q.contiguous().view(torch.int16).numpy().view(np.uint16)
+    ops, done = 0.0, 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        sl = slice(b, b + 1)
+        oracle.decode_attention(q16[sl], 0, kc[sl], ks[sl], vc[sl], vs[sl], False, 1.0 / math.sqrt(w.D))
+        ops += 4.0 * w.Hq * w.Nq * w.N * w.D
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    t = time.perf_counter() - t0
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.B} sequences of {w.name} (all {w.Hq} q-heads, {w.Nq} new token against "
+                      f"{w.N} cached keys; numpy fp64 on the dequantized cache), {t:.1f} s"}
+
+
+def run_decode(args, w):
+    """One decode step = one attention call of w.Nq new tokens against an NVFP4 KV cache that is
+    quantized once, before the timed region (a cache is written once and read every step)."""
+    import torch
+    from bit_quantized_attention_03_amd import inputs as I
+    from bit_quantized_attention_03_amd import sage
+    dev = torch.device("cuda:0")
+    q_cpu, k_cpu, v_cpu = I.make_qkv(w, seed=0)
+    q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
+    kq = sage.quantize(k, sage.NVFP4, (1, 16), sage.SEARCH)
+    vq = sage.quantize(v, sage.NVFP4, (1, 16), sage.SEARCH)
+    del k, v
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(record):
+        if record:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        out = sage.decode(q, kq, vq, False)
+        if record:
+            e1.record(stream)
+            ev.append((e0, e1))
+        return out
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    ops = 4.0 * w.B * w.Hq * w.Nq * w.N * w.D
+    # algorithmic bytes of one call: the cache (codes + scales of K and V), Q and fp32 O
+    cache = 2 * w.B * w.Hkv * w.N * (w.D // 2 + w.D // 16)
+    alg = cache + w.B * w.Hq * w.Nq * w.D * 2 + w.B * w.Hq * w.Nq * w.D * 4
+    achieved = alg / (kern_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "quantized attention fwd TOPS (4*B*H*N^2*d/t) at d=128 N=4096 + % of MFMA peak",
+        "value": round(ops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 cache, fp32 softmax",
+        "data": "synthetic (seeded PCG64; N(0,1) queries, keys and values)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.N, "D": w.D,
+                   "causal": False, "variant": "decode", "input_dtype": "bfloat16",
+                   "step": "decode attention of the new tokens against the NVFP4 KV cache (split + combine); "
+                           "ops counted as 4*B*Hq*Nq*Nk*d"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel": "decode (split + combine)",
+                     "kernel_ms": round(kern_ms, 4), "algorithmic_bytes": alg},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = decode_cpu_baseline(w, q_cpu, kq.codes.cpu().numpy(), kq.scales.cpu().numpy(),
+                                                  vq.codes.cpu().numpy(), vq.scales.cpu().numpy(),
+                                                  args.cpu_seconds)
+    print(json.dumps(rec))
 
 
 def calibrate_copy(n: int = 1 << 28, reps: int = 3):
@@ -174,6 +266,8 @@ def main():
     w = I.workload(args.workload)
     variant = args.variant or DEFAULT_VARIANT[w.name]
     causal = bool(args.causal or w.causal)
+    if variant == "decode":
+        return run_decode(args, w)
     if args.traffic_from:
         return traffic_from(args.traffic_from, traffic_key(w.name, causal, variant), "attn_",
                             os.path.join(ROOT, "profiles", "attn_traffic.json"))

@@ -236,6 +236,35 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
                                        (int)qs.D, frac, causal, mask_out, workspace, stream));
 }
 
+size_t sage_decode_workspace_bytes(sage_shape qs, sage_shape ks) {
+  if (!shape_ok(qs) || !shape_ok(ks) || qs.H % ks.H != 0) return 0;
+  return decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
+}
+
+int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
+                    int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!q || !k || !v || !out || !shape_ok(qs)) return SAGE_EINVAL;
+  if (!k->codes || !k->scales || !v->codes || !v->scales) return SAGE_EINVAL;
+  const sage_shape &ks = k->shape, &vs = v->shape;
+  if (!shape_ok(ks) || !shape_ok(vs)) return SAGE_EINVAL;
+  if (ks.B != qs.B || vs.B != qs.B || vs.H != ks.H || vs.N != ks.N || ks.D != qs.D || vs.D != qs.D) return SAGE_EINVAL;
+  if (qs.H % ks.H != 0 || (causal != 0 && causal != 1)) return SAGE_EINVAL;
+  if (qs.N > ks.N || ks.N == 0) return SAGE_EINVAL;   // the new tokens are the cache's last positions
+  if (ks.N > (1 << 26)) return SAGE_EINVAL;           // cache offsets are 32-bit (64 bytes a key)
+  if (!is16(q_dt) || k->fmt != SAGE_NVFP4 || v->fmt != SAGE_NVFP4 || qs.D != 128) return SAGE_ENOTSUP;
+  if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
+  if (!aligned16(q) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
+  const size_t need = decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
+  if (!workspace || workspace_bytes < need) return SAGE_EWORKSPACE;
+  if (!aligned16(workspace)) return SAGE_EALIGN;
+  if (qs.B == 0 || qs.N == 0) return SAGE_OK;
+  const float sc = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)qs.D);
+  return launched(launch_decode((const uint16_t*)q, q_dt == SAGE_FP16, qs.B, qs.H, ks.H, qs.N, ks.N,
+                                (const uint8_t*)k->codes, (const uint8_t*)k->scales, (const uint8_t*)v->codes,
+                                (const uint8_t*)v->scales, causal, sc, out, out_dt == SAGE_BF16, workspace, stream));
+}
+
 int sage_sink_blocks(sage_shape qs, int q_block, int k_block, int n_first, int n_last, int causal, uint8_t* mask_out,
                      hipStream_t stream) {
   if (!mask_out || !shape_ok(qs)) return SAGE_EINVAL;

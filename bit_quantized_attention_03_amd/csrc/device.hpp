@@ -126,4 +126,22 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---- lane exchange ----------------------------------------------------------------
+// The value of lane ^ m (m in {1, 2, 4, 8}; the lanes of a row of 16 exchange) through DPP:
+// xor 1 and xor 2 are quad permutations, xor 8 rotates the row by 8, xor 4 is the half-row
+// mirror (i -> 7 - i within 8) followed by the reversed quad (i -> 3 - i within 4).
+template <int m>
+__device__ __forceinline__ float lane_xor(float v) {
+  int x = __builtin_bit_cast(int, v);
+  if constexpr (m == 1) x = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  else if constexpr (m == 2) x = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  else if constexpr (m == 8) x = __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, true);  // row_ror:8
+  else {
+    static_assert(m == 4, "lanes of one row of 16");
+    x = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);   // row_half_mirror
+    x = __builtin_amdgcn_mov_dpp(x, 0x1B, 0xF, 0xF, true);    // quad_perm [3,2,1,0]
+  }
+  return __builtin_bit_cast(float, x);
+}
+
 }  // namespace sage

@@ -32,6 +32,12 @@ hipError_t launch_convert_f32(const float* x, int64_t n, int fmt, void* out, hip
 hipError_t launch_thrift_select(const uint16_t* q, const uint16_t* ks, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
                                 int D, double frac, int causal, uint8_t* mask, void* ws, hipStream_t st);
 size_t thrift_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int D);
+// Decode-shaped attention on an NVFP4 KV cache (rows along D, d = 128): split workgroups
+// write partial (O, max, sum) to ws (decode_ws_bytes), a combine kernel writes out.
+size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk);
+hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
+                         const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int causal,
+                         float sm_scale, void* out, bool out_bf16, void* ws, hipStream_t st);
 // Static sink-and-recent block mask [BH, nQB, nKB] (blocks of 128 Q rows and 64 keys).
 hipError_t launch_sink_mask(int64_t BH, int64_t N, int n_first, int n_last, int causal, uint8_t* mask, hipStream_t st);
 

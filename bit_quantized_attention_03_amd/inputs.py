@@ -26,6 +26,7 @@ class Workload:
     dtype: torch.dtype
     causal: bool
     recipe: str
+    Nq: int = 0      # query rows when they differ from N (decode: a few new tokens against N keys)
 
 
 WORKLOADS = {
@@ -34,6 +35,8 @@ WORKLOADS = {
     "video_fp8": Workload("video_fp8", 2, 24, 24, 16384, 64, torch.bfloat16, False, "video"),
     "fp4_search": Workload("fp4_search", 2, 16, 16, 8192, 128, torch.bfloat16, False, "fp4"),
     "thrift_long": Workload("thrift_long", 1, 32, 8, 32768, 128, torch.bfloat16, True, "thrift"),
+    # one new token per sequence against a 32K-token KV cache (held in NVFP4 by the decode path)
+    "decode_nvfp4": Workload("decode_nvfp4", 8, 32, 8, 32768, 128, torch.bfloat16, False, "decode", Nq=1),
 }
 
 
@@ -46,9 +49,9 @@ def _to16(x: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
 
 
 def make_qkv(w: Workload, seed: int = 0):
-    """Returns CPU tensors (q [B,Hq,N,D], k [B,Hkv,N,D], v [B,Hkv,N,D]) of dtype w.dtype."""
+    """Returns CPU tensors (q [B,Hq,Nq or N,D], k [B,Hkv,N,D], v [B,Hkv,N,D]) of dtype w.dtype."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    qs, ks = (w.B, w.Hq, w.N, w.D), (w.B, w.Hkv, w.N, w.D)
+    qs, ks = (w.B, w.Hq, w.Nq or w.N, w.D), (w.B, w.Hkv, w.N, w.D)
     q = rng.standard_normal(qs)
     k = rng.standard_normal(ks)
     v = rng.standard_normal(ks)
@@ -68,6 +71,8 @@ def make_qkv(w: Workload, seed: int = 0):
             x[sel] = 4.0 * rng.standard_t(3, size=int(sel.sum()))
     elif w.recipe == "thrift":    # 64 attention-sink keys (the first K block) scaled x6
         k[:, :, :64, :] *= 6.0
+    elif w.recipe == "decode":    # plain N(0, 1) queries, keys and values
+        pass
     else:
         raise ValueError(w.recipe)
     return _to16(q, w.dtype), _to16(k, w.dtype), _to16(v, w.dtype)

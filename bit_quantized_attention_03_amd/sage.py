@@ -70,6 +70,10 @@ def lib():
         L.thrift_workspace_bytes.argtypes = [Shape, Shape, C.c_int, C.c_int]
         L.sage_convert_f32.argtypes = [C.c_void_p, C.c_int64, C.c_int, C.c_void_p, C.c_void_p]
         L.sage_sink_blocks.argtypes = [Shape, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_void_p, C.c_void_p]
+        L.sage_decode_workspace_bytes.restype = C.c_size_t
+        L.sage_decode_workspace_bytes.argtypes = [Shape, Shape]
+        L.sage_decode_fwd.argtypes = [C.c_void_p, C.c_int, Shape, C.POINTER(QTensorC), C.POINTER(QTensorC), C.c_int,
+                                      C.c_float, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]
         _lib = L
     return _lib
 
@@ -219,6 +223,22 @@ def sink_select(q: torch.Tensor, n_first: int, n_last: int, causal: bool,
     _check("sage_sink_blocks", lib().sage_sink_blocks(_shape(q), q_block, k_block, int(n_first), int(n_last),
                                                       int(causal), _ptr(mask), _stream()))
     return mask
+
+
+def decode(q: torch.Tensor, k: QT, v: QT, causal: bool = False, sm_scale: float = 0.0,
+           out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Nq new rows q [B,Hq,Nq,D] against an NVFP4 KV cache (k, v from quantize(x, NVFP4, (1, 16), ...))."""
+    _dev(q)
+    B, Hq, Nq, D = q.shape
+    out = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q.device)
+    ks = Shape(*k.shape)
+    wsb = lib().sage_decode_workspace_bytes(_shape(q), ks)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=q.device)
+    kc, vc = k.c(), v.c()
+    _check("sage_decode_fwd", lib().sage_decode_fwd(_ptr(q), _TORCH_FMT[q.dtype], _shape(q), C.byref(kc), C.byref(vc),
+                                                    int(causal), float(sm_scale), _ptr(out), _TORCH_FMT[out_dtype],
+                                                    _ptr(ws), ws.numel(), _stream()))
+    return out
 
 
 def convert_f32(x: torch.Tensor, fmt: int) -> torch.Tensor:

@@ -202,6 +202,24 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
                          size_t workspace_bytes, hipStream_t stream);
 size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_block);
 
+/* Decode-shaped attention on an NVFP4 KV cache — "Search Your Block Floating Point Scales!"
+ * (Method > ScaleSearchAttention: the KV cache stored in 4 bits).  Nq new query rows attend to
+ * a cache of Nk keys; query i stands at position Nk - Nq + i, and with causal = 1 it sees keys
+ * j <= Nk - Nq + i (else all Nk).  out = softmax(q K^T sm_scale) V, with K and V the cache's
+ * NVFP4 values (E2M1 x UE4M3), computed in fp32 (P is not quantized); sm_scale 0 selects
+ * 1 / sqrt(D).  q-head h reads KV head h / (Hq / Hkv).
+ *   q   [B,Hq,Nq,D] in q_dt (SAGE_BF16 | SAGE_FP16), 16-byte aligned;
+ *   k,v SAGE_NVFP4 along D, shape [B,Hkv,Nk,D]: codes [B,Hkv,Nk,D/2] (16-byte aligned),
+ *       UE4M3 scales [B,Hkv,Nk,D/16] (sage_quantize_blocks with block (1, 16));
+ *   out [B,Hq,Nq,D] in out_dt (SAGE_FP32 | SAGE_BF16);
+ *   workspace >= sage_decode_workspace_bytes(q shape, k shape) bytes of device memory
+ *   (partial results of the key splits).
+ * D = 128 (else SAGE_ENOTSUP); 1 <= Nk <= 2^26 and Nq <= Nk (else SAGE_EINVAL).            */
+int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
+                    int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+size_t sage_decode_workspace_bytes(sage_shape qs, sage_shape ks);
+
 /* Sink-aware static block selection — "Search Your Block Floating Point Scales!" (Method >
  * ScaleSearchAttention: the first and the last blocks of the KV cache are kept at full
  * precision, the middle ones low-bit).  For every (b, q-head) and Q block qb, with kl its

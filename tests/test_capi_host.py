@@ -135,6 +135,18 @@ def test_validation_before_launch(L):
     assert L.sage_sink_blocks(shp, 64, 64, 1, 1, 1, 0x1000_0000, None) == -2
     assert L.sage_sink_blocks(shp, 128, 64, 1, 1, 2, 0x1000_0000, None) == -1
     assert L.sage_sink_blocks(shp, 128, 64, 1, 1, 1, None, None) == -1
+    # decode: NVFP4 cache, D = 128, Nq <= Nk, workspace
+    qd = sage.Shape(1, 4, 2, 128)
+    kn = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128))
+    k8 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128))
+    short = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 1, 128))
+    assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(k8), C.byref(k8), 0, 0.0, 0x1000_0000, sage.FP32,
+                             0x1000_0000, 1 << 30, None) == -2
+    assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(short), C.byref(short), 0, 0.0, 0x1000_0000,
+                             sage.FP32, 0x1000_0000, 1 << 30, None) == -1
+    assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(kn), C.byref(kn), 0, 0.0, 0x1000_0000, sage.FP32,
+                             None, 0, None) == -4
+    assert L.sage_decode_workspace_bytes(qd, sage.Shape(1, 2, 100, 128)) > 0
     # smoothing workspace
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
 

@@ -73,3 +73,23 @@ def test_full_size_sampled_parity(name, causal, variant):
         gs.append(g); os_.append(o)
     rel, cos = check_out(np.concatenate(gs), np.concatenate(os_), f"{name} {variant} sampled rows")
     print(f"  sampled rows: rel_err_vs_oracle = {rel:.2e}, cosine {cos:.7f}")
+
+
+def test_decode_full_size_sampled():
+    """decode_nvfp4 (8 sequences, 32 q-heads over 8 KV heads, one new token against 32768
+    cached keys) in bench.py's launch configuration; the oracle attends for two sequences."""
+    from bit_quantized_attention_03_amd import sage
+    w = I.workload("decode_nvfp4")
+    print("[case] full size decode_nvfp4", flush=True)
+    q, k, v = I.make_qkv(w, seed=0)
+    kq = sage.quantize(k.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
+    vq = sage.quantize(v.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
+    out = sage.decode(q.cuda(), kq, vq, False).cpu().numpy()
+    cshape, sshape = (w.B, w.Hkv, w.N, 64), (w.B, w.Hkv, w.N, 8)
+    kc, ks = u8(kq.codes).reshape(cshape), u8(kq.scales).reshape(sshape)
+    vc, vs = u8(vq.codes).reshape(cshape), u8(vq.scales).reshape(sshape)
+    for b in (0, w.B - 1):
+        sl = slice(b, b + 1)
+        want = oracle.decode_attention(I.bits16(q[sl]), 0, kc[sl], ks[sl], vc[sl], vs[sl], False, 1.0 / math.sqrt(128))
+        rel, cos = check_out(out[sl], want, f"decode full size, sequence {b}")
+        print(f"  sequence {b}: rel_err_vs_oracle = {rel:.2e}, cosine {cos:.7f}")
