@@ -105,8 +105,9 @@ def decode_cpu_baseline(w, q, kc, ks, vc, vs, budget_s: float):
     import numpy as np
     import torch
     import oracle
-    cshape, sshape = (w.B, w.Hkv, w.N, 64), (w.B, w.Hkv, w.N, 8)
-    kc, ks, vc, vs = kc.reshape(cshape), ks.reshape(sshape), vc.reshape(cshape), vs.reshape(sshape)
+    Np = (w.N + 63) // 64 * 64
+    kc, ks = kc.reshape(w.B, w.Hkv, w.N, 64), ks.reshape(w.B, w.Hkv, w.N, 8)
+    vc, vs = vc.reshape(w.B, w.Hkv, w.D, Np // 2), vs.reshape(w.B, w.Hkv, Np // 16, w.D)
     q16 = q.contiguous().view(torch.int16).numpy().view(np.uint16)
     ops, done = 0.0, 0
     t0 = time.perf_counter()
@@ -132,8 +133,8 @@ def run_decode(args, w):
     dev = torch.device("cuda:0")
     q_cpu, k_cpu, v_cpu = I.make_qkv(w, seed=0)
     q, k, v = q_cpu.to(dev), k_cpu.to(dev), v_cpu.to(dev)
-    kq = sage.quantize(k, sage.NVFP4, (1, 16), sage.SEARCH)
-    vq = sage.quantize(v, sage.NVFP4, (1, 16), sage.SEARCH)
+    kq = sage.quantize(k, sage.NVFP4, (1, 16), sage.SEARCH)    # K rows along D
+    vq = sage.quantize(v, sage.NVFP4, (16, 1), sage.SEARCH)    # V along the tokens
     del k, v
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()

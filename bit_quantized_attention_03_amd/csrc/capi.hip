@@ -255,6 +255,7 @@ int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qten
   if (!is16(q_dt) || k->fmt != SAGE_NVFP4 || v->fmt != SAGE_NVFP4 || qs.D != 128) return SAGE_ENOTSUP;
   if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
   if (!aligned16(q) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
+  if ((uintptr_t)k->scales % 2) return SAGE_EALIGN;   // read as byte pairs
   const size_t need = decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
   if (!workspace || workspace_bytes < need) return SAGE_EWORKSPACE;
   if (!aligned16(workspace)) return SAGE_EALIGN;

@@ -1,26 +1,33 @@
 // Decode-shaped attention on a KV cache held in NVFP4 — "Search Your Block Floating Point
 // Scales!", Method > ScaleSearchAttention (the KV cache kept in 4 bits).  A few new query rows
-// attend to a long cache whose K and V rows are NVFP4 along D: per token and 16-channel group,
-// 8 code bytes (two E2M1 codes each, even element in the low nibble) and one UE4M3 scale, the
-// layout sage_quantize_blocks writes for blocks of (1, 16).  Q stays 16-bit and P fp32.
+// attend to a long cache.  K rows are NVFP4 along D (per token and 16-channel group, 8 code
+// bytes and one UE4M3 scale: sage_quantize_blocks' (1, 16) layout); V is NVFP4 along the
+// tokens (per channel and 16-token group: the (16, 1) layout), the operand order P.V wants.
+// Q stays 16-bit; P is rounded to f16 for the matrix product (its sum stays fp32).
 //
-// The work is reading the cache (144 bytes per key per KV head at d = 128), so the kernel is
-// shaped for HBM rather than for the matrix cores:
-//   * split along the keys: a workgroup takes 512 keys of one (b, KV head) for RG query rows
-//     (the rows are the q-heads of the KV head's group times the new tokens);
-//   * lane = (key slot t, channel group g): 8 lanes cover a key's 128 channels, so a wave
-//     reads 8 whole K and V rows per step (512 contiguous bytes each), and the codes of the
-//     next 8 steps are in flight while a step's arithmetic runs;
-//   * a key's dot products are summed over its 8 lanes with DPP; every lane of the key then
-//     holds the same score, so each key slot keeps its own running max and sum and no value
-//     crosses slots until the end, when slots, waves and splits are merged (log-sum-exp);
-//   * the running max moves only when a score passes it by 16 (log2 units): P stays fp32 and
-//     at most 2^16, and the rescale of O leaves the step loop almost always untaken.
+// The work is reading the cache (144 bytes per key per KV head at d = 128).  Both products
+// run on the matrix cores, so the vector work per key does not grow with the query rows:
+//   * a workgroup takes 1024 keys of one (b, KV head) for 16 query rows (the q-heads of the
+//     KV head's group times the new tokens); each of its 4 waves walks its own 16-key tiles
+//     with its own running max and sum, merged at the end (log-sum-exp);
+//   * S^T (16 keys x 16 rows) = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: lane (r, h) of the
+//     A operand holds key r's 32 channels 32h..32h+31, dequantized in registers from one
+//     16-byte load (E2M1 x UE4M3 is exact in bf16 and f16); Q^T is the B operand with the
+//     same channel order, loaded once;
+//   * the accumulator leaves lane (r, h) with row r's scores of keys 4h..4h+3: exactly the
+//     B operand P^T of O^T (channels x rows) += V^T P^T on v_mfma_f32_16x16x16_f16, whose A
+//     operand V^T needs 4 consecutive tokens of one channel: 2 bytes of the along-token codes;
+//     f16 keeps 11 bits of P (bf16's 8 would cost about 1e-3 of max|O|);
+//   * the running max moves only when a score passes it by 15 (log2 units), checked once per
+//     tile for the whole wave; P <= 2^15 stays finite in f16;
+//   * the workgroup's V codes and scales (1024 tokens x 128 channels) are copied to LDS with
+//     16-byte loads first (channel rows padded to 528 bytes, so the 16 channel lanes of a read
+//     hit distinct banks); each wave then walks its own 256 keys, reading K through a ring of
+//     8 tiles in flight (issued before V's loads) and V's 2-byte pieces from LDS;
+//   * a split writes only the R real rows of its partial O (not the 16 of the row group).
 // decode_combine_kernel merges the splits and writes O.
 #include "device.hpp"
 #include "kernels.hpp"
-
-#include <type_traits>
 
 namespace sage {
 namespace {
@@ -28,219 +35,242 @@ namespace {
 constexpr int DK = 128;             // head dimension
 constexpr int DEC_CHUNK = 1024;     // keys per split workgroup
 constexpr int DEC_THREADS = 256;    // 4 waves x 8 key slots
-constexpr float kLazy = 16.0f;      // headroom of the running max, log2 units
+constexpr float kLazy = 15.0f;      // headroom of the running max, log2 units (P <= 2^15 fits f16)
 
 struct DecodeArgs {
   const uint16_t* q;                           // [B, Hq, Nq, 128] 16-bit
-  const uint8_t *kc, *ks, *vc, *vs;            // codes [B, Hkv, Nk, 64], scales [B, Hkv, Nk, 8]
-  float* part_o;                               // [B * Hkv, nsplit, Rp, 128]
-  float* part_ml;                              // [B * Hkv, nsplit, Rp, 2]
-  int64_t Hq, Hkv, Nq, Nk, nsplit, R, nrg;     // R = (Hq / Hkv) * Nq rows per KV head; nrg groups of RG
-  int q_f16, causal;
+  const uint8_t *kc, *ks;                      // K codes [B, Hkv, Nk, 64], scales [B, Hkv, Nk, 8]
+  const uint8_t *vc, *vs;                      // V codes [B, Hkv, 128, Np/2], scales [B, Hkv, Np/16, 128]
+  float* part_o;                               // [B * Hkv, nsplit, R, 128]
+  float* part_ml;                              // [B * Hkv, nsplit, R, 2]
+  int64_t Hq, Hkv, Nq, Nk, Np, nsplit, R, nrg; // R = (Hq / Hkv) * Nq rows per KV head, nrg groups of 16
+  int causal;
   float qscale;                                // sm_scale * log2(e)
 };
 
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+
+// eight fp32 values -> the MFMA operand type (bf16 or f16; exact for E2M1 x UE4M3 values)
+template <bool F16>
+__device__ __forceinline__ auto pack8(const float* x) {
+  if constexpr (F16) {
+    v8h r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[e];
+    return r;
+  } else {
+    v4i w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = (int)pack_bf16x2(x[2 * e], x[2 * e + 1]);
+    return __builtin_bit_cast(v8bf, w);
+  }
+}
+
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-// the 16 E2M1 values of 8 code bytes (unscaled), element e = 2 * byte + nibble
-__device__ __forceinline__ void e2m1x16(v2i w, float* x) {
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t u = (uint32_t)w[h];
-    const auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 0);   // byte 0: elements 0, 1
-    const auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 1);
-    const auto d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 2);
-    const auto d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 3);
-    float* y = x + 8 * h;
-    y[0] = d0[0]; y[1] = d0[1]; y[2] = d1[0]; y[3] = d1[1];
-    y[4] = d2[0]; y[5] = d2[1]; y[6] = d3[0]; y[7] = d3[1];
-  }
+// A UE4M3 scale byte's value: gfx950's E4M3 conversion (OCP E4M3, the format the quantizers
+// encode with; exact).
+__device__ __forceinline__ float ue4m3(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
+
+// the 8 E2M1 values of 4 code bytes (element e = 2 * byte + nibble), times s
+__device__ __forceinline__ void e2m1x8(uint32_t u, float s, float* x) {
+  const auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 0);
+  const auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 1);
+  const auto d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 2);
+  const auto d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 3);
+  x[0] = d0[0] * s; x[1] = d0[1] * s; x[2] = d1[0] * s; x[3] = d1[1] * s;
+  x[4] = d2[0] * s; x[5] = d2[1] * s; x[6] = d3[0] * s; x[7] = d3[1] * s;
 }
 
-// Dot product of this lane's 16 channels: q as 8 packed 16-bit pairs (the input's own bits),
-// the 16 E2M1 codes decoded to the same 16-bit type (exact), fp32 accumulation by dot2.
+struct Tile {
+  v4i kw;          // key (key0 + r)'s code bytes 16h..16h+15
+  uint32_t ks2;    // its two scale bytes (groups 2h, 2h + 1)
+};
+
+constexpr int VROW = DEC_CHUNK / 2 + 16;            // LDS bytes of a channel's codes (padded)
+constexpr int VSC0 = DK * VROW;                      // LDS offset of the scales [64 groups][128]
+constexpr int VLDS = VSC0 + (DEC_CHUNK / 16) * DK;   // 75776 bytes
+
+// Two workgroups a CU (their LDS allows no more): the register budget is 256 per lane.
 template <bool F16>
-__device__ __forceinline__ float dot16(const uint32_t* qp, v2i w) {
-  float acc = 0.0f;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t u = (uint32_t)w[h];
-#pragma unroll
-    for (int by = 0; by < 4; ++by) {
-      const uint32_t qv = qp[4 * h + by];
-      if constexpr (F16) {
-        v2h k2;
-        if (by == 0) k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 0);
-        else if (by == 1) k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 1);
-        else if (by == 2) k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 2);
-        else k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 3);
-        acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(v2h, qv), k2, acc, false);
-      } else {
-        v2bf k2;
-        if (by == 0) k2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 0);
-        else if (by == 1) k2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 1);
-        else if (by == 2) k2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 2);
-        else k2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(u, 1.0f, 3);
-        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, qv), k2, acc, false);
-      }
-    }
-  }
-  return acc;
-}
-
-template <int RG, bool F16>
-__global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(DecodeArgs a) {
-  __shared__ float sh_o[4][RG][DK];
-  __shared__ float sh_m[4][RG], sh_l[4][RG];
+__global__ __launch_bounds__(DEC_THREADS, 2) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t vl[VLDS];   // V codes + scales; later the merge
+  __shared__ float sh_m[4][16], sh_l[4][16];
   const int64_t id = blockIdx.x;
   const int64_t rg = id % a.nrg, split = (id / a.nrg) % a.nsplit, bkv = id / a.nrg / a.nsplit;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, t = lane >> 3, g = lane & 7;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r = lane & 15, h = lane >> 4;
   const int64_t G = a.Hq / a.Hkv, b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   constexpr float NEG = -__builtin_inff();
+  using OpT = decltype(pack8<F16>((const float*)nullptr));
 
-  // this lane's 16 channels of each row, as the input's 16-bit pairs
-  uint32_t q[RG][8];
-  int qpos[RG];
-#pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    const int64_t row = rg * RG + r;
-    const bool act = row < a.R;
-    const int64_t rr = act ? row : 0;   // rows past R compute on row 0 and are dropped
+  // Q^T operand: row r of the group, channels 32h + 8kk .. +7 for kk = 0..3 (rows past R: zero)
+  const int64_t row = rg * 16 + r;
+  const bool act = row < a.R;
+  int qpos = -1;   // the last visible key of this row (-1: none)
+  OpT qb[4];
+  {
+    const int64_t rr = act ? row : 0;
     const int64_t hq = kvh * G + rr / a.Nq, i = rr % a.Nq;
-    qpos[r] = act ? (int)(a.Nk - a.Nq + i) : -1;   // -1: no key is visible
-    const uint16_t* qp = a.q + ((b * a.Hq + hq) * a.Nq + i) * DK + g * 16;
-    const v4i w0 = *(const v4i*)qp, w1 = *(const v4i*)(qp + 8);
+    if (act) qpos = (int)(a.Nk - a.Nq + i);
+    const uint16_t* qp = a.q + ((b * a.Hq + hq) * a.Nq + i) * DK + 32 * h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      q[r][e] = (uint32_t)w0[e];
-      q[r][4 + e] = (uint32_t)w1[e];
+    for (int kk = 0; kk < 4; ++kk) {
+      const v4i w = act ? *(const v4i*)(qp + 8 * kk) : v4i{0, 0, 0, 0};
+      qb[kk] = __builtin_bit_cast(OpT, w);
     }
   }
-  float m[RG], l[RG], o[RG][16];
+  float m = NEG, lpart = 0.0f;
+  v4f o[8];
 #pragma unroll
-  for (int r = 0; r < RG; ++r) {
-    m[r] = NEG;
-    l[r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) o[r][c] = 0.0f;
-  }
+  for (int cb = 0; cb < 8; ++cb) o[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // 32-bit offsets from the (b, KV head)'s cache; keys past the cache read the last key (their
-  // scores are masked), so no load needs a guard
   const int Nk = (int)a.Nk, j0 = (int)(split * DEC_CHUNK);
+  const uint32_t hNp = (uint32_t)(a.Np / 2);
   const uint8_t* kc = a.kc + bkv * a.Nk * 64;
-  const uint8_t* vc = a.vc + bkv * a.Nk * 64;
   const uint8_t* ks = a.ks + bkv * a.Nk * 8;
-  const uint8_t* vs = a.vs + bkv * a.Nk * 8;
+  const uint8_t* vc = a.vc + bkv * DK * (a.Np / 2);
+  const uint8_t* vs = a.vs + bkv * (a.Np / 16) * DK;
   const bool causal = a.causal != 0;
   const float qs = a.qscale;
-  struct Step {
-    v2i kc, vc;
-    uint32_t ks, vs;
+  // this wave's tile it starts at key j0 + 256 wv + 16 it; K rows past the cache are clamped
+  // (their keys are masked)
+  auto load = [&](int it, Tile& T) __attribute__((always_inline)) {
+    const int key0 = j0 + 256 * wv + 16 * it;
+    const uint32_t jk = (uint32_t)(key0 + r < Nk ? key0 + r : Nk - 1);
+    T.kw = *(const v4i*)(kc + jk * 64u + 16u * (uint32_t)h);
+    T.ks2 = *(const uint16_t*)(ks + jk * 8u + 2u * (uint32_t)h);
   };
-  auto load = [&](int j, Step& s) __attribute__((always_inline)) {
-    const uint32_t jc = (uint32_t)(j < Nk ? j : Nk - 1);
-    s.kc = *(const v2i*)(kc + jc * 64u + (uint32_t)g * 8u);
-    s.vc = *(const v2i*)(vc + jc * 64u + (uint32_t)g * 8u);
-    s.ks = ks[jc * 8u + (uint32_t)g];
-    s.vs = vs[jc * 8u + (uint32_t)g];
-  };
-  // steps of 32 keys; a ring of DEPTH steps of codes (18 bytes a lane each) is in flight, each
-  // loaded DEPTH steps before its arithmetic
-  constexpr int STEPS = DEC_CHUNK / 32, DEPTH = 8;
-  static_assert(STEPS % DEPTH == 0, "whole rounds of the ring");
-  const int jl = j0 + wv * 8 + t;   // this lane's key in step 0
-  Step ring[DEPTH];
+  constexpr int TILES = DEC_CHUNK / 64, DEPTH = 8;   // 16 tiles of 16 keys per wave
+  static_assert(TILES % DEPTH == 0, "whole rounds of the ring");
+  Tile ring[DEPTH];   // the first tiles' K loads go out before V's
 #pragma unroll
-  for (int u = 0; u < DEPTH; ++u) load(jl + 32 * u, ring[u]);
-  for (int st0 = 0; st0 < STEPS; st0 += DEPTH) {
+  for (int u = 0; u < DEPTH; ++u) load(u, ring[u]);
+  // V of the chunk into LDS: codes row c = bytes j0/2 .. j0/2 + 511 of channel c; scales of
+  // the chunk's 64 token groups (past the padded cache: zeros, never used)
+  {   // every load is issued before the first LDS write: one round trip, 18 x 16 bytes a thread
+    constexpr int NC = DK * (DEC_CHUNK / 32) / DEC_THREADS;        // 16 code segments a thread
+    constexpr int NS = (DEC_CHUNK / 16) * (DK / 16) / DEC_THREADS;  // 2 scale segments a thread
+    const uint32_t cb0 = (uint32_t)j0 / 2u, nb = (uint32_t)hNp;      // code bytes of a channel row
+    const uint32_t g0 = (uint32_t)j0 / 16u, ng = (uint32_t)(a.Np / 16);
+    v4i wc[NC], ws[NS];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
+      const uint32_t c = idx / (DEC_CHUNK / 32), seg = idx % (DEC_CHUNK / 32), at = cb0 + 16u * seg;
+      wc[u] = at < nb ? *(const v4i*)(vc + c * nb + at) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
+      const uint32_t gi = idx / (DK / 16), cs = idx % (DK / 16);
+      ws[u] = g0 + gi < ng ? *(const v4i*)(vs + (g0 + gi) * DK + 16u * cs) : v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
+      *(v4i*)(vl + (idx / (DEC_CHUNK / 32)) * VROW + 16u * (idx % (DEC_CHUNK / 32))) = wc[u];
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
+      *(v4i*)(vl + VSC0 + (idx / (DK / 16)) * DK + 16u * (idx % (DK / 16))) = ws[u];
+    }
+  }
+  __syncthreads();   // V is in LDS
+  for (int it0 = 0; it0 < TILES; it0 += DEPTH) {
 #pragma unroll
     for (int u = 0; u < DEPTH; ++u) {
-      const int j = jl + 32 * (st0 + u);
-      const Step cur = ring[u];
-      if (st0 + DEPTH < STEPS) load(j + 32 * DEPTH, ring[u]);   // wave-uniform
-      const float sk = e4m3_to_f32(cur.ks) * qs;
-      float s[RG];
+      const int it = it0 + u;
+      const Tile T = ring[u];
+      if (it + DEPTH < TILES) load(it + DEPTH, ring[u]);   // wave-uniform
+      const int kl0 = 256 * wv + 16 * it;                  // the tile's first key within the chunk
+      const int key0 = j0 + kl0;
+      // S^T = K Q^T over the 4 channel slices
+      v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+      const float s0 = ue4m3(T.ks2 & 0xffu), s1 = ue4m3((T.ks2 >> 8) & 0xffu);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        float x[8];
+        e2m1x8((uint32_t)T.kw[kk], kk < 2 ? s0 : s1, x);
+        if constexpr (F16) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pack8<true>(x), qb[kk], acc, 0, 0, 0);
+        else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8<false>(x), qb[kk], acc, 0, 0, 0);
+      }
+      // row r's scores of keys key0 + 4h + e, in log2 units; masked keys -inf
+      float p[4];
       bool up = false;
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        float acc = dot16<F16>(q[r], cur.kc) * sk;
-        acc += lane_xor<1>(acc);   // sum over the key's 8 lanes: every lane gets the same value
-        acc += lane_xor<2>(acc);
-        acc += lane_xor<4>(acc);
-        const bool vis = j < Nk && (causal ? j <= qpos[r] : qpos[r] >= 0);
-        s[r] = vis ? acc : NEG;
-        up |= s[r] > m[r] + kLazy;   // also the first visible key (m = -inf)
+      for (int e = 0; e < 4; ++e) {
+        const int j = key0 + 4 * h + e;
+        const bool vis = j < Nk && (causal ? j <= qpos : qpos >= 0);
+        p[e] = vis ? acc[e] * qs : NEG;
+        up |= p[e] > m + kLazy;   // also the first visible key (m = -inf)
       }
       if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform: move the running max
+        float tmax = __builtin_fmaxf(__builtin_fmaxf(p[0], p[1]), __builtin_fmaxf(p[2], p[3]));
+        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));   // the row's 16 keys sit in lanes r + 16h
+        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+        if (tmax > m + kLazy) {
+          const float alpha = m == NEG ? 0.0f : __builtin_amdgcn_exp2f(m - tmax);
+          lpart *= alpha;
 #pragma unroll
-        for (int r = 0; r < RG; ++r) {
-          const bool mv = s[r] > m[r] + kLazy;
-          const float alpha = !mv ? 1.0f : (m[r] == NEG ? 0.0f : __builtin_amdgcn_exp2f(m[r] - s[r]));
-          l[r] *= alpha;
-#pragma unroll
-          for (int c = 0; c < 16; ++c) o[r][c] *= alpha;
-          m[r] = mv ? s[r] : m[r];
+          for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
+          m = tmax;
         }
       }
-      float x[16];
-      e2m1x16(cur.vc, x);
-      const float vsc = e4m3_to_f32(cur.vs);
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        const float pr = s[r] == NEG ? 0.0f : __builtin_amdgcn_exp2f(s[r] - m[r]);   // m may still be -inf
-        l[r] += pr;
-        const float ps = pr * vsc;
+      for (int e = 0; e < 4; ++e) {
+        p[e] = p[e] == NEG ? 0.0f : __builtin_amdgcn_exp2f(p[e] - m);   // m may still be -inf
+        lpart += p[e];
+      }
+      const v4h pb = v4h{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+      // O^T += V^T P^T over the 8 channel blocks; V codes of channel 16 cb + r, tokens 4h..4h+3
+      const uint32_t vo = (uint32_t)kl0 / 2u + 2u * (uint32_t)h, so = VSC0 + ((uint32_t)kl0 / 16u) * DK;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) o[r][c] = __builtin_fmaf(ps, x[c], o[r][c]);
+      for (int cb = 0; cb < 8; ++cb) {
+        const uint32_t ch = 16u * (uint32_t)cb + (uint32_t)r;
+        const uint32_t vw = *(const uint16_t*)(vl + ch * VROW + vo);
+        const _Float16 vsc = (_Float16)ue4m3(vl[so + ch]);   // exact in f16
+        const v2h sc2 = v2h{vsc, vsc};
+        const v2h d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 0) * sc2;   // exact: E2M1 x UE4M3
+        const v2h d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 1) * sc2;
+        const v4h va = v4h{d0[0], d0[1], d1[0], d1[1]};
+        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[cb], 0, 0, 0);
       }
     }
   }
-
-  // merge the wave's 8 key slots (lanes that differ in bits 3..5 hold the same channels);
-  // both lanes of a pair form the same two products and add them, so they stay equal
+  // this wave's row sums: row r's keys sit in lanes r + 16h
+  float lrow = lpart + __shfl_xor(lpart, 16);
+  lrow += __shfl_xor(lrow, 32);
+  // O^T: lane (r, h) holds row r, channels 16 cb + 4h + e; the V area becomes [4][16][128] floats
+  __syncthreads();   // every wave is done with V
+  float(*sh_o)[16][DK] = reinterpret_cast<float(*)[16][DK]>(vl);
 #pragma unroll
-  for (int mask = 8; mask < 64; mask *= 2)
+  for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-    for (int r = 0; r < RG; ++r) {
-      const float mo = __shfl_xor(m[r], mask), lo = __shfl_xor(l[r], mask);
-      const float M = __builtin_fmaxf(m[r], mo);
-      const float wa = M == NEG ? 0.0f : __builtin_amdgcn_exp2f(m[r] - M);
-      const float wb = M == NEG ? 0.0f : __builtin_amdgcn_exp2f(mo - M);
-      l[r] = l[r] * wa + lo * wb;
-#pragma unroll
-      for (int c = 0; c < 16; ++c) o[r][c] = o[r][c] * wa + __shfl_xor(o[r][c], mask) * wb;
-      m[r] = M;
-    }
-  if (t == 0) {
-#pragma unroll
-    for (int r = 0; r < RG; ++r) {
-#pragma unroll
-      for (int c = 0; c < 16; ++c) sh_o[wv][r][g * 16 + c] = o[r][c];
-      if (g == 0) {
-        sh_m[wv][r] = m[r];
-        sh_l[wv][r] = l[r];
-      }
-    }
+    for (int e = 0; e < 4; ++e) sh_o[wv][r][16 * cb + 4 * h + e] = o[cb][e];
+  if (h == 0) {
+    sh_m[wv][r] = m;
+    sh_l[wv][r] = lrow;
   }
   __syncthreads();
   // merge the 4 waves; write this split's unnormalized O with its max and sum
-  const int64_t Rp = a.nrg * RG;
-  for (int i = threadIdx.x; i < RG * DK; i += DEC_THREADS) {
-    const int r = i / DK, c = i % DK;
-    float M = sh_m[0][r];
+  for (int i = threadIdx.x; i < 16 * DK; i += DEC_THREADS) {
+    const int rr = i / DK, c = i % DK;
+    float M = sh_m[0][rr];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, sh_m[w][r]);
-    float acc = 0.0f, L = 0.0f;
+    for (int w = 1; w < 4; ++w) M = __builtin_fmaxf(M, sh_m[w][rr]);
+    float accv = 0.0f, L = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float wt = M == NEG ? 0.0f : __builtin_amdgcn_exp2f(sh_m[w][r] - M);
-      acc += sh_o[w][r][c] * wt;
-      L += sh_l[w][r] * wt;
+      const float wt = M == NEG ? 0.0f : __builtin_amdgcn_exp2f(sh_m[w][rr] - M);
+      accv += sh_o[w][rr][c] * wt;
+      L += sh_l[w][rr] * wt;
     }
-    const int64_t prow = (bkv * a.nsplit + split) * Rp + rg * RG + r;
-    a.part_o[prow * DK + c] = acc;
+    const int64_t grow = rg * 16 + rr;   // the row within the KV head's R rows
+    if (grow >= a.R) continue;
+    const int64_t prow = (bkv * a.nsplit + split) * a.R + grow;
+    a.part_o[prow * DK + c] = accv;
     if (c == 0) {
       a.part_ml[prow * 2] = M;
       a.part_ml[prow * 2 + 1] = L;
@@ -253,14 +283,14 @@ __global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(DecodeArgs a)
 // weights are formed once in LDS (splits beyond 1024 are folded in by a loop).
 __global__ __launch_bounds__(DK) void decode_combine_kernel(const float* __restrict__ part_o,
                                                             const float* __restrict__ part_ml, int64_t Hq,
-                                                            int64_t Hkv, int64_t Nq, int64_t R, int64_t Rp,
+                                                            int64_t Hkv, int64_t Nq, int64_t R,
                                                             int64_t nsplit, int out_bf16, void* out) {
   __shared__ float wt[1024];
   __shared__ float red[2];
   const int64_t row = blockIdx.x % R, bkv = blockIdx.x / R;
   const int c = threadIdx.x;
   constexpr float NEG = -__builtin_inff();
-  auto ml = [&](int64_t s, int k) { return part_ml[((bkv * nsplit + s) * Rp + row) * 2 + k]; };
+  auto ml = [&](int64_t s, int k) { return part_ml[((bkv * nsplit + s) * R + row) * 2 + k]; };
   float M = NEG;
   for (int64_t s = c; s < nsplit; s += DK) M = __builtin_fmaxf(M, ml(s, 0));
   M = wave_max(M);
@@ -278,11 +308,11 @@ __global__ __launch_bounds__(DK) void decode_combine_kernel(const float* __restr
     for (; s + 8 <= n; s += 8) {   // eight independent loads in flight
       float v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part_o[((bkv * nsplit + s0 + s + u) * Rp + row) * DK + c];
+      for (int u = 0; u < 8; ++u) v[u] = part_o[((bkv * nsplit + s0 + s + u) * R + row) * DK + c];
 #pragma unroll
       for (int u = 0; u < 8; ++u) num += v[u] * wt[s + u];
     }
-    for (; s < n; ++s) num += part_o[((bkv * nsplit + s0 + s) * Rp + row) * DK + c] * wt[s];
+    for (; s < n; ++s) num += part_o[((bkv * nsplit + s0 + s) * R + row) * DK + c] * wt[s];
   }
   const int64_t G = Hq / Hkv, b = bkv / Hkv, hq = (bkv % Hkv) * G + row / Nq, qi = row % Nq;
   const int64_t at = ((b * Hq + hq) * Nq + qi) * DK + c;
@@ -291,40 +321,32 @@ __global__ __launch_bounds__(DK) void decode_combine_kernel(const float* __restr
   else ((float*)out)[at] = v;
 }
 
-int64_t decode_rg(int64_t R) { return R >= 4 ? 4 : (R == 1 ? 1 : (R == 2 ? 2 : 4)); }
-
 }  // namespace
 
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk) {
-  const int64_t R = (Hq / Hkv) * Nq, RG = decode_rg(R), Rp = (R + RG - 1) / RG * RG;
+  const int64_t R = (Hq / Hkv) * Nq;
   const int64_t nsplit = (Nk + DEC_CHUNK - 1) / DEC_CHUNK;
-  return (size_t)(B * Hkv * nsplit * Rp) * (DK + 2) * sizeof(float);
+  return (size_t)(B * Hkv * nsplit * R) * (DK + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
                          const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int causal,
                          float sm_scale, void* out, bool out_bf16, void* ws, hipStream_t st) {
-  const int64_t R = (Hq / Hkv) * Nq, RG = decode_rg(R), nrg = (R + RG - 1) / RG, Rp = nrg * RG;
+  const int64_t R = (Hq / Hkv) * Nq, nrg = (R + 15) / 16;
   const int64_t nsplit = (Nk + DEC_CHUNK - 1) / DEC_CHUNK;
   DecodeArgs a;
   a.q = q;
   a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.part_o = (float*)ws;
-  a.part_ml = (float*)ws + B * Hkv * nsplit * Rp * DK;
-  a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.nsplit = nsplit; a.R = R; a.nrg = nrg;
-  a.q_f16 = q_f16 ? 1 : 0;
+  a.part_ml = (float*)ws + B * Hkv * nsplit * R * DK;
+  a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.Np = (Nk + 63) / 64 * 64;
+  a.nsplit = nsplit; a.R = R; a.nrg = nrg;
   a.causal = causal;
   a.qscale = (float)((double)sm_scale * 1.4426950408889634);
   const int64_t nwg = B * Hkv * nsplit * nrg;
-  auto go = [&](auto rgc, auto f16c) {
-    decode_split_kernel<decltype(rgc)::value, decltype(f16c)::value><<<(unsigned)nwg, DEC_THREADS, 0, st>>>(a);
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  if (RG == 4) { if (q_f16) go(std::integral_constant<int, 4>{}, T_{}); else go(std::integral_constant<int, 4>{}, F_{}); }
-  else if (RG == 2) { if (q_f16) go(std::integral_constant<int, 2>{}, T_{}); else go(std::integral_constant<int, 2>{}, F_{}); }
-  else { if (q_f16) go(std::integral_constant<int, 1>{}, T_{}); else go(std::integral_constant<int, 1>{}, F_{}); }
-  decode_combine_kernel<<<(unsigned)(B * Hkv * R), DK, 0, st>>>(a.part_o, a.part_ml, Hq, Hkv, Nq, R, Rp, nsplit,
+  if (q_f16) decode_split_kernel<true><<<(unsigned)nwg, DEC_THREADS, 0, st>>>(a);
+  else decode_split_kernel<false><<<(unsigned)nwg, DEC_THREADS, 0, st>>>(a);
+  decode_combine_kernel<<<(unsigned)(B * Hkv * R), DK, 0, st>>>(a.part_o, a.part_ml, Hq, Hkv, Nq, R, nsplit,
                                                                  out_bf16 ? 1 : 0, out);
   return hipGetLastError();
 }

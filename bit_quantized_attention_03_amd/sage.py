@@ -227,7 +227,8 @@ def sink_select(q: torch.Tensor, n_first: int, n_last: int, causal: bool,
 
 def decode(q: torch.Tensor, k: QT, v: QT, causal: bool = False, sm_scale: float = 0.0,
            out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """Nq new rows q [B,Hq,Nq,D] against an NVFP4 KV cache (k, v from quantize(x, NVFP4, (1, 16), ...))."""
+    """Nq new rows q [B,Hq,Nq,D] against an NVFP4 KV cache: k from quantize(K, NVFP4, (1, 16), ...)
+    (rows along D), v from quantize(V, NVFP4, (16, 1), ...) (along the tokens)."""
     _dev(q)
     B, Hq, Nq, D = q.shape
     out = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q.device)

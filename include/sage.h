@@ -206,11 +206,14 @@ size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_b
  * (Method > ScaleSearchAttention: the KV cache stored in 4 bits).  Nq new query rows attend to
  * a cache of Nk keys; query i stands at position Nk - Nq + i, and with causal = 1 it sees keys
  * j <= Nk - Nq + i (else all Nk).  out = softmax(q K^T sm_scale) V, with K and V the cache's
- * NVFP4 values (E2M1 x UE4M3), computed in fp32 (P is not quantized); sm_scale 0 selects
- * 1 / sqrt(D).  q-head h reads KV head h / (Hq / Hkv).
+ * NVFP4 values (E2M1 x UE4M3): scores fp32, P rounded to f16 for P.V with fp32 accumulation,
+ * the softmax sum of the unrounded P; sm_scale 0 selects 1 / sqrt(D).  q-head h reads KV
+ * head h / (Hq / Hkv).
  *   q   [B,Hq,Nq,D] in q_dt (SAGE_BF16 | SAGE_FP16), 16-byte aligned;
- *   k,v SAGE_NVFP4 along D, shape [B,Hkv,Nk,D]: codes [B,Hkv,Nk,D/2] (16-byte aligned),
- *       UE4M3 scales [B,Hkv,Nk,D/16] (sage_quantize_blocks with block (1, 16));
+ *   k   SAGE_NVFP4 along D, shape [B,Hkv,Nk,D]: codes [B,Hkv,Nk,D/2] (16-byte aligned), UE4M3
+ *       scales [B,Hkv,Nk,D/16] (2-byte aligned) (sage_quantize_blocks with block (1, 16));
+ *   v   SAGE_NVFP4 along the tokens, shape [B,Hkv,Nk,D]: codes [B,Hkv,D,Np/2], Np = Nk rounded
+ *       up to 64 (16-byte aligned), UE4M3 scales [B,Hkv,Np/16,D] (block (16, 1));
  *   out [B,Hq,Nq,D] in out_dt (SAGE_FP32 | SAGE_BF16);
  *   workspace >= sage_decode_workspace_bytes(q shape, k shape) bytes of device memory
  *   (partial results of the key splits).

@@ -235,17 +235,29 @@ def nvfp4_rows_value(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return vals * np.repeat(e4m3_decode(scales), 16, axis=-1)
 
 
+def nvfp4_tokens_value(codes: np.ndarray, scales: np.ndarray, N: int) -> np.ndarray:
+    """fp64 values [..., N, D] of NVFP4 along the tokens: codes [..., D, Np/2] (channel rows,
+    token pairs, even token in the low nibble), UE4M3 scales [..., Np/16, D] (one per channel
+    and 16-token group); Np = N rounded up to 64."""
+    codes = np.asarray(codes, np.uint8); scales = np.asarray(scales, np.uint8)
+    lo = e2m1_decode(codes & 15); hi = e2m1_decode(codes >> 4)
+    vals = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)   # [..., D, Np]
+    s = np.repeat(e4m3_decode(scales), 16, axis=-2)                                        # [..., Np, D]
+    return (np.swapaxes(vals, -1, -2) * s)[..., :N, :]
+
+
 def decode_attention(q16: np.ndarray, dt: int, k_codes, k_scales, v_codes, v_scales, causal: bool,
                      sm_scale: float) -> np.ndarray:
     """Decode-shaped attention on a KV cache held in NVFP4 ("Search Your Block Floating Point
     Scales!", Method › ScaleSearchAttention: the KV cache stored in 4 bits).  q [B,Hq,Nq,D]
-    16-bit; K and V as NVFP4 rows along D, [B,Hkv,Nk,D/2] codes and [B,Hkv,Nk,D/16] scales.
+    16-bit; K as NVFP4 rows along D ([B,Hkv,Nk,D/2] codes, [B,Hkv,Nk,D/16] scales), V as NVFP4
+    along the tokens ([B,Hkv,D,Np/2] codes, [B,Hkv,Np/16,D] scales, Np = Nk rounded up to 64).
     Query i stands at position Nk - Nq + i (the newest tokens); with causal masking it sees
     keys j <= Nk - Nq + i.  Textbook fp64 softmax(q K^T sm_scale) V on the cache's values;
     q-head h reads KV head h // (Hq / Hkv)."""
     q = decode16(np.asarray(q16, np.uint16), dt).astype(np.float64)
     K = nvfp4_rows_value(k_codes, k_scales)
-    V = nvfp4_rows_value(v_codes, v_scales)
+    V = nvfp4_tokens_value(v_codes, v_scales, K.shape[2])
     B, Hq, Nq, D = q.shape
     Hkv, Nk = K.shape[1], K.shape[2]
     G = Hq // Hkv

@@ -83,11 +83,11 @@ def test_decode_full_size_sampled():
     print("[case] full size decode_nvfp4", flush=True)
     q, k, v = I.make_qkv(w, seed=0)
     kq = sage.quantize(k.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
-    vq = sage.quantize(v.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
+    vq = sage.quantize(v.cuda(), sage.NVFP4, (16, 1), sage.SEARCH)
     out = sage.decode(q.cuda(), kq, vq, False).cpu().numpy()
-    cshape, sshape = (w.B, w.Hkv, w.N, 64), (w.B, w.Hkv, w.N, 8)
-    kc, ks = u8(kq.codes).reshape(cshape), u8(kq.scales).reshape(sshape)
-    vc, vs = u8(vq.codes).reshape(cshape), u8(vq.scales).reshape(sshape)
+    Np = (w.N + 63) // 64 * 64
+    kc, ks = u8(kq.codes).reshape(w.B, w.Hkv, w.N, 64), u8(kq.scales).reshape(w.B, w.Hkv, w.N, 8)
+    vc, vs = u8(vq.codes).reshape(w.B, w.Hkv, 128, Np // 2), u8(vq.scales).reshape(w.B, w.Hkv, Np // 16, 128)
     for b in (0, w.B - 1):
         sl = slice(b, b + 1)
         want = oracle.decode_attention(I.bits16(q[sl]), 0, kc[sl], ks[sl], vc[sl], vs[sl], False, 1.0 / math.sqrt(128))

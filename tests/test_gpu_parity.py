@@ -277,12 +277,13 @@ def test_sink_mask_bit_exact(N, causal):
 
 # ------------------------------------------------------------------------------ decode
 DEC_CASES = [   # (B, Hq, Hkv, Nq, Nk, causal): rows per KV head R = (Hq / Hkv) * Nq
-    (1, 4, 2, 3, 1000, True),      # R = 6: two row groups, the second half empty
+    (1, 4, 2, 3, 1000, True),      # R = 6 of a 16-row group
     (2, 8, 2, 1, 4500, False),     # GQA 4:1, R = 4; nine key splits, the last ragged
     (1, 2, 2, 1, 100, False),      # R = 1; one short split
     (1, 6, 2, 1, 513, True),       # R = 3; a split of one key
     (1, 4, 4, 5, 1100, True),      # MHA with 5 new tokens
-    (1, 4, 2, 64, 700, True),      # 64 new tokens
+    (1, 4, 2, 64, 700, True),      # 64 new tokens: R = 128, eight row groups
+    (1, 16, 2, 2, 2100, True),     # R = 16: one full row group
 ]
 
 
@@ -297,12 +298,12 @@ def test_decode_parity(B, Hq, Hkv, Nq, Nk, causal):
     print(f"[case] decode B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}", flush=True)
     q, k, v = _decode_inputs(B, Hq, Hkv, Nq, Nk)
     kq = sage.quantize(k.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
-    vq = sage.quantize(v.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
+    vq = sage.quantize(v.cuda(), sage.NVFP4, (16, 1), sage.SEARCH)
     out = sage.decode(q.cuda(), kq, vq, causal).cpu().numpy()
-    cshape, sshape = (B, Hkv, Nk, 64), (B, Hkv, Nk, 8)
-    want = oracle.decode_attention(np16(q), 0, u8(kq.codes).reshape(cshape), u8(kq.scales).reshape(sshape),
-                                   u8(vq.codes).reshape(cshape), u8(vq.scales).reshape(sshape), causal,
-                                   1.0 / math.sqrt(128))
+    Np = (Nk + 63) // 64 * 64
+    want = oracle.decode_attention(np16(q), 0, u8(kq.codes).reshape(B, Hkv, Nk, 64),
+                                   u8(kq.scales).reshape(B, Hkv, Nk, 8), u8(vq.codes).reshape(B, Hkv, 128, Np // 2),
+                                   u8(vq.scales).reshape(B, Hkv, Np // 16, 128), causal, 1.0 / math.sqrt(128))
     rel, cos = check_out(out, want, f"decode {B} {Hq} {Hkv} {Nq} {Nk} causal={causal}")
     print(f"  rel_err_vs_oracle={rel:.2e} cos={cos:.7f}")
 
@@ -311,7 +312,7 @@ def test_decode_bf16_output_and_fp16_query():
     sage = _sage()
     q, k, v = _decode_inputs(1, 8, 2, 2, 777, seed=3)
     kq = sage.quantize(k.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
-    vq = sage.quantize(v.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
+    vq = sage.quantize(v.cuda(), sage.NVFP4, (16, 1), sage.SEARCH)
     a = sage.decode(q.cuda(), kq, vq, True).cpu()
     b = sage.decode(q.cuda(), kq, vq, True, out_dtype=torch.bfloat16).cpu().float()
     assert torch.all((a - b).abs() <= a.abs() * 2.0 ** -8 + 1e-30)
