@@ -7,23 +7,23 @@
 //
 // The work is reading the cache (144 bytes per key per KV head at d = 128).  Both products
 // run on the matrix cores, so the vector work per key does not grow with the query rows:
-//   * a workgroup takes 1024 keys of one (b, KV head) for 16 query rows (the q-heads of the
-//     KV head's group times the new tokens); each of its 4 waves walks its own 16-key tiles
-//     with its own running max and sum, merged at the end (log-sum-exp);
-//   * S^T (16 keys x 16 rows) = K Q^T on v_mfma_f32_16x16x32_{bf16,f16}: lane (r, h) of the
-//     A operand holds key r's 32 channels 32h..32h+31, dequantized in registers from one
-//     16-byte load (E2M1 x UE4M3 is exact in bf16 and f16); Q^T is the B operand with the
-//     same channel order, loaded once;
+//   * a workgroup takes 512 keys of one (b, KV head) for 16 query rows (the q-heads of the
+//     KV head's group times the new tokens); each of its 4 waves walks its own 128 keys in
+//     16-key tiles with its own running max and sum, merged at the end (log-sum-exp);
+//   * S^T (16 keys x 16 rows) = K Q^T on v_mfma_f32_16x16x32_f16: lane (r, h) of the A
+//     operand holds key r's 32 channels 32h..32h+31, dequantized in registers from one 16-byte
+//     load (E2M1 pairs to f16 times the scale pair: exact); Q^T is the B operand with the same
+//     channel order, loaded once (a bf16 row scaled by a power of two into f16's range: exact);
 //   * the accumulator leaves lane (r, h) with row r's scores of keys 4h..4h+3: exactly the
 //     B operand P^T of O^T (channels x rows) += V^T P^T on v_mfma_f32_16x16x16_f16, whose A
 //     operand V^T needs 4 consecutive tokens of one channel: 2 bytes of the along-token codes;
 //     f16 keeps 11 bits of P (bf16's 8 would cost about 1e-3 of max|O|);
 //   * the running max moves only when a score passes it by 15 (log2 units), checked once per
 //     tile for the whole wave; P <= 2^15 stays finite in f16;
-//   * the workgroup's V codes and scales (1024 tokens x 128 channels) are copied to LDS with
-//     16-byte loads first (channel rows padded to 528 bytes, so the 16 channel lanes of a read
-//     hit distinct banks); each wave then walks its own 256 keys, reading K through a ring of
-//     8 tiles in flight (issued before V's loads) and V's 2-byte pieces from LDS;
+//   * the workgroup's V codes and scales (512 tokens x 128 channels) go to LDS by direct
+//     global->LDS loads (channel rows padded to 272 bytes, so the 16 channel lanes of a read
+//     hit distinct banks), after each wave's K loads for all its 8 tiles; V's 2-byte pieces are
+//     then read from LDS;
 //   * a split writes only the R real rows of its partial O (not the 16 of the row group).
 // decode_combine_kernel merges the splits and writes O.
 #include "device.hpp"
@@ -33,7 +33,7 @@ namespace sage {
 namespace {
 
 constexpr int DK = 128;             // head dimension
-constexpr int DEC_CHUNK = 1024;     // keys per split workgroup
+constexpr int DEC_CHUNK = 512;      // keys per split workgroup
 constexpr int DEC_THREADS = 256;    // 4 waves x 8 key slots
 constexpr float kLazy = 15.0f;      // headroom of the running max, log2 units (P <= 2^15 fits f16)
 
@@ -51,37 +51,11 @@ struct DecodeArgs {
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
-// eight fp32 values -> the MFMA operand type (bf16 or f16; exact for E2M1 x UE4M3 values)
-template <bool F16>
-__device__ __forceinline__ auto pack8(const float* x) {
-  if constexpr (F16) {
-    v8h r;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r[e] = (_Float16)x[e];
-    return r;
-  } else {
-    v4i w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = (int)pack_bf16x2(x[2 * e], x[2 * e + 1]);
-    return __builtin_bit_cast(v8bf, w);
-  }
-}
-
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 // A UE4M3 scale byte's value: gfx950's E4M3 conversion (OCP E4M3, the format the quantizers
 // encode with; exact).
 __device__ __forceinline__ float ue4m3(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
-
-// the 8 E2M1 values of 4 code bytes (element e = 2 * byte + nibble), times s
-__device__ __forceinline__ void e2m1x8(uint32_t u, float s, float* x) {
-  const auto d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 0);
-  const auto d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 1);
-  const auto d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 2);
-  const auto d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(u, 1.0f, 3);
-  x[0] = d0[0] * s; x[1] = d0[1] * s; x[2] = d1[0] * s; x[3] = d1[1] * s;
-  x[4] = d2[0] * s; x[5] = d2[1] * s; x[6] = d3[0] * s; x[7] = d3[1] * s;
-}
 
 struct Tile {
   v4i kw;          // key (key0 + r)'s code bytes 16h..16h+15
@@ -89,12 +63,13 @@ struct Tile {
 };
 
 constexpr int VROW = DEC_CHUNK / 2 + 16;            // LDS bytes of a channel's codes (padded)
-constexpr int VSC0 = DK * VROW;                      // LDS offset of the scales [64 groups][128]
-constexpr int VLDS = VSC0 + (DEC_CHUNK / 16) * DK;   // 75776 bytes
+constexpr int VSC0 = DK * VROW;                      // LDS offset of the scales [32 groups][128]
+constexpr int VLDS = VSC0 + (DEC_CHUNK / 16) * DK;   // 38912 bytes
+typedef __attribute__((address_space(3))) void lds_void;
 
-// Two workgroups a CU (their LDS allows no more): the register budget is 256 per lane.
+// Up to four workgroups a CU (39 KB of LDS each): a register budget of 128 per lane.
 template <bool F16>
-__global__ __launch_bounds__(DEC_THREADS, 2) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vl[VLDS];   // V codes + scales; later the merge
   __shared__ float sh_m[4][16], sh_l[4][16];
   const int64_t id = blockIdx.x;
@@ -102,22 +77,48 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_split_kernel(DecodeArgs
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, r = lane & 15, h = lane >> 4;
   const int64_t G = a.Hq / a.Hkv, b = bkv / a.Hkv, kvh = bkv % a.Hkv;
   constexpr float NEG = -__builtin_inff();
-  using OpT = decltype(pack8<F16>((const float*)nullptr));
 
-  // Q^T operand: row r of the group, channels 32h + 8kk .. +7 for kk = 0..3 (rows past R: zero)
+  // Q^T operand in f16: row r of the group, channels 32h + 8kk .. +7 for kk = 0..3 (rows past
+  // R: zero).  A bf16 row is first scaled by 2^-E, E >= 0 the least that brings its largest
+  // magnitude to 2^14 or below: every bf16 value then lands exactly in f16 (8 significant bits
+  // of 11; a component below 2^-14 of that scale would become an f16 subnormal, below 2^-28 of
+  // the row's largest term), and 2^E goes into the row's score scale.
   const int64_t row = rg * 16 + r;
   const bool act = row < a.R;
   int qpos = -1;   // the last visible key of this row (-1: none)
-  OpT qb[4];
+  v8h qb[4];
+  float qs = a.qscale;
   {
     const int64_t rr = act ? row : 0;
     const int64_t hq = kvh * G + rr / a.Nq, i = rr % a.Nq;
     if (act) qpos = (int)(a.Nk - a.Nq + i);
     const uint16_t* qp = a.q + ((b * a.Hq + hq) * a.Nq + i) * DK + 32 * h;
+    v4i w[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const v4i w = act ? *(const v4i*)(qp + 8 * kk) : v4i{0, 0, 0, 0};
-      qb[kk] = __builtin_bit_cast(OpT, w);
+    for (int kk = 0; kk < 4; ++kk) w[kk] = act ? *(const v4i*)(qp + 8 * kk) : v4i{0, 0, 0, 0};
+    if constexpr (F16) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qb[kk] = __builtin_bit_cast(v8h, w[kk]);
+    } else {
+      float x[4][8];
+      float mx = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[kk][e] = bf16_to_f32((uint16_t)((uint32_t)w[kk][e >> 1] >> (16 * (e & 1))));
+          mx = __builtin_fmaxf(mx, __builtin_fabsf(x[kk][e]));
+        }
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));   // the row's 128 channels sit in lanes r + 16h
+      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+      const int ex = (int)((__float_as_uint(mx) >> 23) & 255u) - 127;   // mx = 1.f * 2^ex (or 0)
+      const int E = ex > 14 ? ex - 14 : 0;
+      const float down = __builtin_ldexpf(1.0f, -E);
+      qs = qs * __builtin_ldexpf(1.0f, E);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qb[kk][e] = (_Float16)(x[kk][e] * down);
     }
   }
   float m = NEG, lpart = 0.0f;
@@ -132,51 +133,47 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_split_kernel(DecodeArgs
   const uint8_t* vc = a.vc + bkv * DK * (a.Np / 2);
   const uint8_t* vs = a.vs + bkv * (a.Np / 16) * DK;
   const bool causal = a.causal != 0;
-  const float qs = a.qscale;
-  // this wave's tile it starts at key j0 + 256 wv + 16 it; K rows past the cache are clamped
-  // (their keys are masked)
+  // this wave's tile it starts at key j0 + (DEC_CHUNK / 4) wv + 16 it; K rows past the cache
+  // are clamped (their keys are masked)
   auto load = [&](int it, Tile& T) __attribute__((always_inline)) {
-    const int key0 = j0 + 256 * wv + 16 * it;
+    const int key0 = j0 + (DEC_CHUNK / 4) * wv + 16 * it;
     const uint32_t jk = (uint32_t)(key0 + r < Nk ? key0 + r : Nk - 1);
     T.kw = *(const v4i*)(kc + jk * 64u + 16u * (uint32_t)h);
     T.ks2 = *(const uint16_t*)(ks + jk * 8u + 2u * (uint32_t)h);
   };
-  constexpr int TILES = DEC_CHUNK / 64, DEPTH = 8;   // 16 tiles of 16 keys per wave
+  constexpr int TILES = DEC_CHUNK / 64, DEPTH = 8;   // 8 tiles of 16 keys per wave: all in flight
   static_assert(TILES % DEPTH == 0, "whole rounds of the ring");
   Tile ring[DEPTH];   // the first tiles' K loads go out before V's
 #pragma unroll
   for (int u = 0; u < DEPTH; ++u) load(u, ring[u]);
-  // V of the chunk into LDS: codes row c = bytes j0/2 .. j0/2 + 511 of channel c; scales of
-  // the chunk's 64 token groups (past the padded cache: zeros, never used)
-  {   // every load is issued before the first LDS write: one round trip, 18 x 16 bytes a thread
-    constexpr int NC = DK * (DEC_CHUNK / 32) / DEC_THREADS;        // 16 code segments a thread
-    constexpr int NS = (DEC_CHUNK / 16) * (DK / 16) / DEC_THREADS;  // 2 scale segments a thread
+  // V of the chunk into LDS by direct global->LDS loads (no registers): a wave instruction
+  // fills 1 KB of LDS, lane i its 16-byte slot i, and each lane fetches the global segment that
+  // belongs to its slot.  Code slots: row c (channel) x 17 (16 segments of the chunk's
+  // DEC_CHUNK/2 bytes + one padding slot); then the scale slots: 32 token groups x 8 segments.
+  // Segments past the padded cache fetch the row's last valid one (finite codes and scales;
+  // their keys are masked), padding slots fetch segment 0.
+  {
+    constexpr int CODE_SLOTS = DK * (VROW / 16), SLOTS = CODE_SLOTS + (DEC_CHUNK / 16) * (DK / 16);
+    static_assert(SLOTS % 64 == 0, "whole wave instructions");
     const uint32_t cb0 = (uint32_t)j0 / 2u, nb = (uint32_t)hNp;      // code bytes of a channel row
     const uint32_t g0 = (uint32_t)j0 / 16u, ng = (uint32_t)(a.Np / 16);
-    v4i wc[NC], ws[NS];
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
-      const uint32_t c = idx / (DEC_CHUNK / 32), seg = idx % (DEC_CHUNK / 32), at = cb0 + 16u * seg;
-      wc[u] = at < nb ? *(const v4i*)(vc + c * nb + at) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
-      const uint32_t gi = idx / (DK / 16), cs = idx % (DK / 16);
-      ws[u] = g0 + gi < ng ? *(const v4i*)(vs + (g0 + gi) * DK + 16u * cs) : v4i{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < NC; ++u) {
-      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
-      *(v4i*)(vl + (idx / (DEC_CHUNK / 32)) * VROW + 16u * (idx % (DEC_CHUNK / 32))) = wc[u];
-    }
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      const uint32_t idx = threadIdx.x + DEC_THREADS * u;
-      *(v4i*)(vl + VSC0 + (idx / (DK / 16)) * DK + 16u * (idx % (DK / 16))) = ws[u];
+    for (int k = wv; k < SLOTS / 64; k += 4) {
+      const uint32_t slot = 64u * (uint32_t)k + (uint32_t)lane;
+      const uint8_t* src;
+      if (slot < (uint32_t)CODE_SLOTS) {
+        const uint32_t row = slot / (VROW / 16), seg = slot % (VROW / 16);
+        uint32_t at = cb0 + 16u * (seg < DEC_CHUNK / 32 ? seg : 0u);
+        at = at < nb ? at : nb - 16u;
+        src = vc + row * nb + at;
+      } else {
+        const uint32_t t2 = slot - (uint32_t)CODE_SLOTS, gi = t2 / (DK / 16), cs = t2 % (DK / 16);
+        const uint32_t gg = g0 + gi < ng ? g0 + gi : ng - 1u;
+        src = vs + gg * DK + 16u * cs;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(vl + 1024 * k), 16, 0, 0);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct loads (and the K ring) have landed
   __syncthreads();   // V is in LDS
   for (int it0 = 0; it0 < TILES; it0 += DEPTH) {
 #pragma unroll
@@ -184,17 +181,22 @@ __global__ __launch_bounds__(DEC_THREADS, 2) void decode_split_kernel(DecodeArgs
       const int it = it0 + u;
       const Tile T = ring[u];
       if (it + DEPTH < TILES) load(it + DEPTH, ring[u]);   // wave-uniform
-      const int kl0 = 256 * wv + 16 * it;                  // the tile's first key within the chunk
+      const int kl0 = (DEC_CHUNK / 4) * wv + 16 * it;      // the tile's first key within the chunk
       const int key0 = j0 + kl0;
       // S^T = K Q^T over the 4 channel slices
       v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      const float s0 = ue4m3(T.ks2 & 0xffu), s1 = ue4m3((T.ks2 >> 8) & 0xffu);
+      // K in f16: the E2M1 pairs times the group's scale pair (exact: E2M1 x UE4M3)
+      const _Float16 h0 = (_Float16)ue4m3(T.ks2 & 0xffu), h1 = (_Float16)ue4m3((T.ks2 >> 8) & 0xffu);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        float x[8];
-        e2m1x8((uint32_t)T.kw[kk], kk < 2 ? s0 : s1, x);
-        if constexpr (F16) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(pack8<true>(x), qb[kk], acc, 0, 0, 0);
-        else acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack8<false>(x), qb[kk], acc, 0, 0, 0);
+        const uint32_t u = (uint32_t)T.kw[kk];
+        const v2h sc = kk < 2 ? v2h{h0, h0} : v2h{h1, h1};
+        const v2h k0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 0) * sc;
+        const v2h k1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 1) * sc;
+        const v2h k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 2) * sc;
+        const v2h k3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 3) * sc;
+        const v8h ka = v8h{k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[kk], acc, 0, 0, 0);
       }
       // row r's scores of keys key0 + 4h + e, in log2 units; masked keys -inf
       float p[4];
