@@ -7,9 +7,11 @@
 //
 // The work is reading the cache (144 bytes per key per KV head at d = 128).  Both products
 // run on the matrix cores, so the vector work per key does not grow with the query rows:
-//   * a workgroup takes 512 keys of one (b, KV head) for 16 query rows (the q-heads of the
-//     KV head's group times the new tokens); each of its 4 waves walks its own 128 keys in
-//     16-key tiles with its own running max and sum, merged at the end (log-sum-exp);
+//   * a workgroup takes consecutive 512-key chunks of one (b, KV head) for 16 query rows (the
+//     q-heads of the KV head's group times the new tokens); in each chunk, each of its 4 waves
+//     walks its own 128 keys in 16-key tiles with its own running max and sum (kept across the
+//     chunks), merged at the end (log-sum-exp): the Q set-up and the merge are paid once per
+//     workgroup, and the combine reads one partial per workgroup;
 //   * S^T (16 keys x 16 rows) = K Q^T on v_mfma_f32_16x16x32_f16: lane (r, h) of the A
 //     operand holds key r's 32 channels 32h..32h+31, dequantized in registers from one 16-byte
 //     load (E2M1 pairs to f16 times the scale pair: exact); Q^T is the B operand with the same
@@ -22,8 +24,8 @@
 //     tile for the whole wave; P <= 2^15 stays finite in f16;
 //   * the workgroup's V codes and scales (512 tokens x 128 channels) go to LDS by direct
 //     global->LDS loads (channel rows padded to 272 bytes, so the 16 channel lanes of a read
-//     hit distinct banks), after each wave's K loads for all its 8 tiles; V's 2-byte pieces are
-//     then read from LDS;
+//     hit distinct banks), after each wave's K loads for its first 4 tiles; V's 2-byte pieces
+//     are then read from LDS;
 //   * a split writes only the R real rows of its partial O (not the 16 of the row group).
 // decode_combine_kernel merges the splits and writes O.
 #include "device.hpp"
@@ -33,7 +35,9 @@ namespace sage {
 namespace {
 
 constexpr int DK = 128;             // head dimension
-constexpr int DEC_CHUNK = 512;      // keys per split workgroup
+constexpr int DEC_CHUNK = 512;      // keys staged in LDS at a time
+constexpr int DEC_MAX_CHUNKS = 8;  // chunks one split workgroup may take
+constexpr int DEC_SLOTS = 1024;     // workgroups resident at once: 256 CUs x 4
 constexpr int DEC_THREADS = 256;    // 4 waves x 8 key slots
 constexpr float kLazy = 15.0f;      // headroom of the running max, log2 units (P <= 2^15 fits f16)
 
@@ -44,6 +48,7 @@ struct DecodeArgs {
   float* part_o;                               // [B * Hkv, nsplit, R, 128]
   float* part_ml;                              // [B * Hkv, nsplit, R, 2]
   int64_t Hq, Hkv, Nq, Nk, Np, nsplit, R, nrg; // R = (Hq / Hkv) * Nq rows per KV head, nrg groups of 16
+  int chunks;                                  // 512-key chunks per split
   int causal;
   float qscale;                                // sm_scale * log2(e)
 };
@@ -126,118 +131,123 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb) o[cb] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int Nk = (int)a.Nk, j0 = (int)(split * DEC_CHUNK);
+  const int Nk = (int)a.Nk;
   const uint32_t hNp = (uint32_t)(a.Np / 2);
   const uint8_t* kc = a.kc + bkv * a.Nk * 64;
   const uint8_t* ks = a.ks + bkv * a.Nk * 8;
   const uint8_t* vc = a.vc + bkv * DK * (a.Np / 2);
   const uint8_t* vs = a.vs + bkv * (a.Np / 16) * DK;
   const bool causal = a.causal != 0;
-  // this wave's tile it starts at key j0 + (DEC_CHUNK / 4) wv + 16 it; K rows past the cache
-  // are clamped (their keys are masked)
-  auto load = [&](int it, Tile& T) __attribute__((always_inline)) {
-    const int key0 = j0 + (DEC_CHUNK / 4) * wv + 16 * it;
-    const uint32_t jk = (uint32_t)(key0 + r < Nk ? key0 + r : Nk - 1);
-    T.kw = *(const v4i*)(kc + jk * 64u + 16u * (uint32_t)h);
-    T.ks2 = *(const uint16_t*)(ks + jk * 8u + 2u * (uint32_t)h);
-  };
-  constexpr int TILES = DEC_CHUNK / 64, DEPTH = 8;   // 8 tiles of 16 keys per wave: all in flight
+  constexpr int TILES = DEC_CHUNK / 64, DEPTH = 4;   // 8 tiles of 16 keys per wave, 4 in flight
   static_assert(TILES % DEPTH == 0, "whole rounds of the ring");
-  Tile ring[DEPTH];   // the first tiles' K loads go out before V's
+  for (int chunk = 0; chunk < a.chunks; ++chunk) {
+    const int j0 = (int)((split * a.chunks + chunk) * DEC_CHUNK);
+    if (j0 >= Nk) break;   // workgroup-uniform
+    if (chunk > 0) __syncthreads();   // every wave is done with the previous chunk's V
+    // this wave's tile it starts at key j0 + (DEC_CHUNK / 4) wv + 16 it; K rows past the cache
+    // are clamped (their keys are masked)
+    auto load = [&](int it, Tile& T) __attribute__((always_inline)) {
+      const int key0 = j0 + (DEC_CHUNK / 4) * wv + 16 * it;
+      const uint32_t jk = (uint32_t)(key0 + r < Nk ? key0 + r : Nk - 1);
+      T.kw = *(const v4i*)(kc + jk * 64u + 16u * (uint32_t)h);
+      T.ks2 = *(const uint16_t*)(ks + jk * 8u + 2u * (uint32_t)h);
+    };
+    Tile ring[DEPTH];   // the first tiles' K loads go out before V's
 #pragma unroll
-  for (int u = 0; u < DEPTH; ++u) load(u, ring[u]);
-  // V of the chunk into LDS by direct global->LDS loads (no registers): a wave instruction
-  // fills 1 KB of LDS, lane i its 16-byte slot i, and each lane fetches the global segment that
-  // belongs to its slot.  Code slots: row c (channel) x 17 (16 segments of the chunk's
-  // DEC_CHUNK/2 bytes + one padding slot); then the scale slots: 32 token groups x 8 segments.
-  // Segments past the padded cache fetch the row's last valid one (finite codes and scales;
-  // their keys are masked), padding slots fetch segment 0.
-  {
-    constexpr int CODE_SLOTS = DK * (VROW / 16), SLOTS = CODE_SLOTS + (DEC_CHUNK / 16) * (DK / 16);
-    static_assert(SLOTS % 64 == 0, "whole wave instructions");
-    const uint32_t cb0 = (uint32_t)j0 / 2u, nb = (uint32_t)hNp;      // code bytes of a channel row
-    const uint32_t g0 = (uint32_t)j0 / 16u, ng = (uint32_t)(a.Np / 16);
-    for (int k = wv; k < SLOTS / 64; k += 4) {
-      const uint32_t slot = 64u * (uint32_t)k + (uint32_t)lane;
-      const uint8_t* src;
-      if (slot < (uint32_t)CODE_SLOTS) {
-        const uint32_t row = slot / (VROW / 16), seg = slot % (VROW / 16);
-        uint32_t at = cb0 + 16u * (seg < DEC_CHUNK / 32 ? seg : 0u);
-        at = at < nb ? at : nb - 16u;
-        src = vc + row * nb + at;
-      } else {
-        const uint32_t t2 = slot - (uint32_t)CODE_SLOTS, gi = t2 / (DK / 16), cs = t2 % (DK / 16);
-        const uint32_t gg = g0 + gi < ng ? g0 + gi : ng - 1u;
-        src = vs + gg * DK + 16u * cs;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(vl + 1024 * k), 16, 0, 0);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct loads (and the K ring) have landed
-  __syncthreads();   // V is in LDS
-  for (int it0 = 0; it0 < TILES; it0 += DEPTH) {
-#pragma unroll
-    for (int u = 0; u < DEPTH; ++u) {
-      const int it = it0 + u;
-      const Tile T = ring[u];
-      if (it + DEPTH < TILES) load(it + DEPTH, ring[u]);   // wave-uniform
-      const int kl0 = (DEC_CHUNK / 4) * wv + 16 * it;      // the tile's first key within the chunk
-      const int key0 = j0 + kl0;
-      // S^T = K Q^T over the 4 channel slices
-      v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-      // K in f16: the E2M1 pairs times the group's scale pair (exact: E2M1 x UE4M3)
-      const _Float16 h0 = (_Float16)ue4m3(T.ks2 & 0xffu), h1 = (_Float16)ue4m3((T.ks2 >> 8) & 0xffu);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t u = (uint32_t)T.kw[kk];
-        const v2h sc = kk < 2 ? v2h{h0, h0} : v2h{h1, h1};
-        const v2h k0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 0) * sc;
-        const v2h k1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 1) * sc;
-        const v2h k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 2) * sc;
-        const v2h k3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 3) * sc;
-        const v8h ka = v8h{k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[kk], acc, 0, 0, 0);
-      }
-      // row r's scores of keys key0 + 4h + e, in log2 units; masked keys -inf
-      float p[4];
-      bool up = false;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = key0 + 4 * h + e;
-        const bool vis = j < Nk && (causal ? j <= qpos : qpos >= 0);
-        p[e] = vis ? acc[e] * qs : NEG;
-        up |= p[e] > m + kLazy;   // also the first visible key (m = -inf)
-      }
-      if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform: move the running max
-        float tmax = __builtin_fmaxf(__builtin_fmaxf(p[0], p[1]), __builtin_fmaxf(p[2], p[3]));
-        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));   // the row's 16 keys sit in lanes r + 16h
-        tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
-        if (tmax > m + kLazy) {
-          const float alpha = m == NEG ? 0.0f : __builtin_amdgcn_exp2f(m - tmax);
-          lpart *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
-          m = tmax;
+    for (int u = 0; u < DEPTH; ++u) load(u, ring[u]);
+    // V of the chunk into LDS by direct global->LDS loads (no registers): a wave instruction
+    // fills 1 KB of LDS, lane i its 16-byte slot i, and each lane fetches the global segment that
+    // belongs to its slot.  Code slots: row c (channel) x 17 (16 segments of the chunk's
+    // DEC_CHUNK/2 bytes + one padding slot); then the scale slots: 32 token groups x 8 segments.
+    // Segments past the padded cache fetch the row's last valid one (finite codes and scales;
+    // their keys are masked), padding slots fetch segment 0.
+    {
+      constexpr int CODE_SLOTS = DK * (VROW / 16), SLOTS = CODE_SLOTS + (DEC_CHUNK / 16) * (DK / 16);
+      static_assert(SLOTS % 64 == 0, "whole wave instructions");
+      const uint32_t cb0 = (uint32_t)j0 / 2u, nb = (uint32_t)hNp;      // code bytes of a channel row
+      const uint32_t g0 = (uint32_t)j0 / 16u, ng = (uint32_t)(a.Np / 16);
+      for (int k = wv; k < SLOTS / 64; k += 4) {
+        const uint32_t slot = 64u * (uint32_t)k + (uint32_t)lane;
+        const uint8_t* src;
+        if (slot < (uint32_t)CODE_SLOTS) {
+          const uint32_t row = slot / (VROW / 16), seg = slot % (VROW / 16);
+          uint32_t at = cb0 + 16u * (seg < DEC_CHUNK / 32 ? seg : 0u);
+          at = at < nb ? at : nb - 16u;
+          src = vc + row * nb + at;
+        } else {
+          const uint32_t t2 = slot - (uint32_t)CODE_SLOTS, gi = t2 / (DK / 16), cs = t2 % (DK / 16);
+          const uint32_t gg = g0 + gi < ng ? g0 + gi : ng - 1u;
+          src = vs + gg * DK + 16u * cs;
         }
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(vl + 1024 * k), 16, 0, 0);
       }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the direct loads (and the K ring) have landed
+    __syncthreads();   // V is in LDS
+    for (int it0 = 0; it0 < TILES; it0 += DEPTH) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = p[e] == NEG ? 0.0f : __builtin_amdgcn_exp2f(p[e] - m);   // m may still be -inf
-        lpart += p[e];
-      }
-      const v4h pb = v4h{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-      // O^T += V^T P^T over the 8 channel blocks; V codes of channel 16 cb + r, tokens 4h..4h+3
-      const uint32_t vo = (uint32_t)kl0 / 2u + 2u * (uint32_t)h, so = VSC0 + ((uint32_t)kl0 / 16u) * DK;
+      for (int u = 0; u < DEPTH; ++u) {
+        const int it = it0 + u;
+        const Tile T = ring[u];
+        if (it + DEPTH < TILES) load(it + DEPTH, ring[u]);   // wave-uniform
+        const int kl0 = (DEC_CHUNK / 4) * wv + 16 * it;      // the tile's first key within the chunk
+        const int key0 = j0 + kl0;
+        // S^T = K Q^T over the 4 channel slices
+        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        // K in f16: the E2M1 pairs times the group's scale pair (exact: E2M1 x UE4M3)
+        const _Float16 h0 = (_Float16)ue4m3(T.ks2 & 0xffu), h1 = (_Float16)ue4m3((T.ks2 >> 8) & 0xffu);
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) {
-        const uint32_t ch = 16u * (uint32_t)cb + (uint32_t)r;
-        const uint32_t vw = *(const uint16_t*)(vl + ch * VROW + vo);
-        const _Float16 vsc = (_Float16)ue4m3(vl[so + ch]);   // exact in f16
-        const v2h sc2 = v2h{vsc, vsc};
-        const v2h d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 0) * sc2;   // exact: E2M1 x UE4M3
-        const v2h d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 1) * sc2;
-        const v4h va = v4h{d0[0], d0[1], d1[0], d1[1]};
-        o[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[cb], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t u = (uint32_t)T.kw[kk];
+          const v2h sc = kk < 2 ? v2h{h0, h0} : v2h{h1, h1};
+          const v2h k0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 0) * sc;
+          const v2h k1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 1) * sc;
+          const v2h k2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 2) * sc;
+          const v2h k3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(u, 1.0f, 3) * sc;
+          const v8h ka = v8h{k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[kk], acc, 0, 0, 0);
+        }
+        // row r's scores of keys key0 + 4h + e, in log2 units; masked keys -inf
+        float p[4];
+        bool up = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = key0 + 4 * h + e;
+          const bool vis = j < Nk && (causal ? j <= qpos : qpos >= 0);
+          p[e] = vis ? acc[e] * qs : NEG;
+          up |= p[e] > m + kLazy;   // also the first visible key (m = -inf)
+        }
+        if (__builtin_amdgcn_ballot_w64(up) != 0) {   // wave-uniform: move the running max
+          float tmax = __builtin_fmaxf(__builtin_fmaxf(p[0], p[1]), __builtin_fmaxf(p[2], p[3]));
+          tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 16));   // the row's 16 keys sit in lanes r + 16h
+          tmax = __builtin_fmaxf(tmax, __shfl_xor(tmax, 32));
+          if (tmax > m + kLazy) {
+            const float alpha = m == NEG ? 0.0f : __builtin_amdgcn_exp2f(m - tmax);
+            lpart *= alpha;
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) o[cb] *= alpha;
+            m = tmax;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = p[e] == NEG ? 0.0f : __builtin_amdgcn_exp2f(p[e] - m);   // m may still be -inf
+          lpart += p[e];
+        }
+        const v4h pb = v4h{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
+        // O^T += V^T P^T over the 8 channel blocks; V codes of channel 16 cb + r, tokens 4h..4h+3
+        const uint32_t vo = (uint32_t)kl0 / 2u + 2u * (uint32_t)h, so = VSC0 + ((uint32_t)kl0 / 16u) * DK;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) {
+          const uint32_t ch = 16u * (uint32_t)cb + (uint32_t)r;
+          const uint32_t vw = *(const uint16_t*)(vl + ch * VROW + vo);
+          const _Float16 vsc = (_Float16)ue4m3(vl[so + ch]);   // exact in f16
+          const v2h sc2 = v2h{vsc, vsc};
+          const v2h d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 0) * sc2;   // exact: E2M1 x UE4M3
+          const v2h d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 1) * sc2;
+          const v4h va = v4h{d0[0], d0[1], d1[0], d1[1]};
+          o[cb] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb, o[cb], 0, 0, 0);
+        }
       }
     }
   }
@@ -325,9 +335,22 @@ __global__ __launch_bounds__(DK) void decode_combine_kernel(const float* __restr
 
 }  // namespace
 
+// Chunks per split: as many as keep one round of resident workgroups busy (more chunks per
+// workgroup pay the Q set-up and the merge fewer times and leave fewer partials to combine).
+static int64_t decode_chunks(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk) {
+  const int64_t nrg = ((Hq / Hkv) * Nq + 15) / 16, nchunk = (Nk + DEC_CHUNK - 1) / DEC_CHUNK;
+  const int64_t c = (B * Hkv * nrg * nchunk) / DEC_SLOTS;
+  return c < 1 ? 1 : c > DEC_MAX_CHUNKS ? DEC_MAX_CHUNKS : c;
+}
+
+static int64_t decode_splits(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk) {
+  const int64_t per = DEC_CHUNK * decode_chunks(B, Hq, Hkv, Nq, Nk);
+  return (Nk + per - 1) / per;
+}
+
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk) {
   const int64_t R = (Hq / Hkv) * Nq;
-  const int64_t nsplit = (Nk + DEC_CHUNK - 1) / DEC_CHUNK;
+  const int64_t nsplit = decode_splits(B, Hq, Hkv, Nq, Nk);
   return (size_t)(B * Hkv * nsplit * R) * (DK + 2) * sizeof(float);
 }
 
@@ -335,7 +358,7 @@ hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, i
                          const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int causal,
                          float sm_scale, void* out, bool out_bf16, void* ws, hipStream_t st) {
   const int64_t R = (Hq / Hkv) * Nq, nrg = (R + 15) / 16;
-  const int64_t nsplit = (Nk + DEC_CHUNK - 1) / DEC_CHUNK;
+  const int64_t nsplit = decode_splits(B, Hq, Hkv, Nq, Nk);
   DecodeArgs a;
   a.q = q;
   a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
@@ -343,6 +366,7 @@ hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, i
   a.part_ml = (float*)ws + B * Hkv * nsplit * R * DK;
   a.Hq = Hq; a.Hkv = Hkv; a.Nq = Nq; a.Nk = Nk; a.Np = (Nk + 63) / 64 * 64;
   a.nsplit = nsplit; a.R = R; a.nrg = nrg;
+  a.chunks = (int)decode_chunks(B, Hq, Hkv, Nq, Nk);
   a.causal = causal;
   a.qscale = (float)((double)sm_scale * 1.4426950408889634);
   const int64_t nwg = B * Hkv * nsplit * nrg;

@@ -284,6 +284,8 @@ DEC_CASES = [   # (B, Hq, Hkv, Nq, Nk, causal): rows per KV head R = (Hq / Hkv) 
     (1, 4, 4, 5, 1100, True),      # MHA with 5 new tokens
     (1, 4, 2, 64, 700, True),      # 64 new tokens: R = 128, eight row groups
     (1, 16, 2, 2, 2100, True),     # R = 16: one full row group
+    (2, 16, 4, 16, 33068, True),   # R = 64: 2080 chunk-workgroups -> two 512-key chunks per
+                                   # split; the last split stops after its first chunk
 ]
 
 
@@ -358,6 +360,30 @@ def test_attention_parity(name, ov, causal, variant):
     rel, cos = check_out(res.out.cpu().numpy(), orc["out"], f"{name} {variant} causal={causal}")
     ref = fp64_reference(q, k, v, causal)
     print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
+
+
+@pytest.mark.parametrize("direction", [1.0, -1.0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_running_max_moves_often(direction, causal):
+    """Scores that rise (or fall) along the keys by about 60 log2 units over 1000 keys: the
+    softmax reference of the bf16-P pass then passes its lazy threshold on most tiles (or on
+    the first only), and O and l are rescaled each time."""
+    sage = _sage()
+    g = torch.Generator().manual_seed(11)
+    B, H, N, D = 1, 2, 1000, 128
+    u = torch.randn(D, generator=g)
+    u /= u.norm()
+    q = 16.0 * u + 0.3 * torch.randn(B, H, N, D, generator=g)
+    ramp = direction * 16.0 * torch.linspace(-1.0, 1.0, N)[:, None]
+    k = ramp * u + 0.3 * torch.randn(B, H, N, D, generator=g)
+    v = torch.randn(B, H, N, D, generator=g)
+    q, k, v = (t.to(torch.bfloat16) for t in (q, k, v))
+    print(f"[case] ramp direction={direction} causal={causal}", flush=True)
+    res = sage.forward(*_cuda(q, k, v), causal=causal, variant="int8")
+    torch.cuda.synchronize()
+    orc = oracle_pass(q, k, v, causal, "int8")
+    rel, cos = check_out(res.out.cpu().numpy(), orc["out"], f"ramp {direction} causal={causal}")
+    print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f}")
 
 
 def test_attention_bf16_output_within_one_ulp():
