@@ -40,7 +40,10 @@ VARIANT_DTYPE = {"int8": "int8+bf16", "thrift": "int8+bf16", "sink": "int8+bf16"
 KERNEL_SOURCES = {"int8": ("attn_i8.hip", "attn_common.hpp"), "thrift": ("attn_i8.hip", "attn_common.hpp"),
                   "sink": ("attn_i8.hip", "attn_common.hpp"),
                   "int8_fp8pv": ("attn_i8.hip", "attn_common.hpp"),
-                  "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp")}
+                  "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp"),
+                  "decode": ("decode.hip",)}
+# kernels whose counters add up to one launch of the measured step
+TRAFFIC_KERNELS = {"decode": ("decode_split_kernel", "decode_combine_kernel")}
 
 
 def attention_kernel_hash(variant: str) -> str:
@@ -56,8 +59,8 @@ def traffic_key(workload: str, causal: bool, variant: str) -> str:
 
 
 def load_traffic(workload: str, causal: bool, variant: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+    """HBM bytes per attention launch (decode: split + combine) from the committed rocprofv3
+    counter summary, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "attn_traffic.json")
     if not os.path.exists(path):
         return None
@@ -183,7 +186,8 @@ def run_decode(args, w):
                    "step": "decode attention of the new tokens against the NVFP4 KV cache (split + combine); "
                            "ops counted as 4*B*Hq*Nq*Nk*d"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                     "frac": round(achieved / 8000.0, 4), "traffic": None, "kernel": "decode (split + combine)",
+                     "frac": round(achieved / 8000.0, 4), "traffic": load_traffic(w.name, False, "decode"),
+                     "kernel": "decode (split + combine)",
                      "kernel_ms": round(kern_ms, 4), "algorithmic_bytes": alg},
     }
     if not args.no_cpu_baseline:
@@ -219,16 +223,17 @@ def _pmc_mean_kib(run_dir: str, kernel_re: str, counter: str) -> float:
     return sum(vals) / len(vals)
 
 
-def traffic_from(dirs, key: str, kernel_re: str, out_path: str):
+def traffic_from(dirs, key: str, kernel_res, out_path: str):
     """Turn four rocprofv3 --pmc runs (attention FETCH_SIZE, attention WRITE_SIZE, calibration
     FETCH_SIZE, calibration WRITE_SIZE; KiB per dispatch) into HBM bytes per attention launch,
-    each counter scaled by known-bytes / counter-bytes of the calibration kernel."""
+    each counter scaled by known-bytes / counter-bytes of the calibration kernel.  A launch of
+    several kernels (kernel_res) adds their per-dispatch means."""
     fa, wa, fc, wc = dirs
     n = 1 << 28
     f_scale = 4 * n / (_pmc_mean_kib(fc, "convert_kernel", "FETCH_SIZE") * 1024)
     w_scale = 2 * n / (_pmc_mean_kib(wc, "convert_kernel", "WRITE_SIZE") * 1024)
-    fetch = _pmc_mean_kib(fa, kernel_re, "FETCH_SIZE") * 1024 * f_scale
-    write = _pmc_mean_kib(wa, kernel_re, "WRITE_SIZE") * 1024 * w_scale
+    fetch = sum(_pmc_mean_kib(fa, r, "FETCH_SIZE") for r in kernel_res) * 1024 * f_scale
+    write = sum(_pmc_mean_kib(wa, r, "WRITE_SIZE") for r in kernel_res) * 1024 * w_scale
     db = json.load(open(out_path)) if os.path.exists(out_path) else {}
     db[key] = {"kernel_hash": attention_kernel_hash(key.split(":")[2]), "bytes_per_launch": round(fetch + write),
                "fetch_bytes": round(fetch), "write_bytes": round(write),
@@ -267,11 +272,12 @@ def main():
     w = I.workload(args.workload)
     variant = args.variant or DEFAULT_VARIANT[w.name]
     causal = bool(args.causal or w.causal)
+    if args.traffic_from:
+        return traffic_from(args.traffic_from, traffic_key(w.name, causal, variant),
+                            TRAFFIC_KERNELS.get(variant, ("attn_",)),
+                            os.path.join(ROOT, "profiles", "attn_traffic.json"))
     if variant == "decode":
         return run_decode(args, w)
-    if args.traffic_from:
-        return traffic_from(args.traffic_from, traffic_key(w.name, causal, variant), "attn_",
-                            os.path.join(ROOT, "profiles", "attn_traffic.json"))
 
     import torch
     from bit_quantized_attention_03_amd import sage
