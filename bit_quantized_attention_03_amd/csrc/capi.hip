@@ -16,6 +16,8 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool shape_ok(const sage_shape& s) {
   return s.B >= 0 && s.H >= 1 && s.N >= 0 && s.D >= 1 && s.B <= (1 << 20) && s.H <= 65535 && s.B * s.H <= 65535 && s.N <= (1ll << 31);
 }
+// A call whose tensors hold no elements: it validates, then returns without reading a pointer.
+bool empty_call(const sage_shape& s) { return s.B * s.H == 0 || s.N == 0; }
 bool is16(sage_fmt f) { return f == SAGE_BF16 || f == SAGE_FP16; }
 int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int launched(hipError_t e) { return e == hipSuccess ? SAGE_OK : (e == hipErrorNotSupported ? SAGE_ENOTSUP : SAGE_EHIP); }
@@ -45,13 +47,15 @@ size_t sage_smooth_k_workspace_bytes(sage_shape ks) {
 
 int sage_smooth_k(const void* k, sage_fmt dt, sage_shape ks, float* mean_out, void* k_smoothed_out, void* workspace,
                   size_t workspace_bytes, hipStream_t stream) {
-  if (!k || !mean_out || !shape_ok(ks) || ks.D % 8 != 0) return SAGE_EINVAL;
+  if (!shape_ok(ks) || ks.D % 8 != 0) return SAGE_EINVAL;
+  const bool no_heads = ks.B * ks.H == 0;   // N == 0 still writes the (zero) means
+  if ((!k && !no_heads && ks.N > 0) || (!mean_out && !no_heads)) return SAGE_EINVAL;
   if (!is16(dt)) return SAGE_ENOTSUP;
   if (!aligned16(k) || !aligned16(mean_out) || (k_smoothed_out && !aligned16(k_smoothed_out))) return SAGE_EALIGN;
   const size_t need = sage_smooth_k_workspace_bytes(ks);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
   if (workspace && !aligned16(workspace)) return SAGE_EALIGN;
-  if (ks.B == 0) return SAGE_OK;
+  if (no_heads) return SAGE_OK;
   return launched(launch_smooth_k(k, dt == SAGE_FP16, ks.B * ks.H, ks.N, (int)ks.D, mean_out, k_smoothed_out,
                                   (float*)workspace, stream));
 }
@@ -93,7 +97,8 @@ int sage_quantized_bytes(sage_fmt fmt, sage_block block, sage_shape xs, size_t* 
 namespace {
 int quantize_impl(const void* x, sage_fmt in_dt, sage_shape xs, const float* mean, sage_fmt fmt, sage_block block,
                   sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream) {
-  if (!x || !codes_out || !scales_out || !shape_ok(xs)) return SAGE_EINVAL;
+  if (!shape_ok(xs)) return SAGE_EINVAL;
+  if (!empty_call(xs) && (!x || !codes_out || !scales_out)) return SAGE_EINVAL;
   if (!is16(in_dt)) return SAGE_ENOTSUP;
   if (xs.D % 8 != 0) return SAGE_EINVAL;
   size_t cb, sb;
@@ -137,7 +142,7 @@ int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt 
 int sage_quantize_smoothed(const void* k, sage_fmt in_dt, sage_shape ks, const float* mean, sage_fmt fmt,
                            sage_block block, sage_scale_mode mode, void* codes_out, void* scales_out,
                            hipStream_t stream) {
-  if (!mean) return SAGE_EINVAL;
+  if (!mean && !(shape_ok(ks) && empty_call(ks))) return SAGE_EINVAL;
   if (fmt == SAGE_E4M3) return SAGE_ENOTSUP;                                          // a V format
   if ((fmt == SAGE_MXFP4 || fmt == SAGE_NVFP4) && block.tokens != 1) return SAGE_ENOTSUP;   // along D only
   if (!aligned16(mean)) return SAGE_EALIGN;
@@ -146,7 +151,8 @@ int sage_quantize_smoothed(const void* k, sage_fmt in_dt, sage_shape ks, const f
 
 int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, int along_tokens, void* f8_out,
                         void* e8m0_out, hipStream_t stream) {
-  if (!codes || !scales || !f8_out || !e8m0_out || !shape_ok(xs)) return SAGE_EINVAL;
+  if (!shape_ok(xs)) return SAGE_EINVAL;
+  if (!empty_call(xs) && (!codes || !scales || !f8_out || !e8m0_out)) return SAGE_EINVAL;
   if (along_tokens != 0 && along_tokens != 1) return SAGE_EINVAL;
   if (!along_tokens && xs.D % 32) return SAGE_EINVAL;
   if (!aligned16(codes) || !aligned16(f8_out)) return SAGE_EALIGN;
@@ -158,10 +164,11 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
 
 int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
                   void* out, sage_fmt out_dt, hipStream_t stream) {
-  if (!q || !k || !v || !p || !out) return SAGE_EINVAL;
-  if (!q->codes || !k->codes || !v->codes) return SAGE_EINVAL;
+  if (!q || !k || !v || !p) return SAGE_EINVAL;
   const sage_shape &qs = q->shape, &ks = k->shape, &vs = v->shape;
   if (!shape_ok(qs) || !shape_ok(ks) || !shape_ok(vs)) return SAGE_EINVAL;
+  const bool empty = empty_call(qs);
+  if (!empty && (!out || !q->codes || !k->codes || !v->codes)) return SAGE_EINVAL;
   if (ks.B != qs.B || vs.B != qs.B || ks.N != qs.N || vs.N != qs.N || ks.D != qs.D || vs.D != qs.D || vs.H != ks.H)
     return SAGE_EINVAL;
   if (qs.H % ks.H != 0) return SAGE_EINVAL;
@@ -183,17 +190,18 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   a.out = out; a.out_bf16 = out_dt == SAGE_BF16;
 
   if (q->fmt == SAGE_INT8 && k->fmt == SAGE_INT8) {
-    if (!q->scales || !k->scales) return SAGE_EINVAL;
+    if (!empty && (!q->scales || !k->scales)) return SAGE_EINVAL;
     if (is16(v->fmt) && p->p_fmt == SAGE_BF16) {
       if (p->block_mask) {
-        if (!p->q_hi || !p->k_hi || p->hi_dt != SAGE_BF16) return SAGE_EINVAL;
+        if (!empty && (!p->q_hi || !p->k_hi)) return SAGE_EINVAL;
+        if (p->hi_dt != SAGE_BF16) return SAGE_EINVAL;
         if (!aligned16(p->q_hi) || !aligned16(p->k_hi)) return SAGE_EALIGN;
       }
       if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
       return launched(launch_attn_int8(a, 0, stream));
     }
     if (v->fmt == SAGE_E4M3 && p->p_fmt == SAGE_E4M3) {
-      if (!v->scales || p->block_mask) return SAGE_EINVAL;
+      if ((!empty && !v->scales) || p->block_mask) return SAGE_EINVAL;
       if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
       return launched(launch_attn_int8(a, 1, stream));
     }
@@ -203,7 +211,7 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   const bool mx4 = q->fmt == SAGE_MXFP4 && k->fmt == SAGE_MXFP4 && v->fmt == SAGE_MXFP4 && p->p_fmt == SAGE_MXFP4;
   const bool mx8 = q->fmt == SAGE_MXFP8 && k->fmt == SAGE_MXFP8 && v->fmt == SAGE_MXFP8 && p->p_fmt == SAGE_NVFP4;
   if (!mx4 && !mx8) return SAGE_ENOTSUP;
-  if (!q->scales || !k->scales || !v->scales) return SAGE_EINVAL;
+  if (!empty && (!q->scales || !k->scales || !v->scales)) return SAGE_EINVAL;
   if (qs.D != 128) return SAGE_ENOTSUP;   // the microscaled kernels are built for D = 128
   // scale bytes are read as dwords (4 per Q/K row, 2*D per V tile)
   if ((uintptr_t)q->scales % 4 || (uintptr_t)k->scales % 4 || (uintptr_t)v->scales % 4) return SAGE_EALIGN;
@@ -219,7 +227,8 @@ size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_b
 int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sage_shape qs, sage_shape ks,
                          int q_block, int k_block, double frac, int causal, uint8_t* mask_out, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  if (!q || !k_smoothed || !mask_out || !shape_ok(qs) || !shape_ok(ks)) return SAGE_EINVAL;
+  if (!shape_ok(qs) || !shape_ok(ks)) return SAGE_EINVAL;
+  if (!empty_call(qs) && (!q || !k_smoothed || !mask_out)) return SAGE_EINVAL;
   if (ks.B != qs.B || ks.N != qs.N || ks.D != qs.D || qs.H % ks.H != 0 || qs.D % 8 != 0) return SAGE_EINVAL;
   if (dt != SAGE_BF16 || q_block != QBLK || k_block != KBLK || qs.D > 128) return SAGE_ENOTSUP;
   if (!(frac >= 0.0 && frac <= 1.0) || (causal != 0 && causal != 1)) return SAGE_EINVAL;
@@ -228,10 +237,10 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
     if (nqb * nkb > INT32_MAX) return SAGE_EINVAL;
   }
   if (!aligned16(q) || !aligned16(k_smoothed)) return SAGE_EALIGN;
-  const size_t need = thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
-  if (!workspace || workspace_bytes < need) return SAGE_EWORKSPACE;
+  const size_t need = empty_call(qs) ? 0 : thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
   if (!aligned16(workspace)) return SAGE_EALIGN;
-  if (qs.B == 0 || qs.N == 0) return SAGE_OK;
+  if (empty_call(qs)) return SAGE_OK;
   return launched(launch_thrift_select((const uint16_t*)q, (const uint16_t*)k_smoothed, qs.B, qs.H, ks.H, qs.N,
                                        (int)qs.D, frac, causal, mask_out, workspace, stream));
 }
@@ -244,8 +253,9 @@ size_t sage_decode_workspace_bytes(sage_shape qs, sage_shape ks) {
 int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
                     int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
-  if (!q || !k || !v || !out || !shape_ok(qs)) return SAGE_EINVAL;
-  if (!k->codes || !k->scales || !v->codes || !v->scales) return SAGE_EINVAL;
+  if (!k || !v || !shape_ok(qs)) return SAGE_EINVAL;
+  const bool empty = empty_call(qs);   // no new tokens (or no batch): nothing is read
+  if (!empty && (!q || !out || !k->codes || !k->scales || !v->codes || !v->scales)) return SAGE_EINVAL;
   const sage_shape &ks = k->shape, &vs = v->shape;
   if (!shape_ok(ks) || !shape_ok(vs)) return SAGE_EINVAL;
   if (ks.B != qs.B || vs.B != qs.B || vs.H != ks.H || vs.N != ks.N || ks.D != qs.D || vs.D != qs.D) return SAGE_EINVAL;
@@ -257,9 +267,9 @@ int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qten
   if (!aligned16(q) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
   if ((uintptr_t)k->scales % 2) return SAGE_EALIGN;   // read as byte pairs
   const size_t need = decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
-  if (!workspace || workspace_bytes < need) return SAGE_EWORKSPACE;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
   if (!aligned16(workspace)) return SAGE_EALIGN;
-  if (qs.B == 0 || qs.N == 0) return SAGE_OK;
+  if (empty) return SAGE_OK;
   const float sc = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)qs.D);
   return launched(launch_decode((const uint16_t*)q, q_dt == SAGE_FP16, qs.B, qs.H, ks.H, qs.N, ks.N,
                                 (const uint8_t*)k->codes, (const uint8_t*)k->scales, (const uint8_t*)v->codes,
@@ -268,14 +278,15 @@ int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qten
 
 int sage_sink_blocks(sage_shape qs, int q_block, int k_block, int n_first, int n_last, int causal, uint8_t* mask_out,
                      hipStream_t stream) {
-  if (!mask_out || !shape_ok(qs)) return SAGE_EINVAL;
+  if (!shape_ok(qs)) return SAGE_EINVAL;
+  if (!empty_call(qs) && !mask_out) return SAGE_EINVAL;
   if (q_block != QBLK || k_block != KBLK) return SAGE_ENOTSUP;
   if (n_first < 0 || n_last < 0 || (causal != 0 && causal != 1)) return SAGE_EINVAL;
   return launched(launch_sink_mask(qs.B * qs.H, qs.N, n_first, n_last, causal, mask_out, stream));
 }
 
 int sage_convert_f32(const float* x, int64_t n, sage_fmt fmt, void* out, hipStream_t stream) {
-  if (!x || !out || n < 0) return SAGE_EINVAL;
+  if (n < 0 || (n > 0 && (!x || !out))) return SAGE_EINVAL;
   if (fmt != SAGE_BF16 && fmt != SAGE_FP16 && fmt != SAGE_E4M3 && fmt != SAGE_MXFP4 && fmt != SAGE_NVFP4)
     return SAGE_ENOTSUP;
   return launched(launch_convert_f32(x, n, (int)fmt, out, stream));

@@ -17,6 +17,13 @@
  *    launch, so on a validation error no output has been touched.  SAGE_EHIP reports a
  *    failed launch (hipGetLastError after the enqueue).
  *  - Calls are stateless and thread-safe; calls on different streams may overlap.
+ *  - Empty calls: when a call's tensors hold no elements (B = 0 or N = 0; for decode, no
+ *    new tokens), it validates its shapes and arguments, touches no buffer and returns
+ *    SAGE_OK.  Its data pointers may then be null (PyTorch gives an empty tensor a null data
+ *    pointer).  Two outputs are not empty with N = 0: sage_smooth_k still writes the means
+ *    of its B * H heads (0: no tokens, nothing to subtract), and an E4M3 per-channel scale
+ *    array of an empty V is left untouched (the attention never reads it).  Decode needs at
+ *    least one cached key.
  *  - NaN / Inf inputs are outside the contract.
  */
 #ifndef SAGE_H_

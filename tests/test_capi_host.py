@@ -151,6 +151,42 @@ def test_validation_before_launch(L):
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
 
 
+def test_empty_calls_touch_no_pointer(L):
+    """No tokens (N = 0) or no batch (B = 0): every call validates and returns 0 with null
+    data pointers, before any launch (nothing here reaches the GPU)."""
+    from bit_quantized_attention_03_amd import sage
+    for s in (sage.Shape(1, 2, 0, 128), sage.Shape(0, 2, 64, 128)):
+        assert L.sage_quantize_blocks(None, sage.BF16, s, sage.INT8, sage.Block(128, 128), 0, None, None, None) == 0
+        assert L.sage_quantize_blocks(None, sage.BF16, s, sage.NVFP4, sage.Block(16, 1), 1, None, None, None) == 0
+        assert L.sage_quantize_blocks(None, sage.BF16, s, sage.MXFP4, sage.Block(1, 32), 0x100, None, None, None) == 0
+        assert L.sage_quantize_smoothed(None, sage.BF16, s, None, sage.INT8, sage.Block(64, 128), 0, None, None,
+                                        None) == 0
+        assert L.sage_nvfp4_to_mxfp8(None, None, s, 1, None, None, None) == 0
+        qi = sage.QTensorC(sage.INT8, None, None, s)
+        vb = sage.QTensorC(sage.BF16, None, None, s)
+        p = sage.AttnParamsC(1, 0.0, sage.BF16, None, None, None, sage.BF16)
+        assert L.sage_attn_fwd(C.byref(qi), C.byref(qi), C.byref(vb), C.byref(p), None, sage.FP32, None) == 0
+        m4 = sage.QTensorC(sage.MXFP4, None, None, s)
+        p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
+        assert L.sage_attn_fwd(C.byref(m4), C.byref(m4), C.byref(m4), C.byref(p4), None, sage.BF16, None) == 0
+        assert L.thrift_select_blocks(None, None, sage.BF16, s, s, 128, 64, 0.05, 1, None, None, 0, None) == 0
+        assert L.sage_sink_blocks(s, 128, 64, 1, 1, 1, None, None) == 0
+    assert L.sage_smooth_k(None, sage.BF16, sage.Shape(0, 2, 64, 128), None, None, None, 0, None) == 0
+    kn = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128))   # no new tokens
+    assert L.sage_decode_fwd(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(kn), C.byref(kn), 0, 0.0, None,
+                             sage.FP32, None, 0, None) == 0
+    assert L.sage_convert_f32(None, 0, sage.BF16, None, None) == 0
+    # still validated: shapes, formats, and the non-empty outputs
+    assert L.sage_quantize_blocks(None, sage.BF16, sage.Shape(1, 0, 0, 128), sage.INT8, sage.Block(128, 128), 0,
+                                  None, None, None) == -1                          # H = 0
+    assert L.sage_quantize_blocks(None, sage.BF16, sage.Shape(1, 2, 0, 96), sage.INT8, sage.Block(128, 96), 0x100,
+                                  None, None, None) == -2                          # Hadamard needs D in {64, 128}
+    assert L.sage_smooth_k(None, sage.BF16, sage.Shape(1, 2, 0, 128), None, None, None, 0, None) == -1   # means out
+    empty_cache = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 0, 128))
+    assert L.sage_decode_fwd(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(empty_cache), C.byref(empty_cache),
+                             0, 0.0, None, sage.FP32, None, 0, None) == -1         # decode needs a cached key
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     from bit_quantized_attention_03_amd import sage

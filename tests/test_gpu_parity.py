@@ -397,6 +397,31 @@ def test_attention_bf16_output_within_one_ulp():
     assert torch.all((a - b).abs() <= a.abs() * 2.0 ** -8 + 1e-30)
 
 
+@pytest.mark.parametrize("variant", ["int8", "int8_fp8pv", "thrift", "sink", "mxfp4", "nvfp4_search"])
+def test_empty_sequence_and_batch(variant):
+    """N = 0 and B = 0: every step returns at once with empty outputs; with N = 0 the heads'
+    means are written as 0 (no tokens, nothing to subtract)."""
+    sage = _sage()
+    D = 64 if variant == "int8_fp8pv" else 128
+    for shape in ((1, 2, 0, D), (0, 2, 64, D)):
+        print(f"[case] empty {variant} {shape}", flush=True)
+        q = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        res = sage.forward(q, q.clone(), q.clone(), causal=True, variant=variant)
+        torch.cuda.synchronize()
+        assert tuple(res.out.shape) == shape
+        assert torch.equal(res.mean.cpu(), torch.zeros(shape[0], shape[1], D))
+
+
+def test_decode_without_new_tokens():
+    sage = _sage()
+    q, k, v = _decode_inputs(1, 4, 2, 1, 300)
+    kq = sage.quantize(k.cuda(), sage.NVFP4, (1, 16), sage.SEARCH)
+    vq = sage.quantize(v.cuda(), sage.NVFP4, (16, 1), sage.SEARCH)
+    out = sage.decode(q[:, :, :0].contiguous().cuda(), kq, vq, True)
+    torch.cuda.synchronize()
+    assert tuple(out.shape) == (1, 4, 0, 128)
+
+
 def test_zero_q_gives_mean_of_v():
     sage = _sage()
     w = I.workload("llm_int8", B=1, Hq=1, Hkv=1, N=320)
