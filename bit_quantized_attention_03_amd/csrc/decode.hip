@@ -138,6 +138,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
   const uint8_t* vc = a.vc + bkv * DK * (a.Np / 2);
   const uint8_t* vs = a.vs + bkv * (a.Np / 16) * DK;
   const bool causal = a.causal != 0;
+  const int vis_all = causal ? Nk - (int)a.Nq + 1 : Nk;   // keys below it are visible to every row
   constexpr int TILES = DEC_CHUNK / 64, DEPTH = 4;   // 8 tiles of 16 keys per wave, 4 in flight
   static_assert(TILES % DEPTH == 0, "whole rounds of the ring");
   for (int chunk = 0; chunk < a.chunks; ++chunk) {
@@ -195,7 +196,9 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
         // S^T = K Q^T over the 4 channel slices
         v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
         // K in f16: the E2M1 pairs times the group's scale pair (exact: E2M1 x UE4M3)
-        const _Float16 h0 = (_Float16)ue4m3(T.ks2 & 0xffu), h1 = (_Float16)ue4m3((T.ks2 >> 8) & 0xffu);
+        // the two UE4M3 scale bytes to f16 in one conversion (E4M3 values are exact in f16)
+      const v2h hs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(T.ks2, 1.0f, false);
+      const _Float16 h0 = hs[0], h1 = hs[1];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const uint32_t u = (uint32_t)T.kw[kk];
@@ -207,13 +210,16 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
           const v8h ka = v8h{k0[0], k0[1], k1[0], k1[1], k2[0], k2[1], k3[0], k3[1]};
           acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[kk], acc, 0, 0, 0);
         }
-        // row r's scores of keys key0 + 4h + e, in log2 units; masked keys -inf
+        // row r's scores of keys key0 + 4h + e, in log2 units.  A tile below vis_all is
+        // visible to every row and takes no mask (rows past R hold a zero query: finite scores,
+        // never written); otherwise masked keys are -inf.
         float p[4];
         bool up = false;
+        const bool full = key0 + 16 <= vis_all;   // wave-uniform
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = key0 + 4 * h + e;
-          const bool vis = j < Nk && (causal ? j <= qpos : qpos >= 0);
+          const bool vis = full || (j < Nk && (causal ? j <= qpos : qpos >= 0));
           p[e] = vis ? acc[e] * qs : NEG;
           up |= p[e] > m + kLazy;   // also the first visible key (m = -inf)
         }
@@ -229,10 +235,18 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
             m = tmax;
           }
         }
+        if (full) {   // every score finite, so m is too
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p[e] = p[e] == NEG ? 0.0f : __builtin_amdgcn_exp2f(p[e] - m);   // m may still be -inf
-          lpart += p[e];
+          for (int e = 0; e < 4; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(p[e] - m);
+            lpart += p[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            p[e] = p[e] == NEG ? 0.0f : __builtin_amdgcn_exp2f(p[e] - m);   // m may still be -inf
+            lpart += p[e];
+          }
         }
         const v4h pb = v4h{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
         // O^T += V^T P^T over the 8 channel blocks; V codes of channel 16 cb + r, tokens 4h..4h+3
@@ -257,13 +271,18 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
   // O^T: lane (r, h) holds row r, channels 16 cb + 4h + e; the V area becomes [4][16][128] floats
   __syncthreads();   // every wave is done with V
   float(*sh_o)[16][DK] = reinterpret_cast<float(*)[16][DK]>(vl);
+  // the lane's indices again from the thread id (an opaque copy: keeping the set-up's values
+  // alive across the key loop would cost registers there)
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int mr = (int)(tid & 15u), mh = (int)((tid >> 4) & 3u);
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sh_o[wv][r][16 * cb + 4 * h + e] = o[cb][e];
-  if (h == 0) {
-    sh_m[wv][r] = m;
-    sh_l[wv][r] = lrow;
+    for (int e = 0; e < 4; ++e) sh_o[wv][mr][16 * cb + 4 * mh + e] = o[cb][e];
+  if (mh == 0) {
+    sh_m[wv][mr] = m;
+    sh_l[wv][mr] = lrow;
   }
   __syncthreads();
   // merge the 4 waves; write this split's unnormalized O with its max and sum
