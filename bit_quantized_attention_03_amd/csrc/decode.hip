@@ -23,9 +23,10 @@
 //   * the running max moves only when a score passes it by 15 (log2 units), checked once per
 //     tile for the whole wave; P <= 2^15 stays finite in f16;
 //   * the workgroup's V codes and scales (512 tokens x 128 channels) go to LDS by direct
-//     global->LDS loads (channel rows padded to 272 bytes, so the 16 channel lanes of a read
-//     hit distinct banks), after each wave's K loads for its first 4 tiles; V's 2-byte pieces
-//     are then read from LDS;
+//     global->LDS loads (each channel row's 16-byte segments XOR-swizzled, so the 16 channel
+//     lanes of a read hit distinct banks), after each wave's K loads for its first 4 tiles;
+//     V's 2-byte pieces are then read from LDS, lane row r taking channels 8r..8r+7, whose
+//     8 scale bytes are one 8-byte read (UE4M3 scales convert to f16 in pairs, exactly);
 //   * a split writes only the R real rows of its partial O (not the 16 of the row group).
 // decode_combine_kernel merges the splits and writes O.
 #include "device.hpp"
@@ -58,18 +59,20 @@ typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
-// A UE4M3 scale byte's value: gfx950's E4M3 conversion (OCP E4M3, the format the quantizers
-// encode with; exact).
-__device__ __forceinline__ float ue4m3(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
-
 struct Tile {
   v4i kw;          // key (key0 + r)'s code bytes 16h..16h+15
   uint32_t ks2;    // its two scale bytes (groups 2h, 2h + 1)
 };
 
-constexpr int VROW = DEC_CHUNK / 2 + 16;            // LDS bytes of a channel's codes (padded)
-constexpr int VSC0 = DK * VROW;                      // LDS offset of the scales [32 groups][128]
-constexpr int VLDS = VSC0 + (DEC_CHUNK / 16) * DK;   // 38912 bytes
+// V in LDS: channel c's codes in a 256-byte row whose 16-byte segment s sits at s ^ vswz(c),
+// then the scales [32 token groups][128 channels].  The matrix product reads channels 8r + cb
+// in lanes r = 0..15, so the swizzle (r) puts the 16 lanes' 4-byte words in distinct banks.
+constexpr int VROW = DEC_CHUNK / 2;                  // LDS bytes of a channel's codes
+constexpr int VSC0 = DK * VROW;                      // LDS offset of the scales
+constexpr int VLDS = VSC0 + (DEC_CHUNK / 16) * DK;   // 36864 bytes
+constexpr int SH_ROW = DK + 4;                       // merge rows padded: 16 rows hit distinct banks
+static_assert(4 * 16 * SH_ROW * 4 <= VLDS, "the merge fits the V area");
+__device__ __forceinline__ uint32_t vswz(uint32_t c) { return (c >> 3) & 15u; }
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Up to four workgroups a CU (39 KB of LDS each): a register budget of 128 per lane.
@@ -158,21 +161,21 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
     for (int u = 0; u < DEPTH; ++u) load(u, ring[u]);
     // V of the chunk into LDS by direct global->LDS loads (no registers): a wave instruction
     // fills 1 KB of LDS, lane i its 16-byte slot i, and each lane fetches the global segment that
-    // belongs to its slot.  Code slots: row c (channel) x 17 (16 segments of the chunk's
-    // DEC_CHUNK/2 bytes + one padding slot); then the scale slots: 32 token groups x 8 segments.
-    // Segments past the padded cache fetch the row's last valid one (finite codes and scales;
-    // their keys are masked), padding slots fetch segment 0.
+    // belongs to its slot.  Code slots: row c (channel) x 16 physical segments, the logical
+    // segment being the physical one XOR vswz(c); then the scale slots: 32 token groups x 8
+    // segments.  Segments past the padded cache fetch the row's last valid one (finite codes and
+    // scales; their keys are masked).
     {
       constexpr int CODE_SLOTS = DK * (VROW / 16), SLOTS = CODE_SLOTS + (DEC_CHUNK / 16) * (DK / 16);
-      static_assert(SLOTS % 64 == 0, "whole wave instructions");
+      static_assert(SLOTS % 64 == 0 && VROW == 256, "whole wave instructions; 16 segments a row");
       const uint32_t cb0 = (uint32_t)j0 / 2u, nb = (uint32_t)hNp;      // code bytes of a channel row
       const uint32_t g0 = (uint32_t)j0 / 16u, ng = (uint32_t)(a.Np / 16);
       for (int k = wv; k < SLOTS / 64; k += 4) {
         const uint32_t slot = 64u * (uint32_t)k + (uint32_t)lane;
         const uint8_t* src;
         if (slot < (uint32_t)CODE_SLOTS) {
-          const uint32_t row = slot / (VROW / 16), seg = slot % (VROW / 16);
-          uint32_t at = cb0 + 16u * (seg < DEC_CHUNK / 32 ? seg : 0u);
+          const uint32_t row = slot >> 4, seg = (slot & 15u) ^ vswz(row);
+          uint32_t at = cb0 + 16u * seg;
           at = at < nb ? at : nb - 16u;
           src = vc + row * nb + at;
         } else {
@@ -195,10 +198,10 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
         const int key0 = j0 + kl0;
         // S^T = K Q^T over the 4 channel slices
         v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        // K in f16: the E2M1 pairs times the group's scale pair (exact: E2M1 x UE4M3)
-        // the two UE4M3 scale bytes to f16 in one conversion (E4M3 values are exact in f16)
-      const v2h hs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(T.ks2, 1.0f, false);
-      const _Float16 h0 = hs[0], h1 = hs[1];
+        // K in f16: the E2M1 pairs times the group's scale pair (exact: E2M1 x UE4M3); the two
+        // UE4M3 scale bytes go to f16 in one conversion (E4M3 values are exact in f16)
+        const v2h hs = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(T.ks2, 1.0f, false);
+        const _Float16 h0 = hs[0], h1 = hs[1];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const uint32_t u = (uint32_t)T.kw[kk];
@@ -249,14 +252,21 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
           }
         }
         const v4h pb = v4h{(_Float16)p[0], (_Float16)p[1], (_Float16)p[2], (_Float16)p[3]};
-        // O^T += V^T P^T over the 8 channel blocks; V codes of channel 16 cb + r, tokens 4h..4h+3
-        const uint32_t vo = (uint32_t)kl0 / 2u + 2u * (uint32_t)h, so = VSC0 + ((uint32_t)kl0 / 16u) * DK;
+        // O^T += V^T P^T over the 8 channel blocks: block cb gives lane row r channel 8r + cb
+        // (codes of tokens 4h..4h+3: two bytes; the 8 scale bytes of channels 8r..8r+7 are
+        // adjacent and convert to f16 in pairs)
+        const uint32_t vo = (uint32_t)kl0 / 2u + 2u * (uint32_t)h;
+        const uint32_t vrow = (uint32_t)r * (8u * VROW) + ((((vo >> 4) ^ (uint32_t)r) << 4) | (vo & 15u));
+        const uint2 sw = *(const uint2*)(vl + VSC0 + ((uint32_t)kl0 / 16u) * DK + 8u * (uint32_t)r);
+        const v2h vs01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw.x, 1.0f, false);
+        const v2h vs23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw.x, 1.0f, true);
+        const v2h vs45 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw.y, 1.0f, false);
+        const v2h vs67 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw.y, 1.0f, true);
+        const _Float16 vsc8[8] = {vs01[0], vs01[1], vs23[0], vs23[1], vs45[0], vs45[1], vs67[0], vs67[1]};
 #pragma unroll
         for (int cb = 0; cb < 8; ++cb) {
-          const uint32_t ch = 16u * (uint32_t)cb + (uint32_t)r;
-          const uint32_t vw = *(const uint16_t*)(vl + ch * VROW + vo);
-          const _Float16 vsc = (_Float16)ue4m3(vl[so + ch]);   // exact in f16
-          const v2h sc2 = v2h{vsc, vsc};
+          const uint32_t vw = *(const uint16_t*)(vl + vrow + (uint32_t)cb * VROW);   // channel 8r + cb
+          const v2h sc2 = v2h{vsc8[cb], vsc8[cb]};
           const v2h d0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 0) * sc2;   // exact: E2M1 x UE4M3
           const v2h d1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(vw, 1.0f, 1) * sc2;
           const v4h va = v4h{d0[0], d0[1], d1[0], d1[1]};
@@ -268,9 +278,9 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
   // this wave's row sums: row r's keys sit in lanes r + 16h
   float lrow = lpart + __shfl_xor(lpart, 16);
   lrow += __shfl_xor(lrow, 32);
-  // O^T: lane (r, h) holds row r, channels 16 cb + 4h + e; the V area becomes [4][16][128] floats
+  // O^T: lane (r, h) holds row r, channels 8 (4h + e) + cb; the V area becomes [4][16][SH_ROW]
   __syncthreads();   // every wave is done with V
-  float(*sh_o)[16][DK] = reinterpret_cast<float(*)[16][DK]>(vl);
+  float(*sh_o)[16][SH_ROW] = reinterpret_cast<float(*)[16][SH_ROW]>(vl);
   // the lane's indices again from the thread id (an opaque copy: keeping the set-up's values
   // alive across the key loop would cost registers there)
   uint32_t tid = threadIdx.x;
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
 #pragma unroll
   for (int cb = 0; cb < 8; ++cb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sh_o[wv][mr][16 * cb + 4 * mh + e] = o[cb][e];
+    for (int e = 0; e < 4; ++e) sh_o[wv][mr][8 * (4 * mh + e) + cb] = o[cb][e];
   if (mh == 0) {
     sh_m[wv][mr] = m;
     sh_l[wv][mr] = lrow;
