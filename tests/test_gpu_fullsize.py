@@ -29,9 +29,29 @@ FULL = [
 
 @pytest.mark.parametrize("name,causal,variant", FULL)
 def test_full_size_sampled_parity(name, causal, variant):
-    from bit_quantized_attention_03_amd import sage
     w = I.workload(name)
     print(f"[case] full size {name} causal={causal} variant={variant}", flush=True)
+    _sampled_parity(w, causal, variant)
+
+
+LARGE = [
+    # a ragged sequence four times the longest workload's, GQA 2:1, causal
+    (dict(B=1, Hq=2, Hkv=1, N=131149), True),
+    # B * H at the library's limit of 65535 (heads index a launch dimension)
+    (dict(B=3, Hq=21845, Hkv=21845, N=16, D=64), False),
+]
+
+
+@pytest.mark.parametrize("ov,causal", LARGE)
+def test_large_sizes_sampled_parity(ov, causal):
+    w = I.workload("llm_int8", **ov)
+    print(f"[case] large {ov} causal={causal}", flush=True)
+    _sampled_parity(w, causal, "int8")
+
+
+def _sampled_parity(w, causal, variant):
+    from bit_quantized_attention_03_amd import sage
+    name = w.name
     q, k, v = I.make_qkv(w, seed=0)
     B, Hq, N, D = q.shape
     kg = k.cuda()
