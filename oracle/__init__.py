@@ -288,7 +288,7 @@ class _AttnArgs(C.Structure):
         ("v_lp", C.c_void_p), ("v_s", C.c_void_p), ("v_e8", C.c_void_p),
         ("bh_begin", C.c_int64), ("bh_end", C.c_int64), ("qb_begin", C.c_int64), ("qb_end", C.c_int64),
         ("threads", C.c_int32),
-        ("out", C.c_void_p), ("lse", C.c_void_p),
+        ("out", C.c_void_p), ("lse", C.c_void_p), ("p_mode", C.c_int32),
     ]
 
 
@@ -315,6 +315,7 @@ class AttnOperands:
     v_lp: Optional[np.ndarray] = None
     v_s: Optional[np.ndarray] = None
     v_e8: Optional[np.ndarray] = None
+    p_mode: int = 0   # NVFP4 P: 0 max-scaling, 1 / 2 ScaleSearch per 16-key block (as quant_nvfp4)
 
 
 def attention(ops: AttnOperands, B: int, Hq: int, Hkv: int, N: int, D: int, causal: bool, sm_scale: float,
@@ -354,6 +355,7 @@ def attention(ops: AttnOperands, B: int, Hq: int, Hkv: int, N: int, D: int, caus
     a.threads = int(threads or hardware_threads())
     a.out = out.ctypes.data
     a.lse = lse.ctypes.data if lse is not None else None
+    a.p_mode = int(ops.p_mode)
     _load().orc_attention(C.byref(a))
     return (out, lse) if want_lse else out
 

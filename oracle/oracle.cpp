@@ -411,6 +411,49 @@ float nv_block_sse(const float* x, float s, uint8_t* codes_out) {
   return se[0];
 }
 
+// One 16-element block's UE4M3 scale under scale mode `mode` (0, 1, 2 as above); writes the
+// block's E2M1 codes and the index of the winning candidate in the full list (0: max-scale).
+uint8_t nv_choose_scale(const float* vals, int mode, uint8_t* codes, int* chosen) {
+  static const double* grid = [] {
+    static double g[8];
+    for (int k = 0; k < 8; ++k) g[k] = (double)(float)(0.85 + k * 0.3 / 7.0);
+    return g;
+  }();
+  float amax = 0.0f;
+  for (int j = 0; j < 16; ++j) amax = std::max(amax, std::fabs(vals[j]));
+  float smax = amax / 6.0f;
+  // cand[i] < 0 marks a candidate that does not exist (offset outside 0x01..0x7E);
+  // the reported index is the position in the full list either way.
+  std::vector<int> cand;
+  uint8_t c0 = e4m3_encode(smax);
+  if (c0 == 0) c0 = 0x01;
+  cand.push_back(c0);
+  if (mode == 1) {
+    for (int k = 0; k < 8; ++k) {
+      uint8_t ck = e4m3_encode((float)(smax * (float)grid[k]));
+      if (ck == 0) ck = 0x01;
+      cand.push_back(ck);
+    }
+  } else if (mode == 2) {
+    const int offs[8] = {-2, -1, 1, 2, 3, 4, 5, 6};
+    for (int f : offs) {
+      int ck = (int)c0 + f;
+      cand.push_back(ck >= 0x01 && ck <= 0x7E ? ck : -1);
+    }
+  }
+  uint8_t best_c = (uint8_t)cand[0];
+  float best = nv_block_sse(vals, (float)e4m3_decode(best_c), codes);
+  int best_i = 0;
+  for (size_t i = 1; i < cand.size(); ++i) {
+    if (cand[i] < 0) continue;
+    uint8_t cc[16];
+    float sse = nv_block_sse(vals, (float)e4m3_decode((uint8_t)cand[i]), cc);
+    if (sse < best) { best = sse; best_c = (uint8_t)cand[i]; best_i = (int)i; std::memcpy(codes, cc, 16); }
+  }
+  if (chosen) *chosen = best_i;
+  return best_c;
+}
+
 void orc_quant_nvfp4(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N, int64_t D, int axis, int mode,
                      int hadamard, uint8_t* codes, uint8_t* scales,
                      uint8_t* chosen /* nullable: index of winning candidate */) {
@@ -419,48 +462,18 @@ void orc_quant_nvfp4(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t 
   int64_t Np = (N + 63) / 64 * 64;
   int64_t rows = axis == 0 ? N : D;
   int64_t len = axis == 0 ? D : Np;
-  double grid[8];
-  for (int k = 0; k < 8; ++k) grid[k] = (double)(float)(0.85 + k * 0.3 / 7.0);
   for (int64_t b = 0; b < B; ++b)
     for (int64_t h = 0; h < H; ++h)
       for (int64_t r = 0; r < rows; ++r)
         for (int64_t g0 = 0; g0 < len; g0 += G) {
           float vals[16];
-          float amax = 0.0f;
           for (int64_t j = 0; j < G; ++j) {
             int64_t t = axis == 0 ? r : g0 + j, c = axis == 0 ? g0 + j : r;
             vals[j] = t < N ? x[idx4(b, h, t, c, H, N, D)] : 0.0f;
-            amax = std::max(amax, std::fabs(vals[j]));
           }
-          float smax = amax / 6.0f;
-          // cand[i] < 0 marks a candidate that does not exist (offset outside 0x01..0x7E);
-          // the reported index is the position in the full list either way.
-          std::vector<int> cand;
-          uint8_t c0 = e4m3_encode(smax);
-          if (c0 == 0) c0 = 0x01;
-          cand.push_back(c0);
-          if (mode == 1) {
-            for (int k = 0; k < 8; ++k) {
-              uint8_t ck = e4m3_encode((float)(smax * (float)grid[k]));
-              if (ck == 0) ck = 0x01;
-              cand.push_back(ck);
-            }
-          } else if (mode == 2) {
-            const int offs[8] = {-2, -1, 1, 2, 3, 4, 5, 6};
-            for (int f : offs) {
-              int ck = (int)c0 + f;
-              cand.push_back(ck >= 0x01 && ck <= 0x7E ? ck : -1);
-            }
-          }
-          uint8_t best_c = (uint8_t)cand[0], best_codes[16];
-          float best = nv_block_sse(vals, (float)e4m3_decode(best_c), best_codes);
+          uint8_t best_codes[16];
           int best_i = 0;
-          for (size_t i = 1; i < cand.size(); ++i) {
-            if (cand[i] < 0) continue;
-            uint8_t cc[16];
-            float sse = nv_block_sse(vals, (float)e4m3_decode((uint8_t)cand[i]), cc);
-            if (sse < best) { best = sse; best_c = (uint8_t)cand[i]; best_i = (int)i; std::memcpy(best_codes, cc, 16); }
-          }
+          const uint8_t best_c = nv_choose_scale(vals, mode, best_codes, &best_i);
           int64_t srow = ((b * H + h) * rows + r), si = scale_index(b * H + h, r, g0 / G, rows, len / G, axis);
           scales[si] = best_c;
           if (chosen) chosen[si] = (uint8_t)best_i;
@@ -586,6 +599,7 @@ struct orc_attn_args {
   int32_t threads;
   double* out;   // [B,Hq,N,D]; only rows of the subset are written
   double* lse;   // nullable [B,Hq,N]: m + log(l) in natural-log units
+  int32_t p_mode;  // P_NVFP4_MXFP8: the 16-key blocks' scale rule (0 max-scaling, 1 or 2 ScaleSearch)
 };
 
 namespace {
@@ -595,7 +609,7 @@ double mx_p_value(double p, int e) {  // E2M1 at exponent e (exact scaling)
 }
 
 // Quantize one row of Ptilde over a tile (n valid keys; invalid keys are 0) in place.
-void quantize_p_row(double* p, int64_t n, int fmt) {
+void quantize_p_row(double* p, int64_t n, int fmt, int p_mode) {
   if (fmt == P_EXACT) return;
   if (fmt == P_BF16) { for (int64_t j = 0; j < n; ++j) p[j] = bf16_decode(bf16_encode((float)p[j])); return; }
   if (fmt == P_E4M3) { for (int64_t j = 0; j < n; ++j) p[j] = e4m3_decode(e4m3_encode((float)(p[j] * 448.0))); return; }
@@ -608,14 +622,13 @@ void quantize_p_row(double* p, int64_t n, int fmt) {
     }
     return;
   }
-  if (fmt == P_NVFP4_MXFP8) {  // NVFP4 max-scaling per 16 keys, then FP8 with E8M0 per 32 keys
+  if (fmt == P_NVFP4_MXFP8) {  // NVFP4 per 16 keys (scale by p_mode), then FP8 with E8M0 per 32 keys
     for (int64_t g0 = 0; g0 < n; g0 += 16) {
-      float amax = 0.0f;
-      for (int64_t j = g0; j < std::min(n, g0 + 16); ++j) amax = std::max(amax, (float)std::fabs(p[j]));
-      uint8_t sc = e4m3_encode(amax / 6.0f);
-      if (sc == 0) sc = 0x01;
-      float s = (float)e4m3_decode(sc), r = 1.0f / s;
-      for (int64_t j = g0; j < std::min(n, g0 + 16); ++j) p[j] = e2m1_decode(e2m1_encode((float)p[j] * r)) * s;
+      float vals[16];
+      for (int64_t j = 0; j < 16; ++j) vals[j] = g0 + j < n ? (float)p[g0 + j] : 0.0f;
+      uint8_t codes[16];
+      const float s = (float)e4m3_decode(nv_choose_scale(vals, p_mode, codes, nullptr));
+      for (int64_t j = g0; j < std::min(n, g0 + 16); ++j) p[j] = e2m1_decode(codes[j - g0]) * s;
     }
     for (int64_t g0 = 0; g0 < n; g0 += 32) {
       double A = 0.0;
@@ -741,7 +754,7 @@ void orc_attention(const orc_attn_args* a) {
             psum += P[jj];
           }
           l[ii] = l[ii] * alpha + psum;
-          quantize_p_row(P.data(), C, a->p_fmt);
+          quantize_p_row(P.data(), C, a->p_fmt, a->p_mode);
           std::fill(acc.begin(), acc.end(), 0.0);
           for (int64_t jj = 0; jj < C; ++jj) {
             if (P[jj] == 0.0) continue;

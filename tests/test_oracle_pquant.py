@@ -6,8 +6,11 @@ rebuilt here from the algorithm's statement with independent pieces: Ptilde from
 (scores are exact: small integer Q, K and sm_scale = 1/8), nearest-value searches over the
 enumerated E2M1 / E4M3 grids (ties to the even code), torch's bf16 and E4M3 casts, and a
 brute-force search for the smallest block exponent.  Covered: the 32-key MX blocks, the
-16-key NVFP4 blocks followed by FP8 with E8M0 per 32 keys, P x 448 for E4M3, the
-denominator on the unquantized Ptilde, and the running max across two tiles.
+16-key NVFP4 blocks followed by FP8 with E8M0 per 32 keys (max-scaling, or ScaleSearch over
+the 0.85-1.15 grid or the page's bit offsets, rebuilt here from the rule: candidates from
+torch's E4M3 cast, squared errors in fp32 summed as a pairwise tree, first minimum wins),
+P x 448 for E4M3, the denominator on the unquantized Ptilde, and the running max across two
+tiles.
 """
 import numpy as np
 import pytest
@@ -52,7 +55,40 @@ def _smallest_exp(a, qmax):
     return max(-127, e)
 
 
-def _quant_p(pt, fmt):
+def _e4m3_code(x):
+    """E4M3 code of fp32 x >= 0 by torch's cast (RNE, saturating)."""
+    v = float(torch.tensor([float(x)], dtype=torch.float32).to(torch.float8_e4m3fn).float()[0])
+    return int(np.searchsorted(E4M3_VALS, v))
+
+
+def _nv_scale(blk, mode):
+    """The 16-key block's UE4M3 scale value under max-scaling (0) or ScaleSearch (1 grid,
+    2 bit offsets)."""
+    smax = np.float32(blk.max()) / np.float32(6.0)
+    c0 = max(_e4m3_code(smax), 1)
+    cands = [c0]
+    if mode == 1:
+        for k in range(8):
+            g = np.float32(0.85 + k * 0.3 / 7.0)
+            cands.append(max(_e4m3_code(np.float32(smax * g)), 1))
+    elif mode == 2:
+        cands += [c0 + f for f in (-2, -1, 1, 2, 3, 4, 5, 6) if 1 <= c0 + f <= 0x7E]
+    best, best_s = None, None
+    for c in cands:
+        s = np.float32(E4M3_VALS[c])
+        r = np.float32(1.0) / s
+        xh = (_nearest((blk * r).astype(np.float32), E2M1_VALS) * s).astype(np.float32)
+        se = ((blk - xh).astype(np.float32) ** 2).astype(np.float32)
+        w = 1
+        while w < 16:                                          # pairwise tree in index order
+            se[0:16:2 * w] = (se[0:16:2 * w] + se[w:16:2 * w]).astype(np.float32)
+            w *= 2
+        if best is None or se[0] < best:
+            best, best_s = se[0], float(s)
+    return best_s
+
+
+def _quant_p(pt, fmt, p_mode=0):
     """Phat of one tile row (fp32 Ptilde values, as float64 array)."""
     if fmt == oracle.P_EXACT:
         return pt
@@ -72,9 +108,7 @@ def _quant_p(pt, fmt):
     xh = np.empty_like(pt)
     for g in range(0, len(pt), 16):
         blk = pt[g:g + 16].astype(np.float32)
-        smax = np.float32(blk.max()) / np.float32(6.0)
-        s = float(torch.tensor([float(smax)]).to(torch.float8_e4m3fn).float()[0])
-        s = s if s > 0 else 2.0 ** -9
+        s = _nv_scale(blk, p_mode)
         r = np.float32(1.0) / np.float32(s)
         xh[g:g + 16] = _nearest((blk * r).astype(np.float32), E2M1_VALS) * s
     for g in range(0, len(pt), 32):
@@ -84,7 +118,7 @@ def _quant_p(pt, fmt):
     return out
 
 
-def _expected(q, k, n_tiles, fmt):
+def _expected(q, k, n_tiles, fmt, p_mode=0):
     """Online softmax over 64-key tiles with Phat from _quant_p; O[i, j] = weight of key j."""
     S = (q @ k.T) * 0.125                                      # exact: small integers / 8
     N = S.shape[1]
@@ -101,7 +135,7 @@ def _expected(q, k, n_tiles, fmt):
             Pt = Pt.astype(np.float32).astype(np.float64)
         l = l * alpha + Pt.sum(axis=1)
         O *= alpha[:, None]
-        O[:, cols] += np.stack([_quant_p(Pt[i], fmt) for i in range(S.shape[0])])
+        O[:, cols] += np.stack([_quant_p(Pt[i], fmt, p_mode) for i in range(S.shape[0])])
         m = mnew
     return O / l[:, None]
 
@@ -123,3 +157,23 @@ def test_p_quantization_seen_through_one_hot_v(fmt, N):
     assert np.max(np.abs(out - want)) <= 1e-12 * np.max(np.abs(want))
     if fmt != oracle.P_EXACT:   # the quantizer really changed P (the check is not vacuous)
         assert np.max(np.abs(want - _expected(q, k, N // 64, oracle.P_EXACT))) > 1e-6
+
+
+@pytest.mark.parametrize("p_mode", [1, 2])
+@pytest.mark.parametrize("N", [64, 128])
+def test_p_scalesearch_seen_through_one_hot_v(p_mode, N):
+    """NVFP4 P with each 16-key block's scale chosen by ScaleSearch: the output matches the
+    rebuild, and differs from max-scaling (the search changes some blocks' scales)."""
+    D = N
+    rng = np.random.default_rng(200 + N + p_mode)
+    q = rng.integers(-1, 2, size=(N, D)).astype(np.float64)
+    k = rng.integers(-1, 2, size=(N, D)).astype(np.float64)
+    v = np.eye(N, D)
+    to16 = lambda a: I.bits16(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).reshape(1, 1, N, D))
+    ops = oracle.AttnOperands(qk_fmt=oracle.QK_HI, p_fmt=oracle.P_NVFP4_MXFP8, v_fmt=oracle.V_HI, q_hi=to16(q),
+                              k_hi=to16(k), v_hi=to16(v), p_mode=p_mode)
+    out = oracle.attention(ops, 1, 1, 1, N, D, False, 0.125)[0, 0]
+    want = _expected(q, k, N // 64, oracle.P_NVFP4_MXFP8, p_mode)
+    assert np.max(np.abs(out - want)) <= 1e-12 * np.max(np.abs(want))
+    plain = _expected(q, k, N // 64, oracle.P_NVFP4_MXFP8, 0)
+    assert np.max(np.abs(want - plain)) > 1e-6
