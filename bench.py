@@ -73,7 +73,8 @@ def load_traffic(workload: str, causal: bool, variant: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float, hadamard: bool = False):
+def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float, hadamard: bool = False,
+                 p_search: int = 0):
     """The oracle as it stands, on whole (b, h) heads of the same workload (CPU tensors q, k,
     v), until ~budget_s."""
     import oracle
@@ -92,7 +93,7 @@ def cpu_baseline(w, q, k, v, causal: bool, variant: str, budget_s: float, hadama
         hk = h // g
         qs, ks_, vs = (q[b:b + 1, h:h + 1].contiguous(), k[b:b + 1, hk:hk + 1].contiguous(),
                        v[b:b + 1, hk:hk + 1].contiguous())
-        oracle_pass(qs, ks_, vs, causal, variant, threads=threads, hadamard=hadamard)
+        oracle_pass(qs, ks_, vs, causal, variant, threads=threads, hadamard=hadamard, p_search=p_search)
         ops += 4.0 * w.N * w.N * w.D / (2.0 if causal else 1.0)
         done.append(f"({b},{h})")
         if time.perf_counter() - t0 > budget_s:
@@ -252,6 +253,9 @@ def main():
     ap.add_argument("--causal", action="store_true", help="causal mask (the thrift workload is always causal)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--p-search", type=int, default=0, choices=(0, 1, 2),
+                    help="nvfp4_search only: each 16-key block of P picks its scale by ScaleSearch "
+                         "(1: the 0.85-1.15 grid, 2: the bit offsets) instead of max-scaling")
     ap.add_argument("--hadamard", action="store_true",
                     help="Hadamard incoherence processing of Q and K_s inside their quantizers")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -327,7 +331,8 @@ def main():
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         out = sage.attn_fwd(qq, kq, vq, causal, pf, block_mask=mask,
-                            q_hi=q if mask is not None else None, k_hi=ks if mask is not None else None)
+                            q_hi=q if mask is not None else None, k_hi=ks if mask is not None else None,
+                            p_search=args.p_search if pf == sage.NVFP4 else 0)
         if record:
             e1.record(stream)
             ev.append((e0, e1))
@@ -368,14 +373,16 @@ def main():
                             "smooth_k + quantize + sink_select (first and last valid K block in bf16) + attn_fwd"
                             if variant == "sink" else
                             "smooth_k (mean) + quantize (Q, V; K with the smoothing fused) + attn_fwd")
-                   + (" (Q, K_s Hadamard-transformed in their quantizers)" if args.hadamard else "")},
+                   + (" (Q, K_s Hadamard-transformed in their quantizers)" if args.hadamard else "")
+                   + (f" (P's 16-key blocks scaled by ScaleSearch mode {args.p_search})" if args.p_search else "")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "attn_fwd", "kernel_ms": round(attn_ms, 4),
                      "qk_pv_peak": round(mixed, 1), "qk_pv_frac": round(achieved / mixed, 4)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, variant, args.cpu_seconds, args.hadamard)
+        rec["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, causal, variant, args.cpu_seconds, args.hadamard,
+                                           args.p_search)
     print(json.dumps(rec))
 
 

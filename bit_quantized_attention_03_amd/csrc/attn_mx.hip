@@ -126,7 +126,60 @@ struct MxDma {
 __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) { return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
 __device__ __forceinline__ v8i pad8(v4i lo) { return v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0}; }
 
-template <int D, bool CAUSAL, bool FP4, bool OUT_BF16>
+// ScaleSearch for one 16-key block of P held in one lane ("Search Your Block Floating Point
+// Scales!", Method > ScaleSearch, applied to P): besides the max-scale code c0, try the
+// candidates of scale mode PS (1: fp32(smax * g_k) for the 8 grid multipliers g_k = 0.85 +
+// k * 0.3 / 7; 2: the bit offsets -2, -1, 1 .. 6 on c0 that stay within 0x01..0x7E) and keep
+// the first with the least squared error: e = x - E2M1(x * fp32(1 / s)) * s, e * e summed in
+// fp32 as a pairwise tree in key order.
+__device__ __forceinline__ float p_block_sse(const float (&x)[16], uint32_t c) {
+  const float s = e4m3_to_f32(c), r = 1.0f / s;
+  float se[16];
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[i] * r, x[i + 1] * r, 1.0f, 0);
+    const auto xh = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+    const float e0 = x[i] - xh[0] * s, e1 = x[i + 1] - xh[1] * s;
+    se[i] = e0 * e0;
+    se[i + 1] = e1 * e1;
+  }
+#pragma unroll
+  for (int w = 1; w < 16; w *= 2)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2 * w) se[i] = se[i] + se[i + w];
+  return se[0];
+}
+
+template <int PS>
+__device__ __forceinline__ uint32_t p_scale_search(const float (&x)[16], float smax, uint32_t c0) {
+  uint32_t best_c = c0;
+  float best = p_block_sse(x, c0);
+  if constexpr (PS == 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      constexpr float g[8] = {(float)(0.85 + 0 * 0.3 / 7.0), (float)(0.85 + 1 * 0.3 / 7.0), (float)(0.85 + 2 * 0.3 / 7.0),
+                              (float)(0.85 + 3 * 0.3 / 7.0), (float)(0.85 + 4 * 0.3 / 7.0), (float)(0.85 + 5 * 0.3 / 7.0),
+                              (float)(0.85 + 6 * 0.3 / 7.0), (float)(0.85 + 7 * 0.3 / 7.0)};
+      uint32_t ck = f32_to_e4m3(smax * g[k]);
+      ck = ck == 0 ? 1u : ck;
+      const float e = p_block_sse(x, ck);
+      if (e < best) { best = e; best_c = ck; }
+    }
+  } else if constexpr (PS == 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = j < 2 ? j - 2 : j - 1;   // -2, -1, 1, 2, .., 6
+      const int ck = (int)c0 + f;
+      if (ck >= 0x01 && ck <= 0x7E) {
+        const float e = p_block_sse(x, (uint32_t)ck);
+        if (e < best) { best = e; best_c = (uint32_t)ck; }
+      }
+    }
+  }
+  return best_c;
+}
+
+template <int D, bool CAUSAL, bool FP4, bool OUT_BF16, int PS>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   using L = MxLayout<D, FP4>;
   constexpr int NCC = D / 32;     // 32-channel output chunks
@@ -321,6 +374,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
         const float amax = __builtin_amdgcn_exp2f(__builtin_fmaf(mb[bb], dq, -moff));
         uint32_t c0 = f32_to_e4m3(amax / 6.0f);
         c0 = c0 == 0 ? 1u : c0;
+        if constexpr (PS != 0) c0 = p_scale_search<PS>(s[bb], amax / 6.0f, c0);
         sc[bb] = e4m3_to_f32(c0);
         rc[bb] = 1.0f / sc[bb];
         // largest |xhat| of the block: E2M1 rounding is monotonic, so it is the max element's
@@ -407,10 +461,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool FP4, bool OUT_BF16>
+template <int D, bool CAUSAL, bool FP4, bool OUT_BF16, int PS>
 hipError_t launch_mx_cfg(const MxParams& p, hipStream_t st) {
   using L = MxLayout<D, FP4>;
-  auto kern = attn_mx_kernel<D, CAUSAL, FP4, OUT_BF16>;
+  auto kern = attn_mx_kernel<D, CAUSAL, FP4, OUT_BF16, PS>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
@@ -421,9 +475,16 @@ hipError_t launch_mx_cfg(const MxParams& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool CAUSAL, bool FP4>
+template <bool CAUSAL, bool FP4, int PS>
 hipError_t dispatch_mx(const MxParams& p, bool out_bf16, hipStream_t st) {
-  return out_bf16 ? launch_mx_cfg<128, CAUSAL, FP4, true>(p, st) : launch_mx_cfg<128, CAUSAL, FP4, false>(p, st);
+  return out_bf16 ? launch_mx_cfg<128, CAUSAL, FP4, true, PS>(p, st) : launch_mx_cfg<128, CAUSAL, FP4, false, PS>(p, st);
+}
+
+template <bool CAUSAL>
+hipError_t dispatch_nv(const MxParams& p, bool out_bf16, int p_mode, hipStream_t st) {
+  if (p_mode == 1) return dispatch_mx<CAUSAL, false, 1>(p, out_bf16, st);
+  if (p_mode == 2) return dispatch_mx<CAUSAL, false, 2>(p, out_bf16, st);
+  return dispatch_mx<CAUSAL, false, 0>(p, out_bf16, st);
 }
 
 }  // namespace
@@ -442,8 +503,8 @@ hipError_t launch_attn_mx(const AttnArgs& a, int nvfp4_variant, hipStream_t st) 
   p.total_wg = a.B * a.Hq * p.nPairs;
   p.sm_log2 = a.sm_scale * LOG2E;
   const bool causal = a.causal != 0, fp4 = nvfp4_variant == 0;
-  if (causal) return fp4 ? dispatch_mx<true, true>(p, a.out_bf16, st) : dispatch_mx<true, false>(p, a.out_bf16, st);
-  return fp4 ? dispatch_mx<false, true>(p, a.out_bf16, st) : dispatch_mx<false, false>(p, a.out_bf16, st);
+  if (fp4) return causal ? dispatch_mx<true, true, 0>(p, a.out_bf16, st) : dispatch_mx<false, true, 0>(p, a.out_bf16, st);
+  return causal ? dispatch_nv<true>(p, a.out_bf16, a.p_scale_mode, st) : dispatch_nv<false>(p, a.out_bf16, a.p_scale_mode, st);
 }
 
 }  // namespace sage

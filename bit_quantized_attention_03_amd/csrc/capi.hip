@@ -188,6 +188,11 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   a.v_is_f16 = v->fmt == SAGE_FP16;
   a.mask = p->block_mask; a.q_hi = (const uint16_t*)p->q_hi; a.k_hi = (const uint16_t*)p->k_hi;
   a.out = out; a.out_bf16 = out_dt == SAGE_BF16;
+  a.p_scale_mode = (int)p->p_scale_mode;
+  if (p->p_scale_mode != SAGE_SCALE_ABSMAX && p->p_scale_mode != SAGE_SCALE_SEARCH &&
+      p->p_scale_mode != SAGE_SCALE_SEARCH_OFFSETS)
+    return SAGE_EINVAL;
+  if (p->p_scale_mode != SAGE_SCALE_ABSMAX && p->p_fmt != SAGE_NVFP4) return SAGE_EINVAL;
 
   if (q->fmt == SAGE_INT8 && k->fmt == SAGE_INT8) {
     if (!empty && (!q->scales || !k->scales)) return SAGE_EINVAL;

@@ -75,7 +75,7 @@ static_assert(4 * 16 * SH_ROW * 4 <= VLDS, "the merge fits the V area");
 __device__ __forceinline__ uint32_t vswz(uint32_t c) { return (c >> 3) & 15u; }
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Up to four workgroups a CU (39 KB of LDS each): a register budget of 128 per lane.
+// Up to four workgroups a CU (36 KB of LDS each): a register budget of 128 per lane.
 template <bool F16>
 __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t vl[VLDS];   // V codes + scales; later the merge

@@ -56,6 +56,7 @@ struct AttnArgs {
   const uint8_t* mask; const uint16_t* q_hi; const uint16_t* k_hi;
   void* out;
   int out_bf16;
+  int p_scale_mode;   // NVFP4 P: 0 max-scaling, 1 / 2 ScaleSearch per 16-key block
 };
 hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st);
 hipError_t launch_attn_mx(const AttnArgs& a, int nvfp4_variant, hipStream_t st);

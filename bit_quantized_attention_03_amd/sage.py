@@ -37,7 +37,8 @@ class QTensorC(C.Structure):
 
 class AttnParamsC(C.Structure):
     _fields_ = [("causal", C.c_int32), ("sm_scale", C.c_float), ("p_fmt", C.c_int),
-                ("block_mask", C.c_void_p), ("q_hi", C.c_void_p), ("k_hi", C.c_void_p), ("hi_dt", C.c_int)]
+                ("block_mask", C.c_void_p), ("q_hi", C.c_void_p), ("k_hi", C.c_void_p), ("hi_dt", C.c_int),
+                ("p_scale_mode", C.c_int)]
 
 
 _lib = None
@@ -187,12 +188,15 @@ def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
 def attn_fwd(q: QT, k: QT, v: QT, causal: bool, p_fmt: int, sm_scale: float = 0.0,
              block_mask: Optional[torch.Tensor] = None, q_hi: Optional[torch.Tensor] = None,
              k_hi: Optional[torch.Tensor] = None, out_dtype: torch.dtype = torch.float32,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+             out: Optional[torch.Tensor] = None, p_search: int = ABSMAX) -> torch.Tensor:
+    """Fused attention on quantized operands.  p_search (NVFP4 P only): ABSMAX, SEARCH or
+    SEARCH_OFFSETS, the rule by which each 16-key block of P picks its scale."""
     B, Hq, N, D = q.shape
     dev = q.codes.device
     if out is None:
         out = torch.empty((B, Hq, N, D), dtype=out_dtype, device=dev)
-    params = AttnParamsC(int(causal), float(sm_scale), p_fmt, _ptr(block_mask), _ptr(q_hi), _ptr(k_hi), BF16)
+    params = AttnParamsC(int(causal), float(sm_scale), p_fmt, _ptr(block_mask), _ptr(q_hi), _ptr(k_hi), BF16,
+                         int(p_search))
     qc, kc, vc = q.c(), k.c(), v.c()
     _check("sage_attn_fwd", lib().sage_attn_fwd(C.byref(qc), C.byref(kc), C.byref(vc), C.byref(params), _ptr(out),
                                                 _TORCH_FMT[out.dtype], _stream()))
@@ -268,13 +272,15 @@ class Pass:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str = "int8",
             sm_scale: float = 0.0, thrift_frac: float = 0.05, search_mode: int = SEARCH,
             out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False, hadamard: bool = False,
-            sink_first: int = 1, sink_last: int = 1) -> Pass:
+            sink_first: int = 1, sink_last: int = 1, p_search: int = ABSMAX) -> Pass:
     """K smoothing -> block quantization -> (Thrift selection) -> fused attention.  K_s is only
     materialized when Thrift needs it (or keep_smoothed); otherwise K is quantized with the
     smoothing applied on the fly (identical codes).  hadamard: Q and K_s are quantized after
     the orthogonal Hadamard transform of their rows (QK^T unchanged; V and Thrift's bf16
     tiles take the original rows).  variant "sink": INT8 tiles except each Q block's first
-    sink_first and last sink_last valid K blocks, which run in bf16 (a static Thrift mask)."""
+    sink_first and last sink_last valid K blocks, which run in bf16 (a static Thrift mask).
+    p_search (variant "nvfp4_search"): the rule by which each 16-key block of P picks its
+    scale (ABSMAX, SEARCH or SEARCH_OFFSETS)."""
     B, Hq, N, D = q.shape
     need_ks = variant in ("thrift", "sink") or keep_smoothed
     mean, ks = smooth_k(k, want_smoothed=need_ks)
@@ -308,7 +314,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
         qq = nvfp4_to_mxfp8(quantize(q, NVFP4, (1, 16), search_mode, hadamard), False)
         kq = nvfp4_to_mxfp8(quant_k(NVFP4, (1, 16), search_mode), False)
         vq = nvfp4_to_mxfp8(quantize(v, NVFP4, (16, 1), search_mode), True)
-        out = attn_fwd(qq, kq, vq, causal, NVFP4, sm_scale, out_dtype=out_dtype)
+        out = attn_fwd(qq, kq, vq, causal, NVFP4, sm_scale, out_dtype=out_dtype, p_search=p_search)
     else:
         raise ValueError(f"unknown variant {variant!r}; one of {VARIANTS}")
     return Pass(mean, ks, qq, kq, vq, mask, out)

@@ -92,6 +92,12 @@ typedef struct {
   const void* q_hi;           /* 16-bit Q   [B, Hq,  N, D] read for masked tiles (else NULL) */
   const void* k_hi;           /* 16-bit K_s [B, Hkv, N, D] read for masked tiles (else NULL) */
   sage_fmt hi_dt;             /* dtype of q_hi / k_hi: SAGE_BF16 */
+  sage_scale_mode p_scale_mode; /* p_fmt SAGE_NVFP4 only: how each 16-key block of P picks its UE4M3
+                                 scale before the FP8 conversion.  SAGE_SCALE_ABSMAX (max-scaling),
+                                 or SAGE_SCALE_SEARCH / SAGE_SCALE_SEARCH_OFFSETS: the ScaleSearch
+                                 rule of sage_quantize_blocks applied to the block of fp32 P
+                                 ("Search Your Block Floating Point Scales!", Method > ScaleSearch).
+                                 Must be SAGE_SCALE_ABSMAX for every other p_fmt (else SAGE_EINVAL). */
 } sage_attn_params;
 
 /* Library version string (static storage). */

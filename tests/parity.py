@@ -41,7 +41,7 @@ def check_out(gpu: np.ndarray, orc: np.ndarray, what: str = ""):
 
 def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str,
                 bh=None, qb=None, frac: float = 0.05, search_mode: int = 1, threads=None, hadamard: bool = False,
-                sink=(1, 1)):
+                sink=(1, 1), p_search: int = 0):
     """The whole quantize-and-attend pass on the oracle, from the same 16-bit inputs.
     hadamard: Q and K_s are quantized after the Hadamard transform of their rows."""
     dt = I.dtype_code(q.dtype)
@@ -87,7 +87,7 @@ def oracle_pass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
         v8, ve = oracle.nvfp4_to_mxfp8(vc, vsc, N, D, 1)
         res.update(q_codes=q8, q_scales=qe, k_codes=k8, k_scales=ke, v_codes=v8, v_scales=ve)
         ops = oracle.AttnOperands(qk_fmt=oracle.QK_MXFP8, p_fmt=oracle.P_NVFP4_MXFP8, v_fmt=oracle.V_MXFP8, q_lp=q8,
-                                  q_e8=qe, k_lp=k8, k_e8=ke, v_lp=v8, v_e8=ve)
+                                  q_e8=qe, k_lp=k8, k_e8=ke, v_lp=v8, v_e8=ve, p_mode=p_search)
     else:
         raise ValueError(variant)
     res["out"] = oracle.attention(ops, B, Hq, Hkv, N, D, causal, 1.0 / math.sqrt(D), bh=bh, qb=qb, threads=threads)

@@ -99,6 +99,14 @@ def test_validation_before_launch(L):
     mis = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0002, shp)
     m128 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, shp)
     assert L.sage_attn_fwd(C.byref(mis), C.byref(m128), C.byref(m128), C.byref(p4), 0x1000_0000, sage.FP32, None) == -3
+    # P's ScaleSearch: a known mode, and NVFP4 P only
+    qi = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, shp)
+    vb = sage.QTensorC(sage.BF16, 0x1000_0000, None, shp)
+    for p_fmt, mode in ((sage.BF16, 1), (sage.MXFP4, 2), (sage.NVFP4, 5)):
+        pp = sage.AttnParamsC(0, 0.0, p_fmt, None, None, None, sage.BF16, mode)
+        vv = vb if p_fmt == sage.BF16 else m128
+        qq = qi if p_fmt == sage.BF16 else m128
+        assert L.sage_attn_fwd(C.byref(qq), C.byref(qq), C.byref(vv), C.byref(pp), 0x1000_0000, sage.FP32, None) == -1
     # mixed operand sets are not built
     p8 = sage.AttnParamsC(0, 0.0, sage.NVFP4, None, None, None, sage.BF16)
     assert L.sage_attn_fwd(C.byref(m128), C.byref(m128), C.byref(m128), C.byref(p8), 0x1000_0000, sage.FP32, None) == -2

@@ -362,6 +362,26 @@ def test_attention_parity(name, ov, causal, variant):
     print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
 
 
+@pytest.mark.parametrize("p_search", [1, 2])
+@pytest.mark.parametrize("causal,N", [(False, 333), (True, 512)])
+def test_attention_p_scalesearch(p_search, causal, N):
+    """NVFP4 P with each 16-key block's scale chosen by ScaleSearch inside the kernel (grid or
+    bit offsets): parity with the oracle's same rule, and a result that differs from
+    max-scaling (the search does change scales)."""
+    sage = _sage()
+    w = I.workload("fp4_search", B=1, Hq=2, Hkv=2, N=N)
+    q, k, v = I.make_qkv(w, seed=0)
+    print(f"[case] P ScaleSearch mode {p_search} N={N} causal={causal}", flush=True)
+    qc, kc, vc = _cuda(q, k, v)
+    res = sage.forward(qc, kc, vc, causal=causal, variant="nvfp4_search", p_search=p_search)
+    plain = sage.forward(qc, kc, vc, causal=causal, variant="nvfp4_search")
+    torch.cuda.synchronize()
+    orc = oracle_pass(q, k, v, causal, "nvfp4_search", p_search=p_search)
+    rel, cos = check_out(res.out.cpu().numpy(), orc["out"], f"P search {p_search} causal={causal}")
+    assert not torch.equal(res.out, plain.out)
+    print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f}")
+
+
 @pytest.mark.parametrize("direction", [1.0, -1.0])
 @pytest.mark.parametrize("causal", [False, True])
 def test_attention_running_max_moves_often(direction, causal):
