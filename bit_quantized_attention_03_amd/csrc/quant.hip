@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
       const v4f m0 = *(const v4f*)mu, m1 = *(const v4f*)(mu + 4);
 #pragma unroll
       for (int i = 0; i < CPT; ++i)
-        if (threadIdx.x + 256 * i < nchunk) raw[i] = smooth_vals<F16>(raw[i], m0, m1);
+        if ((int)threadIdx.x + 256 * i < nchunk) raw[i] = smooth_vals<F16>(raw[i], m0, m1);
     } else {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
