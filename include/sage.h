@@ -17,6 +17,8 @@
  *    launch, so on a validation error no output has been touched.  SAGE_EHIP reports a
  *    failed launch (hipGetLastError after the enqueue).
  *  - Calls are stateless and thread-safe; calls on different streams may overlap.
+ *  - A call enqueues kernels only (no memset, copy, allocation or synchronisation), so it can
+ *    be captured into a HIP graph and replayed; replays equal eager calls bit for bit.
  *  - Empty calls: when a call's tensors hold no elements (B = 0 or N = 0; for decode, no
  *    new tokens), it validates its shapes and arguments, touches no buffer and returns
  *    SAGE_OK.  Its data pointers may then be null (PyTorch gives an empty tensor a null data
