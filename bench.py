@@ -144,11 +144,23 @@ def run_decode(args, w):
     stream = torch.cuda.current_stream()
     ev = []
 
+    call = lambda: sage.decode(q, kq, vq, False)
+    if args.graph:   # the call captured once into a HIP graph; each step replays it
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            call()
+        stream.wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        call = graph.replay
+
     def step(record):
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-        out = sage.decode(q, kq, vq, False)
+        out = call()
         if record:
             e1.record(stream)
             ev.append((e0, e1))
@@ -184,8 +196,8 @@ def run_decode(args, w):
         "data": "synthetic (seeded PCG64; N(0,1) queries, keys and values)",
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.N, "D": w.D,
                    "causal": False, "variant": "decode", "input_dtype": "bfloat16",
-                   "step": "decode attention of the new tokens against the NVFP4 KV cache (split + combine); "
-                           "ops counted as 4*B*Hq*Nq*Nk*d"},
+                   "step": "decode attention of the new tokens against the NVFP4 KV cache (split + combine"
+                           + (", replayed from a HIP graph" if args.graph else "") + "); ops counted as 4*B*Hq*Nq*Nk*d"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
                      "frac": round(achieved / 8000.0, 4), "traffic": load_traffic(w.name, False, "decode"),
                      "kernel": "decode (split + combine)",
@@ -256,6 +268,8 @@ def main():
     ap.add_argument("--p-search", type=int, default=0, choices=(0, 1, 2),
                     help="nvfp4_search only: each 16-key block of P picks its scale by ScaleSearch "
                          "(1: the 0.85-1.15 grid, 2: the bit offsets) instead of max-scaling")
+    ap.add_argument("--graph", action="store_true",
+                    help="decode only: capture the call into a HIP graph once and time its replays")
     ap.add_argument("--hadamard", action="store_true",
                     help="Hadamard incoherence processing of Q and K_s inside their quantizers")
     ap.add_argument("--calibrate-copy", action="store_true",
