@@ -51,7 +51,6 @@ namespace sage {
 namespace {
 
 constexpr int QB = 128, KT = 64, NWAVES = 8, NTHREADS = 64 * NWAVES;
-constexpr float LOG2E = 1.4426950408889634f;
 // 1.5 * 2^23 and its bit pattern: an int32 x with |x| < 2^22 added to the pattern gives the
 // float kMagic + x exactly.
 constexpr float kMagic = 12582912.0f;
