@@ -29,6 +29,8 @@
 #include "attn_common.hpp"
 #include "kernels.hpp"
 
+#include <atomic>
+
 namespace sage {
 namespace {
 
@@ -465,10 +467,15 @@ template <int D, bool CAUSAL, bool FP4, bool OUT_BF16, int PS>
 hipError_t launch_mx_cfg(const MxParams& p, hipStream_t st) {
   using L = MxLayout<D, FP4>;
   auto kern = attn_mx_kernel<D, CAUSAL, FP4, OUT_BF16, PS>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  // The dynamic-LDS limit is set once per device (bit d of the mask: done on device d), from
+  // any thread; devices past 63 set it on every launch.
+  static std::atomic<uint64_t> attr_set{0};
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit == 0 || (attr_set.load(std::memory_order_acquire) & bit) == 0) {
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
-    attr_set = true;
+    attr_set.fetch_or(bit, std::memory_order_release);
   }
   if (p.total_wg == 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3((unsigned)p.total_wg), dim3(NTHREADS), L::TOTAL, st, p);
