@@ -77,6 +77,22 @@ def test_smooth_and_int8_bit_exact(name, ov):
                               s_o.view(np.uint32))
 
 
+def test_int8_ties_round_half_even_bit_exact():
+    # exact ties of x * (1/s) go to the even code on the GPU too (the same blocks as the oracle pin)
+    from tests.test_oracle_quant import int8_tie_input
+    sage = _sage()
+    xb, want = int8_tie_input()
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    print("[case] INT8 tie blocks", flush=True)
+    qt = sage.quantize(x, sage.INT8, (64, x.shape[-1]))
+    got = qt.codes.cpu().numpy().view(np.int8).reshape(want.shape)
+    assert np.array_equal(got, want)
+    c_o, s_o = oracle.quant_int8(xb, 0, 64)
+    assert np.array_equal(got, c_o)
+    assert np.array_equal(qt.scales.cpu().view(torch.float32).numpy().reshape(s_o.shape).view(np.uint32),
+                          s_o.view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt,block,mode", [("INT8", (64, 128), 0), ("INT8", (100, 128), 0), ("INT8", (4096, 128), 0),
                                             ("MXFP4", (1, 32), 0), ("NVFP4", (1, 16), 1), ("NVFP4", (1, 16), 2)])
 def test_quantize_smoothed_equals_quantize_of_smoothed(fmt, block, mode):

@@ -103,6 +103,45 @@ def test_int8_on_grid_and_zero_block():
     assert scales[0, 0, 1] == 0.0 and np.all(got[0, 0, 64:128] == 0)
 
 
+# Exact ties of x * (1/s) between two integers, for three scales whose reciprocal is a power of
+# two (so x * (1/s) is exact): amax = 127 (s = 1), 63.5 (s = 0.5) and 254 (s = 2).  Rounding
+# half to even sends each tie to the even neighbour; half away from zero or truncation would
+# not.  Expected codes follow from that definition alone, written out by hand.
+INT8_TIE_BLOCKS = [
+    # (amax, [(x, expected code), ...])
+    (127.0, [(0.5, 0), (1.5, 2), (2.5, 2), (3.5, 4), (4.5, 4), (5.5, 6), (6.5, 6), (7.5, 8),
+             (64.5, 64), (100.5, 100), (125.5, 126), (126.5, 126)]),
+    (63.5, [(0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.25, 4), (31.25, 62), (31.75, 64), (63.25, 126)]),
+    (254.0, [(1.0, 0), (3.0, 2), (5.0, 2), (7.0, 4), (9.0, 4), (251.0, 126), (253.0, 126)]),
+]
+
+
+def int8_tie_input(D=64):
+    """One 64-token block per entry of INT8_TIE_BLOCKS: the block maximum amax at token 0,
+    channel 0, the ties (and their negatives) after it, zeros elsewhere.  Returns the bf16
+    input [1, 1, 64 * blocks, D] and the expected codes."""
+    nb = len(INT8_TIE_BLOCKS)
+    x = np.zeros((1, 1, 64 * nb, D), np.float32)
+    want = np.zeros(x.shape, np.int8)
+    for b, (amax, ties) in enumerate(INT8_TIE_BLOCKS):
+        t0 = 64 * b
+        x[0, 0, t0, 0] = amax; want[0, 0, t0, 0] = 127
+        for i, (v, c) in enumerate(ties):
+            t, ch = t0 + 1 + i // (D // 2), 2 * (i % (D // 2))
+            x[0, 0, t, ch], want[0, 0, t, ch] = v, c
+            x[0, 0, t, ch + 1], want[0, 0, t, ch + 1] = -v, -c
+    return _bf16(x), want
+
+
+def test_int8_ties_round_half_even():
+    # the fixed tie rule: round to nearest, ties to even
+    xb, want = int8_tie_input()
+    assert np.array_equal(_val(xb), _val(_bf16(_val(xb))))          # the ties are exact in bf16
+    codes, scales = oracle.quant_int8(xb, oracle.BF16, 64)
+    assert np.array_equal(scales[0, 0], np.array([a / 127 for a, _ in INT8_TIE_BLOCKS], np.float32))
+    assert np.array_equal(codes, want)
+
+
 # ---------------------------------------------------------------- FP8 per channel
 
 def test_fp8_channel_half_step(llm_small):
