@@ -21,6 +21,11 @@ bool empty_call(const sage_shape& s) { return s.B * s.H == 0 || s.N == 0; }
 bool is16(sage_fmt f) { return f == SAGE_BF16 || f == SAGE_FP16; }
 int64_t roundup(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int launched(hipError_t e) { return e == hipSuccess ? SAGE_OK : (e == hipErrorNotSupported ? SAGE_ENOTSUP : SAGE_EHIP); }
+bool block_is(const sage_qtensor* t, int32_t tokens, int32_t channels) {
+  return t->block.tokens == tokens && t->block.channels == channels;
+}
+// The attention kernels address tiles with 32-bit offsets (a channel-major V row spans Np bytes).
+constexpr int64_t ATTN_MAX_N = 1ll << 24;
 
 }  // namespace
 
@@ -172,6 +177,7 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   if (ks.B != qs.B || vs.B != qs.B || ks.N != qs.N || vs.N != qs.N || ks.D != qs.D || vs.D != qs.D || vs.H != ks.H)
     return SAGE_EINVAL;
   if (qs.H % ks.H != 0) return SAGE_EINVAL;
+  if (qs.N > ATTN_MAX_N) return SAGE_EINVAL;
   if (qs.D != 64 && qs.D != 128) return SAGE_ENOTSUP;
   if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
   if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
@@ -196,9 +202,11 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
 
   if (q->fmt == SAGE_INT8 && k->fmt == SAGE_INT8) {
     if (!empty && (!q->scales || !k->scales)) return SAGE_EINVAL;
+    if (!block_is(q, QBLK, (int32_t)qs.D) || !block_is(k, KBLK, (int32_t)ks.D)) return SAGE_EINVAL;
     if (is16(v->fmt) && p->p_fmt == SAGE_BF16) {
       if (p->block_mask) {
         if (!empty && (!p->q_hi || !p->k_hi)) return SAGE_EINVAL;
+        if (p->hi_dt == SAGE_FP16) return SAGE_ENOTSUP;
         if (p->hi_dt != SAGE_BF16) return SAGE_EINVAL;
         if (!aligned16(p->q_hi) || !aligned16(p->k_hi)) return SAGE_EALIGN;
       }
@@ -207,6 +215,7 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
     }
     if (v->fmt == SAGE_E4M3 && p->p_fmt == SAGE_E4M3) {
       if ((!empty && !v->scales) || p->block_mask) return SAGE_EINVAL;
+      if (!block_is(v, 0, 1)) return SAGE_EINVAL;
       if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
       return launched(launch_attn_int8(a, 1, stream));
     }
@@ -220,6 +229,7 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   if (qs.D != 128) return SAGE_ENOTSUP;   // the microscaled kernels are built for D = 128
   // scale bytes are read as dwords (4 per Q/K row, 2*D per V tile)
   if ((uintptr_t)q->scales % 4 || (uintptr_t)k->scales % 4 || (uintptr_t)v->scales % 4) return SAGE_EALIGN;
+  if (!block_is(q, 1, 32) || !block_is(k, 1, 32) || !block_is(v, 32, 1)) return SAGE_EINVAL;
   if (qs.B * qs.H == 0 || qs.N == 0) return SAGE_OK;
   return launched(launch_attn_mx(a, mx4 ? 0 : 1, stream));
 }
@@ -268,6 +278,7 @@ int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qten
   if (qs.N > ks.N || ks.N == 0) return SAGE_EINVAL;   // the new tokens are the cache's last positions
   if (ks.N > (1 << 26)) return SAGE_EINVAL;           // cache offsets are 32-bit (64 bytes a key)
   if (!is16(q_dt) || k->fmt != SAGE_NVFP4 || v->fmt != SAGE_NVFP4 || qs.D != 128) return SAGE_ENOTSUP;
+  if (!block_is(k, 1, 16) || !block_is(v, 16, 1)) return SAGE_EINVAL;
   if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
   if (!aligned16(q) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
   if ((uintptr_t)k->scales % 2) return SAGE_EALIGN;   // read as byte pairs

@@ -32,7 +32,7 @@ class Block(C.Structure):
 
 
 class QTensorC(C.Structure):
-    _fields_ = [("fmt", C.c_int), ("codes", C.c_void_p), ("scales", C.c_void_p), ("shape", Shape)]
+    _fields_ = [("fmt", C.c_int), ("codes", C.c_void_p), ("scales", C.c_void_p), ("shape", Shape), ("block", Block)]
 
 
 class AttnParamsC(C.Structure):
@@ -135,14 +135,16 @@ def quantized_bytes(fmt: int, block: tuple, shape: tuple):
 
 @dataclass
 class QT:
-    """A quantized operand: format, code and scale tensors, logical [B,H,N,D] shape."""
+    """A quantized operand: format, code and scale tensors, logical [B,H,N,D] shape and the
+    quantizer block (tokens, channels) the codes were made with ((0, 0) for 16-bit tensors)."""
     fmt: int
     codes: torch.Tensor
     scales: Optional[torch.Tensor]
     shape: tuple
+    block: tuple = (0, 0)
 
     def c(self) -> QTensorC:
-        return QTensorC(self.fmt, _ptr(self.codes), _ptr(self.scales), Shape(*self.shape))
+        return QTensorC(self.fmt, _ptr(self.codes), _ptr(self.scales), Shape(*self.shape), Block(*self.block))
 
 
 def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX, hadamard: bool = False) -> QT:
@@ -155,7 +157,7 @@ def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX, hadama
     scales = torch.empty(max(sb, 16), dtype=torch.uint8, device=x.device)
     _check("sage_quantize_blocks", lib().sage_quantize_blocks(_ptr(x), _TORCH_FMT[x.dtype], _shape(x), fmt,
                                                               Block(*block), mode, _ptr(codes), _ptr(scales), _stream()))
-    return QT(fmt, codes[:cb], scales[:sb], tuple(x.shape))
+    return QT(fmt, codes[:cb], scales[:sb], tuple(x.shape), tuple(block))
 
 
 def quantize_smoothed(k: torch.Tensor, mean: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX,
@@ -169,7 +171,7 @@ def quantize_smoothed(k: torch.Tensor, mean: torch.Tensor, fmt: int, block: tupl
     _check("sage_quantize_smoothed", lib().sage_quantize_smoothed(_ptr(k), _TORCH_FMT[k.dtype], _shape(k), _ptr(mean), fmt,
                                                                   Block(*block), mode, _ptr(codes), _ptr(scales),
                                                                   _stream()))
-    return QT(fmt, codes[:cb], scales[:sb], tuple(k.shape))
+    return QT(fmt, codes[:cb], scales[:sb], tuple(k.shape), tuple(block))
 
 
 def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
@@ -182,7 +184,7 @@ def nvfp4_to_mxfp8(qt: QT, along_tokens: bool) -> QT:
     e8 = torch.empty(max(n // 32, 16), dtype=torch.uint8, device=qt.codes.device)
     _check("sage_nvfp4_to_mxfp8", lib().sage_nvfp4_to_mxfp8(_ptr(qt.codes), _ptr(qt.scales), Shape(*qt.shape),
                                                             int(along_tokens), _ptr(f8), _ptr(e8), _stream()))
-    return QT(MXFP8, f8[:n], e8[:n // 32], qt.shape)
+    return QT(MXFP8, f8[:n], e8[:n // 32], qt.shape, (32, 1) if along_tokens else (1, 32))
 
 
 def attn_fwd(q: QT, k: QT, v: QT, causal: bool, p_fmt: int, sm_scale: float = 0.0,
@@ -195,7 +197,12 @@ def attn_fwd(q: QT, k: QT, v: QT, causal: bool, p_fmt: int, sm_scale: float = 0.
     dev = q.codes.device
     if out is None:
         out = torch.empty((B, Hq, N, D), dtype=out_dtype, device=dev)
-    params = AttnParamsC(int(causal), float(sm_scale), p_fmt, _ptr(block_mask), _ptr(q_hi), _ptr(k_hi), BF16,
+    hi_dt = BF16
+    if q_hi is not None or k_hi is not None:
+        if q_hi is None or k_hi is None or q_hi.dtype != k_hi.dtype:
+            raise ValueError("q_hi and k_hi go together and share one 16-bit dtype")
+        hi_dt = _TORCH_FMT[q_hi.dtype]   # the library accepts bf16 only (fp16: not supported)
+    params = AttnParamsC(int(causal), float(sm_scale), p_fmt, _ptr(block_mask), _ptr(q_hi), _ptr(k_hi), hi_dt,
                          int(p_search))
     qc, kc, vc = q.c(), k.c(), v.c()
     _check("sage_attn_fwd", lib().sage_attn_fwd(C.byref(qc), C.byref(kc), C.byref(vc), C.byref(params), _ptr(out),

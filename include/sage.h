@@ -76,13 +76,17 @@ typedef struct { int64_t B, H, N, D; } sage_shape;
  *   SAGE_NVFP4: (1, 16) along D (Q, K)  or (16, 1) along tokens (V)                       */
 typedef struct { int32_t tokens, channels; } sage_block;
 
-/* A quantized (or 16-bit) operand of sage_attn_fwd; codes/scales in the layouts of
- * sage_quantize_blocks.  `shape` is the logical [B, H, N, D] of the tensor.             */
+/* A quantized (or 16-bit) operand of sage_attn_fwd / sage_decode_fwd; codes/scales in the
+ * layouts of sage_quantize_blocks.  `shape` is the logical [B, H, N, D] of the tensor and
+ * `block` the quantizer block the codes were made with: the attention reads one scale per
+ * block, so a block other than the one an operand set takes returns SAGE_EINVAL (it would
+ * read the scales at the wrong stride).  Unused (any value) for 16-bit tensors.           */
 typedef struct {
   sage_fmt fmt;
   const void* codes;   /* codes, or the 16-bit tensor itself for SAGE_BF16 / SAGE_FP16 */
   const void* scales;  /* NULL for 16-bit tensors */
   sage_shape shape;
+  sage_block block;
 } sage_qtensor;
 
 typedef struct {
@@ -93,7 +97,8 @@ typedef struct {
                                  K block) tile on bf16 Q and K_s (Thrift), 0 = INT8 */
   const void* q_hi;           /* 16-bit Q   [B, Hq,  N, D] read for masked tiles (else NULL) */
   const void* k_hi;           /* 16-bit K_s [B, Hkv, N, D] read for masked tiles (else NULL) */
-  sage_fmt hi_dt;             /* dtype of q_hi / k_hi: SAGE_BF16 */
+  sage_fmt hi_dt;             /* dtype of q_hi / k_hi: SAGE_BF16 (the masked tiles run on bf16 matrix
+                                 instructions); SAGE_FP16 returns SAGE_ENOTSUP, others SAGE_EINVAL */
   sage_scale_mode p_scale_mode; /* p_fmt SAGE_NVFP4 only: how each 16-key block of P picks its UE4M3
                                  scale before the FP8 conversion.  SAGE_SCALE_ABSMAX (max-scaling),
                                  or SAGE_SCALE_SEARCH / SAGE_SCALE_SEARCH_OFFSETS: the ScaleSearch
@@ -188,13 +193,16 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
  * evaluated per Q block of 128 rows over K tiles of 64 keys in ascending order with an fp32
  * running max and sum; P is quantized to p_fmt per tile before P.V.
  * Supported operand sets (Hq a multiple of Hkv = k->shape.H; q-head h reads kv-head
- * h / (Hq / Hkv)):
- *   q, k SAGE_INT8 (blocks 128 / 64 tokens) + v SAGE_BF16 | SAGE_FP16 + p SAGE_BF16
+ * h / (Hq / Hkv)), with the blocks each operand must carry:
+ *   q, k SAGE_INT8 (blocks (128, D) / (64, D)) + v SAGE_BF16 | SAGE_FP16 + p SAGE_BF16
  *        (+ optional block_mask with bf16 q_hi / k_hi)
- *   q, k SAGE_INT8 + v SAGE_E4M3 (per channel) + p SAGE_E4M3 (P scaled by 448)
- *   q, k SAGE_MXFP4 (along D) + v SAGE_MXFP4 (along tokens) + p SAGE_MXFP4 (per 32 keys)
- *   q, k SAGE_MXFP8 (along D) + v SAGE_MXFP8 (along tokens) + p SAGE_NVFP4 (max-scaled per
- *        16 keys, then to MXFP8 like sage_nvfp4_to_mxfp8)
+ *   q, k SAGE_INT8 (blocks (128, D) / (64, D)) + v SAGE_E4M3 (block (0, 1): per channel)
+ *        + p SAGE_E4M3 (P scaled by 448)
+ *   q, k SAGE_MXFP4 (block (1, 32): along D) + v SAGE_MXFP4 (block (32, 1): along tokens)
+ *        + p SAGE_MXFP4 (per 32 keys)
+ *   q, k SAGE_MXFP8 (block (1, 32)) + v SAGE_MXFP8 (block (32, 1)) + p SAGE_NVFP4 (max-scaled
+ *        per 16 keys, then to MXFP8 like sage_nvfp4_to_mxfp8)
+ * Tile offsets inside the kernels are 32-bit: N <= 2^24 (else SAGE_EINVAL).
  * out: [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16).  D in {64, 128} for the INT8 sets;
  * the microscaled sets take D = 128 (else SAGE_ENOTSUP) and 4-byte aligned scale arrays
  * (else SAGE_EALIGN); their running max is exact (P is quantized relative to it).        */
@@ -225,10 +233,10 @@ size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_b
  * the softmax sum of the unrounded P; sm_scale 0 selects 1 / sqrt(D).  q-head h reads KV
  * head h / (Hq / Hkv).
  *   q   [B,Hq,Nq,D] in q_dt (SAGE_BF16 | SAGE_FP16), 16-byte aligned;
- *   k   SAGE_NVFP4 along D, shape [B,Hkv,Nk,D]: codes [B,Hkv,Nk,D/2] (16-byte aligned), UE4M3
- *       scales [B,Hkv,Nk,D/16] (2-byte aligned) (sage_quantize_blocks with block (1, 16));
- *   v   SAGE_NVFP4 along the tokens, shape [B,Hkv,Nk,D]: codes [B,Hkv,D,Np/2], Np = Nk rounded
- *       up to 64 (16-byte aligned), UE4M3 scales [B,Hkv,Np/16,D] (block (16, 1));
+ *   k   SAGE_NVFP4 along D, block (1, 16), shape [B,Hkv,Nk,D]: codes [B,Hkv,Nk,D/2] (16-byte
+ *       aligned), UE4M3 scales [B,Hkv,Nk,D/16] (2-byte aligned);
+ *   v   SAGE_NVFP4 along the tokens, block (16, 1), shape [B,Hkv,Nk,D]: codes [B,Hkv,D,Np/2],
+ *       Np = Nk rounded up to 64 (16-byte aligned), UE4M3 scales [B,Hkv,Np/16,D];
  *   out [B,Hq,Nq,D] in out_dt (SAGE_FP32 | SAGE_BF16);
  *   workspace >= sage_decode_workspace_bytes(q shape, k shape) bytes of device memory
  *   (partial results of the key splits).

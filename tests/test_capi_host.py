@@ -71,7 +71,7 @@ def test_validation_before_launch(L):
                                   None) == -3
     # unsupported head dimension for attention
     s96 = sage.Shape(1, 1, 128, 96)
-    q96 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, s96)
+    q96 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, s96, sage.Block(128, 96))
     assert L.sage_attn_fwd(C.byref(q96), C.byref(q96), C.byref(q96), C.byref(p), 0x1000_0000, sage.FP32, None) == -2
     # search mode only for NVFP4
     assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 1, 0x2000_0000,
@@ -93,14 +93,14 @@ def test_validation_before_launch(L):
                                   0x1000_0000, 1 << 30, None) == -1
     assert L.thrift_workspace_bytes(wide, wide, 128, 64) == 0
     # microscaled attention: D = 128 only, dword-aligned scales
-    m64 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 128, 64))
+    m64 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 128, 64), sage.Block(1, 32))
     p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
     assert L.sage_attn_fwd(C.byref(m64), C.byref(m64), C.byref(m64), C.byref(p4), 0x1000_0000, sage.FP32, None) == -2
-    mis = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0002, shp)
-    m128 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, shp)
+    mis = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0002, shp, sage.Block(1, 32))
+    m128 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, shp, sage.Block(1, 32))
     assert L.sage_attn_fwd(C.byref(mis), C.byref(m128), C.byref(m128), C.byref(p4), 0x1000_0000, sage.FP32, None) == -3
     # P's ScaleSearch: a known mode, and NVFP4 P only
-    qi = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, shp)
+    qi = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, shp, sage.Block(128, 128))
     vb = sage.QTensorC(sage.BF16, 0x1000_0000, None, shp)
     for p_fmt, mode in ((sage.BF16, 1), (sage.MXFP4, 2), (sage.NVFP4, 5)):
         pp = sage.AttnParamsC(0, 0.0, p_fmt, None, None, None, sage.BF16, mode)
@@ -145,18 +145,70 @@ def test_validation_before_launch(L):
     assert L.sage_sink_blocks(shp, 128, 64, 1, 1, 1, None, None) == -1
     # decode: NVFP4 cache, D = 128, Nq <= Nk, workspace
     qd = sage.Shape(1, 4, 2, 128)
-    kn = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128))
+    kn = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128), sage.Block(1, 16))
+    vn = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128), sage.Block(16, 1))
     k8 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128))
-    short = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 1, 128))
+    short = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 1, 128), sage.Block(1, 16))
     assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(k8), C.byref(k8), 0, 0.0, 0x1000_0000, sage.FP32,
                              0x1000_0000, 1 << 30, None) == -2
     assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(short), C.byref(short), 0, 0.0, 0x1000_0000,
                              sage.FP32, 0x1000_0000, 1 << 30, None) == -1
-    assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(kn), C.byref(kn), 0, 0.0, 0x1000_0000, sage.FP32,
+    assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(kn), C.byref(vn), 0, 0.0, 0x1000_0000, sage.FP32,
                              None, 0, None) == -4
+    assert L.sage_decode_fwd(0x1000_0000, sage.BF16, qd, C.byref(kn), C.byref(kn), 0, 0.0, 0x1000_0000, sage.FP32,
+                             0x1000_0000, 1 << 30, None) == -1            # V's block runs along the tokens
     assert L.sage_decode_workspace_bytes(qd, sage.Shape(1, 2, 100, 128)) > 0
     # smoothing workspace
     assert L.sage_smooth_k(0x1000_0000, sage.BF16, shp, 0x1000_0000, None, None, 0, None) == -4
+
+
+def test_operand_blocks_dtypes_and_limits(L):
+    """The attention reads one scale per quantizer block, so each operand must carry the block
+    its operand set takes; masked tiles run on bf16 only; tile offsets cap N at 2^24."""
+    from bit_quantized_attention_03_amd import sage
+    shp = sage.Shape(1, 2, 256, 128)
+    a = 0x1000_0000
+    qi = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(128, 128))
+    ki = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(64, 128))
+    vb = sage.QTensorC(sage.BF16, a, None, shp)
+    p = sage.AttnParamsC(0, 0.0, sage.BF16, None, None, None, sage.BF16)
+    for bad_q, bad_k in (((64, 128), (64, 128)), ((128, 128), (128, 128)), ((128, 64), (64, 128)), ((0, 0), (64, 128))):
+        q = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(*bad_q))
+        k = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(*bad_k))
+        assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(vb), C.byref(p), a, sage.FP32, None) == -1
+    v8 = sage.QTensorC(sage.E4M3, a, a, shp, sage.Block(32, 1))
+    p8 = sage.AttnParamsC(0, 0.0, sage.E4M3, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(v8), C.byref(p8), a, sage.FP32, None) == -1
+    mq = sage.QTensorC(sage.MXFP4, a, a, shp, sage.Block(1, 32))
+    mv_wrong = sage.QTensorC(sage.MXFP4, a, a, shp, sage.Block(1, 32))
+    p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(mq), C.byref(mq), C.byref(mv_wrong), C.byref(p4), a, sage.FP32, None) == -1
+    # masked (Thrift / sink) tiles: bf16 Q and K_s only
+    pm16 = sage.AttnParamsC(0, 0.0, sage.BF16, a, a, a, sage.FP16)
+    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(pm16), a, sage.FP32, None) == -2
+    pm32 = sage.AttnParamsC(0, 0.0, sage.BF16, a, a, a, sage.FP32)
+    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(pm32), a, sage.FP32, None) == -1
+    # sequence length limit of the 32-bit tile offsets
+    big = sage.Shape(1, 1, (1 << 24) + 1, 128)
+    qb = sage.QTensorC(sage.INT8, a, a, big, sage.Block(128, 128))
+    kb = sage.QTensorC(sage.INT8, a, a, big, sage.Block(64, 128))
+    vbig = sage.QTensorC(sage.BF16, a, None, big)
+    assert L.sage_attn_fwd(C.byref(qb), C.byref(kb), C.byref(vbig), C.byref(p), a, sage.FP32, None) == -1
+    ok = sage.Shape(1, 1, 1 << 24, 128)
+    qk = sage.QTensorC(sage.INT8, None, None, ok, sage.Block(128, 128))   # passes the limit, then null codes
+    assert L.sage_attn_fwd(C.byref(qk), C.byref(qk), C.byref(qk), C.byref(p), a, sage.FP32, None) == -1
+
+
+def test_python_binding_rejects_fp16_masked_tiles():
+    """An fp16 pass with a block mask (Thrift or sink) raises a clean error instead of running
+    bf16 matrix instructions on fp16 bits."""
+    import torch
+    from bit_quantized_attention_03_amd import sage
+    x = torch.zeros(1, 1, 64, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):   # the pair must share a dtype
+        sage.attn_fwd(sage.QT(sage.INT8, x, x, (1, 1, 64, 64), (128, 64)), sage.QT(sage.INT8, x, x, (1, 1, 64, 64), (64, 64)),
+                      sage.QT(sage.FP16, x, None, (1, 1, 64, 64)), False, sage.BF16, q_hi=x, k_hi=x.bfloat16(),
+                      block_mask=x, out=torch.empty(0))
 
 
 def test_empty_calls_touch_no_pointer(L):
@@ -170,18 +222,21 @@ def test_empty_calls_touch_no_pointer(L):
         assert L.sage_quantize_smoothed(None, sage.BF16, s, None, sage.INT8, sage.Block(64, 128), 0, None, None,
                                         None) == 0
         assert L.sage_nvfp4_to_mxfp8(None, None, s, 1, None, None, None) == 0
-        qi = sage.QTensorC(sage.INT8, None, None, s)
+        qi = sage.QTensorC(sage.INT8, None, None, s, sage.Block(128, 128))
+        ki = sage.QTensorC(sage.INT8, None, None, s, sage.Block(64, 128))
         vb = sage.QTensorC(sage.BF16, None, None, s)
         p = sage.AttnParamsC(1, 0.0, sage.BF16, None, None, None, sage.BF16)
-        assert L.sage_attn_fwd(C.byref(qi), C.byref(qi), C.byref(vb), C.byref(p), None, sage.FP32, None) == 0
-        m4 = sage.QTensorC(sage.MXFP4, None, None, s)
+        assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(p), None, sage.FP32, None) == 0
+        m4 = sage.QTensorC(sage.MXFP4, None, None, s, sage.Block(1, 32))
+        m4v = sage.QTensorC(sage.MXFP4, None, None, s, sage.Block(32, 1))
         p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
-        assert L.sage_attn_fwd(C.byref(m4), C.byref(m4), C.byref(m4), C.byref(p4), None, sage.BF16, None) == 0
+        assert L.sage_attn_fwd(C.byref(m4), C.byref(m4), C.byref(m4v), C.byref(p4), None, sage.BF16, None) == 0
         assert L.thrift_select_blocks(None, None, sage.BF16, s, s, 128, 64, 0.05, 1, None, None, 0, None) == 0
         assert L.sage_sink_blocks(s, 128, 64, 1, 1, 1, None, None) == 0
     assert L.sage_smooth_k(None, sage.BF16, sage.Shape(0, 2, 64, 128), None, None, None, 0, None) == 0
-    kn = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128))   # no new tokens
-    assert L.sage_decode_fwd(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(kn), C.byref(kn), 0, 0.0, None,
+    kn = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128), sage.Block(1, 16))   # no new tokens
+    vn = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128), sage.Block(16, 1))
+    assert L.sage_decode_fwd(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(kn), C.byref(vn), 0, 0.0, None,
                              sage.FP32, None, 0, None) == 0
     assert L.sage_convert_f32(None, 0, sage.BF16, None, None) == 0
     # still validated: shapes, formats, and the non-empty outputs
@@ -190,8 +245,9 @@ def test_empty_calls_touch_no_pointer(L):
     assert L.sage_quantize_blocks(None, sage.BF16, sage.Shape(1, 2, 0, 96), sage.INT8, sage.Block(128, 96), 0x100,
                                   None, None, None) == -2                          # Hadamard needs D in {64, 128}
     assert L.sage_smooth_k(None, sage.BF16, sage.Shape(1, 2, 0, 128), None, None, None, 0, None) == -1   # means out
-    empty_cache = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 0, 128))
-    assert L.sage_decode_fwd(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(empty_cache), C.byref(empty_cache),
+    empty_cache = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 0, 128), sage.Block(1, 16))
+    empty_vcache = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 0, 128), sage.Block(16, 1))
+    assert L.sage_decode_fwd(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(empty_cache), C.byref(empty_vcache),
                              0, 0.0, None, sage.FP32, None, 0, None) == -1         # decode needs a cached key
 
 

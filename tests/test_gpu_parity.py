@@ -378,6 +378,18 @@ def test_attention_parity(name, ov, causal, variant):
     print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
 
 
+@pytest.mark.parametrize("variant", ["sink", "thrift"])
+def test_fp16_masked_tiles_rejected(variant):
+    # the masked tiles run on bf16 matrix instructions: fp16 Q and K_s get a clean error
+    sage = _sage()
+    w = I.workload("tiny_int8", N=512)
+    q, k, v = _cuda(*I.make_qkv(w, seed=3))
+    print(f"[case] fp16 {variant}", flush=True)
+    with pytest.raises(sage.SageError) as e:
+        sage.forward(q, k, v, causal=True, variant=variant)
+    assert e.value.status == -2
+
+
 @pytest.mark.parametrize("p_search", [1, 2])
 @pytest.mark.parametrize("causal,N", [(False, 333), (True, 512)])
 def test_attention_p_scalesearch(p_search, causal, N):
