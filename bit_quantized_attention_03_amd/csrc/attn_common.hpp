@@ -32,6 +32,13 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// INT8 score tiles are computed transposed (S^T = K Q^T, 32x32 blocks, keys on the accumulator
+// rows): accumulator row m of block b holds this key of the 64-key tile.  Lane half h of the
+// wave holds keys 32 h .. 32 h + 31 across its two blocks.
+__device__ __forceinline__ int tile_key(int b, int m) {
+  return ((m >> 2) & 1) * 32 + 16 * b + (m >> 3) * 4 + (m & 3);
+}
+
 // Workgroup -> (b*Hq + h, pair of Q blocks).  Consecutive work items go to one XCD
 // (workgroups are dealt round-robin over the 8 XCDs), so neighbouring heads share its L2.
 // Causal runs take four heads at a time and walk their pairs from the heaviest down, the four

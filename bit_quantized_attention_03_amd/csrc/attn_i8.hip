@@ -50,7 +50,8 @@
 namespace sage {
 namespace {
 
-constexpr int QB = 128, KT = 64, NWAVES = 8, NTHREADS = 64 * NWAVES;
+using namespace attn;
+
 // 1.5 * 2^23 and its bit pattern: an int32 x with |x| < 2^22 added to the pattern gives the
 // float kMagic + x exactly.
 constexpr float kMagic = 12582912.0f;
@@ -92,36 +93,9 @@ __device__ __forceinline__ int v_off(int row, int byte) {   // byte offset withi
 // FP8 V^T: chunk c (of 4) of channel row r at c ^ ((r >> 2) & 3).
 __device__ __forceinline__ int v8_off(int row, int c) { return row * KT + 16 * (c ^ ((row >> 2) & 3)); }
 
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
 // vmcnt(n), n < 16: wait until at most n vector memory operations of this wave are in flight
 template <int n>
 __device__ __forceinline__ void wait_vmem_n() { __builtin_amdgcn_s_waitcnt(0x0F70 | n); }
-// Workgroup barrier without a memory fence.  The loop's ordering needs are explicit: tile loads
-// are complete (wait_vmem) before the barrier that publishes them, and an LDS buffer is
-// overwritten only after the barrier following the matrix instructions that consumed its reads.
-// (__syncthreads would also drain the tile loads still in flight at every phase boundary.)
-__device__ __forceinline__ void phase_barrier() {
-  __asm__ volatile("" ::: "memory");   // LDS may change across a phase boundary (direct loads land
-  __builtin_amdgcn_s_barrier();       // unseen by the compiler): no LDS access moves across it
-  __asm__ volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ int tile_key(int b, int m) {   // accumulator row m of half b -> key in tile
-  return ((m >> 2) & 1) * 32 + 16 * b + (m >> 3) * 4 + (m & 3);
-}
-
-// v_permlane32_swap on (x, x) returns, in some order depending on the lane half, this lane's
-// value and the value of lane l ^ 32; max and sum of the pair are the same in both halves.
-__device__ __forceinline__ float halves_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float halves_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Direct global -> LDS tile copies by the 4 waves of group A.  Lane l of wave a in round i
 // fills LDS chunk (4i + a) * 64 + l; its source chunk (swizzle undone) is a per-lane
@@ -655,6 +629,8 @@ hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st) {
   }
   const bool thrift = a.mask != nullptr;
   const bool causal = a.causal != 0;
+  // plain INT8 Q.K with bf16 P.V: the software-pipelined kernel (fp16 V at D = 128 stays here)
+  if (!pv_fp8 && !thrift && !(a.v_is_f16 && a.D == 128)) return launch_attn_int8_pipe(a, st);
   if (a.D == 64) {
     if (causal) return pv_fp8 ? dispatch_rest<64, true, true>(p, thrift, a.v_is_f16, a.out_bf16, st)
                               : dispatch_rest<64, true, false>(p, thrift, a.v_is_f16, a.out_bf16, st);

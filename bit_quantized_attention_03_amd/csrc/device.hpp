@@ -51,6 +51,8 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+// bf16 pair (1, 1): with v_dot2_f32_bf16 it sums a packed pair into an fp32 accumulator
+__device__ __forceinline__ bf16x2_t bf16x2_ones() { return __builtin_bit_cast(bf16x2_t, 0x3F803F80u); }
 
 // ---- E4M3 ----------------------------------------------------------------------------
 __device__ __forceinline__ float clamp448(float x) { return __builtin_fminf(__builtin_fmaxf(x, -448.0f), 448.0f); }

@@ -59,6 +59,8 @@ struct AttnArgs {
   int p_scale_mode;   // NVFP4 P: 0 max-scaling, 1 / 2 ScaleSearch per 16-key block
 };
 hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st);
+// INT8 QK^T, bf16 P.V, no block mask: the software-pipelined kernel (attn_i8_pipe.hip).
+hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attn_mx(const AttnArgs& a, int nvfp4_variant, hipStream_t st);
 
 }  // namespace sage
