@@ -24,6 +24,7 @@ int launched(hipError_t e) { return e == hipSuccess ? SAGE_OK : (e == hipErrorNo
 bool block_is(const sage_qtensor* t, int32_t tokens, int32_t channels) {
   return t->block.tokens == tokens && t->block.channels == channels;
 }
+static_assert(SAGE_DECODE_NOALLOC_SCRATCH_BYTES == DECODE_SCRATCH_BYTES, "one scratch size");
 // The attention kernels address tiles with 32-bit offsets (a channel-major V row spans Np bytes).
 constexpr int64_t ATTN_MAX_N = 1ll << 24;
 
@@ -265,9 +266,11 @@ size_t sage_decode_workspace_bytes(sage_shape qs, sage_shape ks) {
   return decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
 }
 
-int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
-                    int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+namespace {
+// Validation shared by the two decode entry points; on SAGE_OK, *empty says whether there is
+// nothing to launch.
+int decode_check(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
+                 int causal, void* out, sage_fmt out_dt, bool* empty_out) {
   if (!k || !v || !shape_ok(qs)) return SAGE_EINVAL;
   const bool empty = empty_call(qs);   // no new tokens (or no batch): nothing is read
   if (!empty && (!q || !out || !k->codes || !k->scales || !v->codes || !v->scales)) return SAGE_EINVAL;
@@ -282,14 +285,45 @@ int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qten
   if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
   if (!aligned16(q) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
   if ((uintptr_t)k->scales % 2) return SAGE_EALIGN;   // read as byte pairs
-  const size_t need = decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
-  if (!aligned16(workspace)) return SAGE_EALIGN;
-  if (empty) return SAGE_OK;
+  *empty_out = empty;
+  return SAGE_OK;
+}
+
+int decode_launch(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
+                  int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, hipStream_t stream) {
+  const sage_shape& ks = k->shape;
   const float sc = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)qs.D);
   return launched(launch_decode((const uint16_t*)q, q_dt == SAGE_FP16, qs.B, qs.H, ks.H, qs.N, ks.N,
                                 (const uint8_t*)k->codes, (const uint8_t*)k->scales, (const uint8_t*)v->codes,
                                 (const uint8_t*)v->scales, causal, sc, out, out_dt == SAGE_BF16, workspace, stream));
+}
+}  // namespace
+
+int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
+                    int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  bool empty = false;
+  const int st = decode_check(q, q_dt, qs, k, v, causal, out, out_dt, &empty);
+  if (st != SAGE_OK) return st;
+  const sage_shape& ks = k->shape;
+  const size_t need = decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
+  if (!aligned16(workspace)) return SAGE_EALIGN;
+  if (empty) return SAGE_OK;
+  return decode_launch(q, q_dt, qs, k, v, causal, sm_scale, out, out_dt, workspace, stream);
+}
+
+int sage_decode_fwd_noalloc(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k, const sage_qtensor* v,
+                            int causal, float sm_scale, void* out, sage_fmt out_dt, hipStream_t stream) {
+  bool empty = false;
+  const int st = decode_check(q, q_dt, qs, k, v, causal, out, out_dt, &empty);
+  if (st != SAGE_OK) return st;
+  const sage_shape& ks = k->shape;
+  if (decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N) > SAGE_DECODE_NOALLOC_SCRATCH_BYTES) return SAGE_EWORKSPACE;
+  if (empty) return SAGE_OK;
+  void* scratch_at = nullptr;
+  if (decode_scratch(&scratch_at) != hipSuccess) return SAGE_EHIP;
+  return decode_launch(q, q_dt, qs, k, v, causal, sm_scale, out, out_dt, scratch_at, stream);
 }
 
 int sage_sink_blocks(sage_shape qs, int q_block, int k_block, int n_first, int n_last, int causal, uint8_t* mask_out,

@@ -32,6 +32,9 @@
 #include "device.hpp"
 #include "kernels.hpp"
 
+#include <atomic>
+#include <mutex>
+
 namespace sage {
 namespace {
 
@@ -404,6 +407,38 @@ hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, i
   decode_combine_kernel<<<(unsigned)(B * Hkv * R), DK, 0, st>>>(a.part_o, a.part_ml, Hq, Hkv, Nq, R, nsplit,
                                                                  out_bf16 ? 1 : 0, out);
   return hipGetLastError();
+}
+
+// ---- scratch of the allocation-free entry point (sage_decode_fwd_noalloc): the split
+// partials live in this array instead of a caller workspace.  Every GPU the library runs on
+// holds its own copy until the process ends; calls on one GPU share it.  In host code the
+// name is only a stand-in: kernels get the device address that decode_scratch looks up.
+static __device__ __align__(256) uint8_t scratch[DECODE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+std::mutex g_scratch_mu;
+}  // namespace
+
+hipError_t decode_scratch(void** p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* a = g_scratch[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {   // first call on this device: look the address up with the device current
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    a = g_scratch[dev].load(std::memory_order_relaxed);
+    if (a == nullptr) {
+      e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (a == nullptr) return hipErrorInvalidSymbol;
+      g_scratch[dev].store(a, std::memory_order_release);
+    }
+  }
+  *p = a;
+  return hipSuccess;
 }
 
 }  // namespace sage

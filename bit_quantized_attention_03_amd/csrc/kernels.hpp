@@ -39,6 +39,10 @@ hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, i
                          const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int causal,
                          float sm_scale, void* out, bool out_bf16, void* ws, hipStream_t st);
 // Static sink-and-recent block mask [BH, nQB, nKB] (blocks of 128 Q rows and 64 keys).
+// The allocation-free decode keeps its split partials in a static device array of this size
+// (SAGE_DECODE_NOALLOC_SCRATCH_BYTES); decode_scratch gives the current device's address of it.
+constexpr size_t DECODE_SCRATCH_BYTES = size_t(8) << 20;
+hipError_t decode_scratch(void** p);
 hipError_t launch_sink_mask(int64_t BH, int64_t N, int n_first, int n_last, int causal, uint8_t* mask, hipStream_t st);
 
 // Attention kernels.

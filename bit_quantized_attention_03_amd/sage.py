@@ -75,6 +75,8 @@ def lib():
         L.sage_decode_workspace_bytes.argtypes = [Shape, Shape]
         L.sage_decode_fwd.argtypes = [C.c_void_p, C.c_int, Shape, C.POINTER(QTensorC), C.POINTER(QTensorC), C.c_int,
                                       C.c_float, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]
+        L.sage_decode_fwd_noalloc.argtypes = [C.c_void_p, C.c_int, Shape, C.POINTER(QTensorC), C.POINTER(QTensorC),
+                                              C.c_int, C.c_float, C.c_void_p, C.c_int, C.c_void_p]
         _lib = L
     return _lib
 
@@ -250,6 +252,24 @@ def decode(q: torch.Tensor, k: QT, v: QT, causal: bool = False, sm_scale: float 
     _check("sage_decode_fwd", lib().sage_decode_fwd(_ptr(q), _TORCH_FMT[q.dtype], _shape(q), C.byref(kc), C.byref(vc),
                                                     int(causal), float(sm_scale), _ptr(out), _TORCH_FMT[out_dtype],
                                                     _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def decode_noalloc(q: torch.Tensor, k: QT, v: QT, out: torch.Tensor, causal: bool = False,
+                   sm_scale: float = 0.0) -> torch.Tensor:
+    """decode() without a workspace: the split partials go to the library's per-GPU scratch
+    array (sage_decode_fwd_noalloc).  The caller passes the output out [B,Hq,Nq,D] (fp32 or
+    bf16); nothing is allocated.  Calls that overlap on one GPU share the scratch and race."""
+    _dev(q, out)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out shape {tuple(out.shape)} != q shape {tuple(q.shape)}")
+    kc, vc = k.c(), v.c()
+    _check("sage_decode_fwd_noalloc",
+           lib().sage_decode_fwd_noalloc(_ptr(q), _TORCH_FMT[q.dtype], _shape(q), C.byref(kc), C.byref(vc),
+                                         int(causal), float(sm_scale), _ptr(out), _TORCH_FMT[out.dtype], _stream()))
     return out
 
 

@@ -246,6 +246,24 @@ int sage_decode_fwd(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qten
                     hipStream_t stream);
 size_t sage_decode_workspace_bytes(sage_shape qs, sage_shape ks);
 
+/* sage_decode_fwd without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and errors as sage_decode_fwd (bit-identical outputs), except that the
+ * split partials go to a scratch array that the library holds on each GPU it runs on, from
+ * this call's first use on that GPU until the process ends:
+ *   - scratch size SAGE_DECODE_NOALLOC_SCRATCH_BYTES; a call whose partials need more
+ *     (sage_decode_workspace_bytes(q shape, k shape) > the limit) returns SAGE_EWORKSPACE
+ *     before any launch;
+ *   - the call allocates nothing; its first call on a device looks the array up (no
+ *     allocation) with that device current, and the stream must belong to the current device;
+ *   - every call on a GPU shares that GPU's array: calls that overlap on one GPU (on
+ *     different streams, or from several threads) race on it and must be serialized by
+ *     the caller.  Calls in order on one stream are safe.                                    */
+#define SAGE_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int sage_decode_fwd_noalloc(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor* k,
+                            const sage_qtensor* v, int causal, float sm_scale, void* out, sage_fmt out_dt,
+                            hipStream_t stream);
+
 /* Sink-aware static block selection — "Search Your Block Floating Point Scales!" (Method >
  * ScaleSearchAttention: the first and the last blocks of the KV cache are kept at full
  * precision, the middle ones low-bit).  For every (b, q-head) and Q block qb, with kl its

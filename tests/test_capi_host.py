@@ -256,3 +256,34 @@ def test_python_binding_refuses_cpu_tensors():
     from bit_quantized_attention_03_amd import sage
     with pytest.raises(ValueError):
         sage.smooth_k(torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16))
+
+
+def test_decode_noalloc_validation(L):
+    """sage_decode_fwd_noalloc validates like sage_decode_fwd and refuses, before any launch,
+    a problem whose split partials exceed its scratch."""
+    from bit_quantized_attention_03_amd import sage
+    assert sage.DECODE_NOALLOC_SCRATCH_BYTES == 8 << 20
+    qb, kvb = sage.Shape(16, 64, 1, 128), sage.Shape(16, 64, 1 << 20, 128)
+    assert L.sage_decode_workspace_bytes(qb, kvb) > sage.DECODE_NOALLOC_SCRATCH_BYTES
+    kb = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, kvb, sage.Block(1, 16))
+    vb = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, kvb, sage.Block(16, 1))
+    assert L.sage_decode_fwd_noalloc(0x1000_0000, sage.BF16, qb, C.byref(kb), C.byref(vb), 0, 0.0, 0x1000_0000,
+                                     sage.FP32, None) == -4
+    # the checks shared with sage_decode_fwd
+    qd = sage.Shape(1, 4, 2, 128)
+    kn = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128), sage.Block(1, 16))
+    vn = sage.QTensorC(sage.NVFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128), sage.Block(16, 1))
+    k8 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 100, 128))
+    assert L.sage_decode_fwd_noalloc(0x1000_0000, sage.BF16, qd, C.byref(k8), C.byref(k8), 0, 0.0, 0x1000_0000,
+                                     sage.FP32, None) == -2
+    assert L.sage_decode_fwd_noalloc(0x1000_0000, sage.BF16, qd, C.byref(kn), C.byref(kn), 0, 0.0, 0x1000_0000,
+                                     sage.FP32, None) == -1                   # V's block runs along the tokens
+    assert L.sage_decode_fwd_noalloc(0x1000_0008, sage.BF16, qd, C.byref(kn), C.byref(vn), 0, 0.0, 0x1000_0000,
+                                     sage.FP32, None) == -3                   # q not 16-byte aligned
+    assert L.sage_decode_fwd_noalloc(0x1000_0000, sage.BF16, qd, C.byref(kn), C.byref(vn), 2, 0.0, 0x1000_0000,
+                                     sage.FP32, None) == -1                   # causal is 0 or 1
+    # no new tokens: nothing to do, nothing touched
+    ke = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128), sage.Block(1, 16))
+    ve = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128), sage.Block(16, 1))
+    assert L.sage_decode_fwd_noalloc(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(ke), C.byref(ve), 0, 0.0,
+                                     None, sage.FP32, None) == 0
