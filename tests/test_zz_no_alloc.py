@@ -51,3 +51,17 @@ def test_noalloc_decode_matches_workspace_decode(out_dtype):
     torch.cuda.synchronize()
     for want, out, case in zip(wants, outs, CASES):
         assert torch.equal(out, want), case
+
+
+def test_noalloc_decode_long_cache_many_splits():
+    """A long cache with one KV head: 1025 key splits, whose partials fill about 1 MiB of the
+    scratch; outputs stay bit-identical to the workspace call."""
+    sage = _sage()
+    B, Hq, Hkv, Nq, Nk = 1, 2, 1, 1, (1 << 19) + 77
+    print(f"[case] decode_noalloc many splits B,Hq,Hkv,Nq,Nk={B, Hq, Hkv, Nq, Nk}", flush=True)
+    q, kq, vq = _problem(sage, B, Hq, Hkv, Nq, Nk, seed=5)
+    want = sage.decode(q, kq, vq, True)
+    out = torch.full_like(want, float("nan"))
+    sage.decode_noalloc(q, kq, vq, out, True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, want)
