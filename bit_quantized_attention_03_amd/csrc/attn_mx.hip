@@ -126,7 +126,9 @@ struct MxDma {
 };
 
 __device__ __forceinline__ v8i cat8(v4i lo, v4i hi) { return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
-__device__ __forceinline__ v8i pad8(v4i lo) { return v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0}; }
+// An FP4 operand is 4 registers; the builtin's 8-register operand gets an undefined upper
+// half (the instruction does not read it), so no zeros are materialized per fragment.
+__device__ __forceinline__ v8i pad8(v4i lo) { return __builtin_shufflevector(lo, lo, 0, 1, 2, 3, -1, -1, -1, -1); }
 
 // ScaleSearch for one 16-key block of P held in one lane ("Search Your Block Floating Point
 // Scales!", Method > ScaleSearch, applied to P): besides the max-scale code c0, try the
@@ -134,7 +136,8 @@ __device__ __forceinline__ v8i pad8(v4i lo) { return v8i{lo[0], lo[1], lo[2], lo
 // k * 0.3 / 7; 2: the bit offsets -2, -1, 1 .. 6 on c0 that stay within 0x01..0x7E) and keep
 // the first with the least squared error: e = x - E2M1(x * fp32(1 / s)) * s, e * e summed in
 // fp32 as a pairwise tree in key order.
-__device__ __forceinline__ float p_block_sse(const float (&x)[16], uint32_t c) {
+template <class Row>
+__device__ __forceinline__ float p_block_sse(const Row& x, uint32_t c) {
   const float s = e4m3_to_f32(c), r = 1.0f / s;
   float se[16];
 #pragma unroll
@@ -152,8 +155,8 @@ __device__ __forceinline__ float p_block_sse(const float (&x)[16], uint32_t c) {
   return se[0];
 }
 
-template <int PS>
-__device__ __forceinline__ uint32_t p_scale_search(const float (&x)[16], float smax, uint32_t c0) {
+template <int PS, class Row>
+__device__ __forceinline__ uint32_t p_scale_search(const Row& x, float smax, uint32_t c0) {
   uint32_t best_c = c0;
   float best = p_block_sse(x, c0);
   if constexpr (PS == 1) {
@@ -289,16 +292,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
         if (FP4) kf[bb][kk] = pad8(*(const v4i*)(ks + kro[bb][kk]));
         else kf[bb][kk] = cat8(*(const v4i*)(ks + kro[bb][2 * kk]), *(const v4i*)(ks + kro[bb][2 * kk + 1]));
       }
-      ksc[bb] = *(const uint32_t*)(ks + ksro[bb]) >> (8 * lh);
+      ksc[bb] = *(const uint32_t*)(ks + ksro[bb]);   // shifted at its use: no early wait
     }
   };
   auto qk_mfma = [&](int t) __attribute__((always_inline)) {
     (void)t;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
+      const uint32_t kscb = ksc[bb] >> (8 * lh);
       v16f s = v16f{};
-      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[bb][0], qf[0], s, FMT, FMT, 0, ksc[bb], 0, qsc);
-      if (NKK > 1) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[bb][1], qf[1], s, FMT, FMT, 2, ksc[bb], 2, qsc);
+      s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[bb][0], qf[0], s, FMT, FMT, 0, kscb, 0, qsc);
+      if (NKK > 1) s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[bb][1], qf[1], s, FMT, FMT, 2, kscb, 2, qsc);
       acc[bb] = s;
     }
   };
@@ -307,18 +311,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   auto valu_phase = [&](int t) __attribute__((always_inline)) {
     if (!active(t)) return;
     const int64_t key0 = (int64_t)t * KT;
-    float s[2][16];
-#pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[bb][r] = acc[bb][r];
+    v16f (&s)[2] = acc;   // worked on in place: a copy would cost 32 moves a tile
     if ((key0 + KT > p.N) || (CAUSAL && key0 + KT - 1 > qrow0)) {   // causal diagonal or ragged tile
+      // 32-bit key indices (N <= 2^24)
+      const int k0 = (int)key0 + (FP4 ? 32 * lh : 16 * lh), n32 = (int)p.N, q32 = (int)qrow;
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t kg = key0 + (FP4 ? 32 * lh + 16 * bb : 32 * bb + 16 * lh) + r;
-          if (kg >= p.N || (CAUSAL && kg > qrow)) s[bb][r] = -__builtin_inff();
+          const int kg = k0 + (FP4 ? 16 * bb : 32 * bb) + r;
+          if (kg >= n32 || (CAUSAL && kg > q32)) s[bb][r] = -__builtin_inff();
         }
     }
     float mb[2];
@@ -339,19 +341,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
       for (int c = 0; c < NCC; ++c) o[c] *= alpha;
     }
     const float dq = p.sm_log2, moff = m_run;
-    float lsum = 0.0f;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s[bb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], dq, -moff));
-        lsum += s[bb][r];
-      }
-    l_run += lsum;
+      for (int r = 0; r < 16; ++r) s[bb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[bb][r], dq, -moff));
+    float ps[16];   // the row sum as a pairwise tree (short dependency chains)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ps[r] = s[0][r] + s[1][r];
+#pragma unroll
+    for (int w2 = 1; w2 < 16; w2 *= 2)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2 * w2) ps[r] = ps[r] + ps[r + w2];
+    l_run += ps[0];
     if (FP4) {
       // one E8M0 block = this lane's 32 keys; its largest P is exp2 of the lane max
       const float amax = __builtin_amdgcn_exp2f(__builtin_fmaf(mlane, dq, -moff));
-      const int e = mx_exp_e2m1(amax);
+      const int e = mx_exp_e2m1_frexp(amax);
       // the conversion divides by 2^(exponent of its scale operand): codes E2M1(P * 2^-e)
       // (an all-zero block, e = -127, converts with 2^-126: its codes are 0 either way)
       const float f = __uint_as_float((uint32_t)(127 + (e < -126 ? -126 : e)) << 23);
@@ -410,15 +415,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
     if (next) qk_load(t + 1);
     if (active(t)) {
       const uint8_t* vs = vst(t);
-      v8i vf[NCC];
+      v4i vlo[NCC], vhi[NCC];
       uint32_t vsc[NCC];
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) {
-        if (FP4) vf[cc] = pad8(*(const v4i*)(vs + vro[cc][0]));
-        else vf[cc] = cat8(*(const v4i*)(vs + vro[cc][0]), *(const v4i*)(vs + vro[cc][1]));
+        vlo[cc] = *(const v4i*)(vs + vro[cc][0]);
+        if (!FP4) vhi[cc] = *(const v4i*)(vs + vro[cc][1]);
         vsc[cc] = vs[L::V_BYTES + lh * D + 32 * cc + li];
       }
-      const v8i pf = FP4 ? v8i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], 0, 0, 0, 0}
+      // all fragment reads in flight before the first product (else each product waits out
+      // its own read's latency)
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        __asm__ volatile("" : "+v"(vlo[cc]));
+        if (!FP4) __asm__ volatile("" : "+v"(vhi[cc]));
+        __asm__ volatile("" : "+v"(vsc[cc]));
+      }
+      v8i vf[NCC];
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) vf[cc] = FP4 ? pad8(vlo[cc]) : cat8(vlo[cc], vhi[cc]);
+      const v8i pf = FP4 ? pad8(v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]})
                          : v8i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc)

@@ -100,6 +100,14 @@ __device__ __forceinline__ int mx_exp_e2m1(float a) {
   int e = (mant <= 0x400000u) ? E - 2 : E - 1;   // m <= 1.5 ?
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
+// mx_exp_e2m1 through the hardware frexp (subnormal inputs included): a = f * 2^x with f in
+// [0.5, 1), so m = 2f and E = x - 1; m <= 1.5 iff f <= 0.75.  Same result, fewer instructions.
+__device__ __forceinline__ int mx_exp_e2m1_frexp(float a) {
+  int x;
+  const float f = __builtin_frexpf(a, &x);
+  const int e = f <= 0.75f ? x - 3 : x - 2;
+  return a == 0.0f ? -127 : (e < -127 ? -127 : (e > 127 ? 127 : e));
+}
 __device__ __forceinline__ int mx_exp_e4m3(float a) {
   // 448 * 2^e >= a: 448 = 1.75 * 2^8.  a = m * 2^E: 1.75 * 2^(E-8) >= a iff m <= 1.75.
   if (a == 0.0f) return -127;
