@@ -66,6 +66,7 @@ struct Params {
   int64_t Hq, Hkv, N, Np, nQB, nKB, nPairs, total_wg;
   float sm_log2;     // sm_scale * log2(e), rounded to fp32
   float sm_log2_lo;  // sm_scale * log2(e) - sm_log2 (the FP8-P path carries the product exactly)
+  Rows16 vr, qhr, khr, outr;   // rows of the 16-bit V, the Thrift tiles' Q and K_s, the output
 };
 
 // LDS: three K tiles (int8 [64][D]) and three V tiles (bf16 [64][D] row-major, or FP8 V^T
@@ -107,7 +108,9 @@ struct DmaPlan {
   static constexpr int V_ROUNDS = (PV8 ? D * KT : KT * 2 * D) / 16 / 256;
   int koff[K_ROUNDS], krow[K_ROUNDS];
   int voff[V_ROUNDS], vrow[V_ROUNDS];
-  __device__ __forceinline__ void init(int a, int lane, int64_t Np) {
+  int vsn;   // row stride of the 16-bit V (elements)
+  __device__ __forceinline__ void init(int a, int lane, int64_t Np, int64_t v_row_stride) {
+    vsn = (int)v_row_stride;
 #pragma unroll
     for (int i = 0; i < K_ROUNDS; ++i) {
       const int pos = (i * 4 + a) * 64 + lane, row = pos / (D / 16), c = (pos % (D / 16)) ^ (row & (D / 16 - 1));
@@ -121,7 +124,7 @@ struct DmaPlan {
         vrow[i] = row; voff[i] = (int)(row * Np) + 16 * c;
       } else {
         const int row = pos / (2 * D / 16), c = (pos % (2 * D / 16)) ^ v_swz<D>(row);
-        vrow[i] = row; voff[i] = row * 2 * D + 16 * c;
+        vrow[i] = row; voff[i] = row * 2 * vsn + 16 * c;   // < 2^31: checked at the boundary
       }
     }
   }
@@ -144,12 +147,12 @@ struct DmaPlan {
       for (int i = 0; i < V_ROUNDS; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(base + voff[i]), (lds_void*)(vb + (i * 4 + a) * 1024), 16, 0, 0);
     } else {
-      const char* base = (const char*)((const uint16_t*)p.v + (bkv * p.N + key0) * D);
+      const char* base = (const char*)((const uint16_t*)p.v + p.vr.at(bkv, key0));
       const bool full = key0 + KT <= p.N;
 #pragma unroll
       for (int i = 0; i < V_ROUNDS; ++i) {
         int off = voff[i];
-        if (!full && key0 + vrow[i] >= p.N) off += (int)((p.N - 1 - key0 - vrow[i]) * 2 * D);
+        if (!full && key0 + vrow[i] >= p.N) off += (int)((p.N - 1 - key0 - vrow[i]) * 2 * vsn);
         __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(vb + (i * 4 + a) * 1024), 16, 0, 0);
       }
     }
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
 
   DmaPlan<D, PV8> dma;
   if (grp == 0) {
-    dma.init(a, lane, p.Np);
+    dma.init(a, lane, p.Np, p.vr.sn);
     dma.k_tile(p, bkv, 0, kbuf(I0{}), a);
     if (nT > 1) dma.k_tile(p, bkv, 1, kbuf(I1{}), a);
     if (nT > 0) dma.v_tile(p, bkv, 0, vbuf(I0{}), a);
@@ -298,9 +301,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
       const int64_t k0 = key0 + tile_key(0, li), k1 = key0 + tile_key(1, li);
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
-        const v8bf qh = row_ok ? *(const v8bf*)(p.qhi + (bh * p.N + qrow) * D + 16 * kc + 8 * lh) : v8bf{};
-        const v8bf kh0 = k0 < p.N ? *(const v8bf*)(p.khi + (bkv * p.N + k0) * D + 16 * kc + 8 * lh) : v8bf{};
-        const v8bf kh1 = k1 < p.N ? *(const v8bf*)(p.khi + (bkv * p.N + k1) * D + 16 * kc + 8 * lh) : v8bf{};
+        const v8bf qh = row_ok ? *(const v8bf*)(p.qhi + p.qhr.at(bh, qrow) + 16 * kc + 8 * lh) : v8bf{};
+        const v8bf kh0 = k0 < p.N ? *(const v8bf*)(p.khi + p.khr.at(bkv, k0) + 16 * kc + 8 * lh) : v8bf{};
+        const v8bf kh1 = k1 < p.N ? *(const v8bf*)(p.khi + p.khr.at(bkv, k1) + 16 * kc + 8 * lh) : v8bf{};
         f[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh0, qh, f[0], 0, 0, 0);
         f[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh1, qh, f[1], 0, 0, 0);
       }
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_kernel(Params p, const fl
           const float* vsc = p.vs + bkv * D + ch;
           v0 *= vsc[0]; v1 *= vsc[1]; v2 *= vsc[2]; v3 *= vsc[3];
         }
-        const int64_t off = (bh * p.N + qrow) * D + ch;
+        const int64_t off = p.outr.at(bh, qrow) + ch;
         if (OUT_BF16) {
           *(v2i*)((uint16_t*)p.out + off) = v2i{(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
         } else {
@@ -617,6 +620,7 @@ hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st) {
   p.v = a.v_codes; p.vs = (const float*)a.v_scales;
   p.mask = a.mask; p.qhi = a.q_hi; p.khi = a.k_hi;
   p.out = a.out;
+  p.vr = a.vr; p.qhr = a.qhr; p.khr = a.khr; p.outr = a.outr;
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
   p.Np = (a.N + KT - 1) / KT * KT;
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;

@@ -47,6 +47,7 @@ struct PipeParams {
   void* out;
   int64_t Hq, Hkv, N, nQB, nKB, nPairs, total_wg;
   float sm_log2;   // sm_scale * log2(e), rounded to fp32
+  Rows16 vr, outr; // rows of V (per KV head) and of the output
 };
 
 // K tile (int8 [64][D]): 16-byte chunk c of row r at chunk position c ^ k_swz(r).  An operand
@@ -124,13 +125,15 @@ struct PipeDma {
   static constexpr int K_PER = (K_INSTR + 7) / 8, V_PER = V_INSTR / 8;
   const int8_t* kbase;       // K and V of this (b, kv-head)
   const uint16_t* vbase;
+  int vsn;                   // V row stride (elements)
   int N;
   int koff[K_PER], voff[V_PER];
   // rows of the tile at key0 that lie below N (1 .. KT): the record count stays far below 2^32
   __device__ __forceinline__ int rows_left(int key0) const { return N - key0 < KT ? N - key0 : KT; }
   __device__ __forceinline__ void init(const PipeParams& p, int64_t bkv, int w, int lane) {
     kbase = p.k + bkv * p.N * D;
-    vbase = p.v + bkv * p.N * D;
+    vbase = p.v + p.vr.head(bkv);
+    vsn = (int)p.vr.sn;
     N = (int)p.N;
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
@@ -143,7 +146,7 @@ struct PipeDma {
     for (int j = 0; j < V_PER; ++j) {
       const int pos = 64 * (w + 8 * j) + lane, row = pos / (2 * D / 16);
       const int c = (pos % (2 * D / 16)) ^ v_swz<D>(row);
-      voff[j] = row * 2 * D + 16 * c;
+      voff[j] = row * 2 * vsn + 16 * c;   // < 2^31: the row stride is checked at the boundary
     }
   }
   __device__ __forceinline__ void k_tile(int t, uint32_t kb, int w) const {
@@ -157,7 +160,8 @@ struct PipeDma {
   }
   __device__ __forceinline__ void v_tile(int t, uint32_t vb, int w) const {
     const int key0 = t * KT;
-    const v4i rsrc = buffer_desc(vbase + (int64_t)key0 * D, rows_left(key0) * 2 * D);
+    // the record count ends right after the last row below N: rows past it read zeros
+    const v4i rsrc = buffer_desc(vbase + (int64_t)key0 * vsn, ((rows_left(key0) - 1) * vsn + D) * 2);
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) lds_dma16(voff[j], rsrc, vb + (w + 8 * j) * 1024);
   }
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
         const int ch = 32 * cc + 8 * g + 4 * lh;
         const float v0 = o[cc][4 * g] * inv, v1 = o[cc][4 * g + 1] * inv, v2 = o[cc][4 * g + 2] * inv,
                     v3 = o[cc][4 * g + 3] * inv;
-        const int64_t off = (bh * p.N + qrow) * D + ch;
+        const int64_t off = p.outr.at(bh, qrow) + ch;
         if (OUT_BF16) *(v2i*)((uint16_t*)p.out + off) = v2i{(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
         else *(v4f*)((float*)p.out + off) = v4f{v0, v1, v2, v3};
       }
@@ -581,6 +585,7 @@ hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st) {
   p.k = (const int8_t*)a.k_codes; p.ks = (const float*)a.k_scales;
   p.v = (const uint16_t*)a.v_codes;
   p.out = a.out;
+  p.vr = a.vr; p.outr = a.outr;
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;
   p.nPairs = (p.nQB + 1) / 2;

@@ -43,6 +43,7 @@ struct MxParams {
   void* out;
   int64_t Hq, Hkv, N, Np, nQB, nKB, nPairs, total_wg;
   float sm_log2;   // sm_scale * log2(e)
+  Rows16 outr;     // output rows
 };
 
 // LDS stages: K tile + its scales, V^T tile + its scales, two of each.
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
         const int ch = 32 * cc + 8 * g + 4 * lh;
         const float v0 = o[cc][4 * g] * inv, v1 = o[cc][4 * g + 1] * inv, v2 = o[cc][4 * g + 2] * inv,
                     v3 = o[cc][4 * g + 3] * inv;
-        const int64_t off = (bh * p.N + qrow) * D + ch;
+        const int64_t off = p.outr.at(bh, qrow) + ch;
         if (OUT_BF16) *(v2i*)((uint16_t*)p.out + off) = v2i{(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
         else *(v4f*)((float*)p.out + off) = v4f{v0, v1, v2, v3};
       }
@@ -519,6 +520,7 @@ hipError_t launch_attn_mx(const AttnArgs& a, int nvfp4_variant, hipStream_t st) 
   p.k = (const uint8_t*)a.k_codes; p.ke = (const uint8_t*)a.k_scales;
   p.v = (const uint8_t*)a.v_codes; p.ve = (const uint8_t*)a.v_scales;
   p.out = a.out;
+  p.outr = a.outr;
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
   p.Np = (a.N + KT - 1) / KT * KT;
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;

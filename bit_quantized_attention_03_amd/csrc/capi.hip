@@ -14,7 +14,8 @@ constexpr int QBLK = 128, KBLK = 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool shape_ok(const sage_shape& s) {
-  return s.B >= 0 && s.H >= 1 && s.N >= 0 && s.D >= 1 && s.B <= (1 << 20) && s.H <= 65535 && s.B * s.H <= 65535 && s.N <= (1ll << 31);
+  return s.B >= 0 && s.H >= 1 && s.N >= 0 && s.D >= 1 && s.D <= 16384 && s.B <= (1 << 20) && s.H <= 65535 &&
+         s.B * s.H <= 65535 && s.N <= (1ll << 31);
 }
 // A call whose tensors hold no elements: it validates, then returns without reading a pointer.
 bool empty_call(const sage_shape& s) { return s.B * s.H == 0 || s.N == 0; }
@@ -25,6 +26,42 @@ bool block_is(const sage_qtensor* t, int32_t tokens, int32_t channels) {
   return t->block.tokens == tokens && t->block.channels == channels;
 }
 static_assert(SAGE_DECODE_NOALLOC_SCRATCH_BYTES == DECODE_SCRATCH_BYTES, "one scratch size");
+
+bool zero_strides(const sage_shape& s) { return s.sb == 0 && s.sh == 0 && s.sn == 0; }
+// Strides absent or exactly the contiguous ones (quantized operands, library-written tensors).
+bool contiguous(const sage_shape& s) {
+  return zero_strides(s) || (s.sb == s.H * s.N * s.D && s.sh == s.N * s.D && s.sn == s.D);
+}
+// The rows of a strided tensor (see sage_shape), checked: strides all zero (contiguous), or
+// non-negative multiples of align elements (the kernels move 16-byte pieces), with no two
+// (b, h, n) rows overlapping and the largest element offset below 2^62.
+bool layout_of(const sage_shape& s, int64_t align, Rows16* r) {
+  if (zero_strides(s)) {
+    *r = rows_contiguous(s.H, s.N, s.D);
+    return true;
+  }
+  if (s.sb < 0 || s.sh < 0 || s.sn < 0 || s.sb % align || s.sh % align || s.sn % align) return false;
+  int64_t st[3] = {s.sb, s.sh, s.sn}, ext[3] = {s.B, s.H, s.N};
+  for (int i = 1; i < 3; ++i)   // order the dimensions by stride
+    for (int j = i; j > 0 && st[j] < st[j - 1]; --j) {
+      const int64_t a = st[j], b = ext[j];
+      st[j] = st[j - 1]; ext[j] = ext[j - 1];
+      st[j - 1] = a; ext[j - 1] = b;
+    }
+  int64_t span = s.D;   // elements spanned by the dimensions inside the current one
+  for (int i = 0; i < 3; ++i) {
+    if (ext[i] <= 1) continue;
+    if (st[i] < span) return false;                                   // rows would overlap
+    if (ext[i] - 1 > ((int64_t(1) << 62) - span) / st[i]) return false;
+    span += (ext[i] - 1) * st[i];
+  }
+  *r = Rows16{s.H, s.sb, s.sh, s.sn};
+  return true;
+}
+bool same_dims(const sage_shape& a, const sage_shape& b) { return a.B == b.B && a.H == b.H && a.N == b.N && a.D == b.D; }
+bool no_dims(const sage_shape& s) { return s.B == 0 && s.H == 0 && s.N == 0 && s.D == 0 && zero_strides(s); }
+// The attention kernels address a V row within a tile with 32-bit byte offsets.
+constexpr int64_t V_MAX_ROW_STRIDE = int64_t(1) << 24;
 // The attention kernels address tiles with 32-bit offsets (a channel-major V row spans Np bytes).
 constexpr int64_t ATTN_MAX_N = 1ll << 24;
 
@@ -57,12 +94,14 @@ int sage_smooth_k(const void* k, sage_fmt dt, sage_shape ks, float* mean_out, vo
   const bool no_heads = ks.B * ks.H == 0;   // N == 0 still writes the (zero) means
   if ((!k && !no_heads && ks.N > 0) || (!mean_out && !no_heads)) return SAGE_EINVAL;
   if (!is16(dt)) return SAGE_ENOTSUP;
+  Rows16 kr;
+  if (!layout_of(ks, 8, &kr)) return SAGE_EINVAL;
   if (!aligned16(k) || !aligned16(mean_out) || (k_smoothed_out && !aligned16(k_smoothed_out))) return SAGE_EALIGN;
   const size_t need = sage_smooth_k_workspace_bytes(ks);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
   if (workspace && !aligned16(workspace)) return SAGE_EALIGN;
   if (no_heads) return SAGE_OK;
-  return launched(launch_smooth_k(k, dt == SAGE_FP16, ks.B * ks.H, ks.N, (int)ks.D, mean_out, k_smoothed_out,
+  return launched(launch_smooth_k(k, kr, dt == SAGE_FP16, ks.B * ks.H, ks.N, (int)ks.D, mean_out, k_smoothed_out,
                                   (float*)workspace, stream));
 }
 
@@ -107,6 +146,8 @@ int quantize_impl(const void* x, sage_fmt in_dt, sage_shape xs, const float* mea
   if (!empty_call(xs) && (!x || !codes_out || !scales_out)) return SAGE_EINVAL;
   if (!is16(in_dt)) return SAGE_ENOTSUP;
   if (xs.D % 8 != 0) return SAGE_EINVAL;
+  Rows16 xr;
+  if (!layout_of(xs, 8, &xr)) return SAGE_EINVAL;
   size_t cb, sb;
   int st = sage_quantized_bytes(fmt, block, xs, &cb, &sb);
   if (st != SAGE_OK) return st;
@@ -128,13 +169,13 @@ int quantize_impl(const void* x, sage_fmt in_dt, sage_shape xs, const float* mea
   const bool f16 = in_dt == SAGE_FP16;
   switch (fmt) {
     case SAGE_INT8:
-      return launched(launch_quant_int8(x, f16, BH, xs.N, (int)xs.D, block.tokens, mean, (int8_t*)codes_out,
+      return launched(launch_quant_int8(x, xr, f16, BH, xs.N, (int)xs.D, block.tokens, mean, (int8_t*)codes_out,
                                         (float*)scales_out, stream, had));
     case SAGE_E4M3:
-      return launched(launch_quant_fp8_channel(x, f16, BH, xs.N, (int)xs.D, (uint8_t*)codes_out, (float*)scales_out,
+      return launched(launch_quant_fp8_channel(x, xr, f16, BH, xs.N, (int)xs.D, (uint8_t*)codes_out, (float*)scales_out,
                                                stream));
     default:
-      return launched(launch_quant_fp4(x, f16, BH, xs.N, (int)xs.D, fmt == SAGE_NVFP4, block.channels == 1 ? 1 : 0,
+      return launched(launch_quant_fp4(x, xr, f16, BH, xs.N, (int)xs.D, fmt == SAGE_NVFP4, block.channels == 1 ? 1 : 0,
                                        (int)mode, mean, (uint8_t*)codes_out, (uint8_t*)scales_out, stream, had));
   }
 }
@@ -160,6 +201,7 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
   if (!shape_ok(xs)) return SAGE_EINVAL;
   if (!empty_call(xs) && (!codes || !scales || !f8_out || !e8m0_out)) return SAGE_EINVAL;
   if (along_tokens != 0 && along_tokens != 1) return SAGE_EINVAL;
+  if (!contiguous(xs)) return SAGE_EINVAL;   // library-written codes
   if (!along_tokens && xs.D % 32) return SAGE_EINVAL;
   if (!aligned16(codes) || !aligned16(f8_out)) return SAGE_EALIGN;
   const int64_t Np = roundup(xs.N, 64);
@@ -169,7 +211,7 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
 }
 
 int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
-                  void* out, sage_fmt out_dt, hipStream_t stream) {
+                  void* out, sage_fmt out_dt, sage_shape os, hipStream_t stream) {
   if (!q || !k || !v || !p) return SAGE_EINVAL;
   const sage_shape &qs = q->shape, &ks = k->shape, &vs = v->shape;
   if (!shape_ok(qs) || !shape_ok(ks) || !shape_ok(vs)) return SAGE_EINVAL;
@@ -184,8 +226,31 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   if (!aligned16(q->codes) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
   if (p->causal != 0 && p->causal != 1) return SAGE_EINVAL;
   if (!(p->sm_scale >= 0.0f) || isinf(p->sm_scale)) return SAGE_EINVAL;
-
+  // layouts: quantized operands contiguous; 16-bit V, the Thrift tiles' Q and K_s and the
+  // output may be strided
   AttnArgs a;
+  if (!contiguous(qs) || !contiguous(ks)) return SAGE_EINVAL;
+  if (is16(v->fmt)) {
+    if (!layout_of(vs, 8, &a.vr) || a.vr.sn > V_MAX_ROW_STRIDE) return SAGE_EINVAL;
+  } else {
+    if (!contiguous(vs)) return SAGE_EINVAL;
+    a.vr = rows_contiguous(vs.H, vs.N, vs.D);
+  }
+  const sage_shape o_dims = {qs.B, qs.H, qs.N, qs.D, 0, 0, 0};
+  if (no_dims(os)) {
+    a.outr = rows_contiguous(qs.H, qs.N, qs.D);
+  } else if (!same_dims(os, o_dims) || !layout_of(os, 4, &a.outr)) {
+    return SAGE_EINVAL;
+  }
+  auto hi_rows = [](const sage_shape& given, const sage_shape& dims, Rows16* r) {
+    if (no_dims(given)) {
+      *r = rows_contiguous(dims.H, dims.N, dims.D);
+      return true;
+    }
+    return same_dims(given, dims) && layout_of(given, 8, r);
+  };
+  if (!hi_rows(p->q_hi_shape, qs, &a.qhr) || !hi_rows(p->k_hi_shape, ks, &a.khr)) return SAGE_EINVAL;
+
   a.B = qs.B; a.Hq = qs.H; a.Hkv = ks.H; a.N = qs.N; a.D = (int)qs.D;
   a.causal = p->causal;
   a.sm_scale = p->sm_scale > 0.0f ? p->sm_scale : 1.0f / sqrtf((float)qs.D);
@@ -252,12 +317,14 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
     const int64_t nqb = (qs.N + QBLK - 1) / QBLK, nkb = (qs.N + KBLK - 1) / KBLK;
     if (nqb * nkb > INT32_MAX) return SAGE_EINVAL;
   }
+  Rows16 qr, kr;
+  if (!layout_of(qs, 8, &qr) || !layout_of(ks, 8, &kr)) return SAGE_EINVAL;
   if (!aligned16(q) || !aligned16(k_smoothed)) return SAGE_EALIGN;
   const size_t need = empty_call(qs) ? 0 : thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
   if (need > 0 && (!workspace || workspace_bytes < need)) return SAGE_EWORKSPACE;
   if (!aligned16(workspace)) return SAGE_EALIGN;
   if (empty_call(qs)) return SAGE_OK;
-  return launched(launch_thrift_select((const uint16_t*)q, (const uint16_t*)k_smoothed, qs.B, qs.H, ks.H, qs.N,
+  return launched(launch_thrift_select((const uint16_t*)q, qr, (const uint16_t*)k_smoothed, kr, qs.B, qs.H, ks.H, qs.N,
                                        (int)qs.D, frac, causal, mask_out, workspace, stream));
 }
 
@@ -282,6 +349,8 @@ int decode_check(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtensor
   if (ks.N > (1 << 26)) return SAGE_EINVAL;           // cache offsets are 32-bit (64 bytes a key)
   if (!is16(q_dt) || k->fmt != SAGE_NVFP4 || v->fmt != SAGE_NVFP4 || qs.D != 128) return SAGE_ENOTSUP;
   if (!block_is(k, 1, 16) || !block_is(v, 16, 1)) return SAGE_EINVAL;
+  Rows16 qr;
+  if (!layout_of(qs, 8, &qr) || !contiguous(ks) || !contiguous(vs)) return SAGE_EINVAL;
   if (out_dt != SAGE_FP32 && out_dt != SAGE_BF16) return SAGE_ENOTSUP;
   if (!aligned16(q) || !aligned16(k->codes) || !aligned16(v->codes) || !aligned16(out)) return SAGE_EALIGN;
   if ((uintptr_t)k->scales % 2) return SAGE_EALIGN;   // read as byte pairs
@@ -293,7 +362,9 @@ int decode_launch(const void* q, sage_fmt q_dt, sage_shape qs, const sage_qtenso
                   int causal, float sm_scale, void* out, sage_fmt out_dt, void* workspace, hipStream_t stream) {
   const sage_shape& ks = k->shape;
   const float sc = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)qs.D);
-  return launched(launch_decode((const uint16_t*)q, q_dt == SAGE_FP16, qs.B, qs.H, ks.H, qs.N, ks.N,
+  Rows16 qr;
+  layout_of(qs, 8, &qr);   // checked by decode_check
+  return launched(launch_decode((const uint16_t*)q, qr, q_dt == SAGE_FP16, qs.B, qs.H, ks.H, qs.N, ks.N,
                                 (const uint8_t*)k->codes, (const uint8_t*)k->scales, (const uint8_t*)v->codes,
                                 (const uint8_t*)v->scales, causal, sc, out, out_dt == SAGE_BF16, workspace, stream));
 }

@@ -46,7 +46,8 @@ constexpr int DEC_THREADS = 256;    // 4 waves x 8 key slots
 constexpr float kLazy = 15.0f;      // headroom of the running max, log2 units (P <= 2^15 fits f16)
 
 struct DecodeArgs {
-  const uint16_t* q;                           // [B, Hq, Nq, 128] 16-bit
+  const uint16_t* q;                           // [B, Hq, Nq, 128] 16-bit, rows qr
+  Rows16 qr;
   const uint8_t *kc, *ks;                      // K codes [B, Hkv, Nk, 64], scales [B, Hkv, Nk, 8]
   const uint8_t *vc, *vs;                      // V codes [B, Hkv, 128, Np/2], scales [B, Hkv, Np/16, 128]
   float* part_o;                               // [B * Hkv, nsplit, R, 128]
@@ -103,7 +104,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_split_kernel(DecodeArgs
     const int64_t rr = act ? row : 0;
     const int64_t hq = kvh * G + rr / a.Nq, i = rr % a.Nq;
     if (act) qpos = (int)(a.Nk - a.Nq + i);
-    const uint16_t* qp = a.q + ((b * a.Hq + hq) * a.Nq + i) * DK + 32 * h;
+    const uint16_t* qp = a.q + a.qr.at(b * a.Hq + hq, i) + 32 * h;
     v4i w[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) w[kk] = act ? *(const v4i*)(qp + 8 * kk) : v4i{0, 0, 0, 0};
@@ -386,13 +387,15 @@ size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t N
   return (size_t)(B * Hkv * nsplit * R) * (DK + 2) * sizeof(float);
 }
 
-hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                         const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int causal,
-                         float sm_scale, void* out, bool out_bf16, void* ws, hipStream_t st) {
+hipError_t launch_decode(const uint16_t* q, const Rows16& qr, bool q_f16, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t Nq, int64_t Nk, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                         const uint8_t* vs, int causal, float sm_scale, void* out, bool out_bf16, void* ws,
+                         hipStream_t st) {
   const int64_t R = (Hq / Hkv) * Nq, nrg = (R + 15) / 16;
   const int64_t nsplit = decode_splits(B, Hq, Hkv, Nq, Nk);
   DecodeArgs a;
   a.q = q;
+  a.qr = qr;
   a.kc = kc; a.ks = ks; a.vc = vc; a.vs = vs;
   a.part_o = (float*)ws;
   a.part_ml = (float*)ws + B * Hkv * nsplit * R * DK;

@@ -6,22 +6,35 @@
 
 namespace sage {
 
+// Rows of a [B, H, N, D] tensor held with element strides (sb, sh, sn) and contiguous
+// channels: row n of head bh = b H + h starts at element b sb + h sh + n sn.  The
+// contiguous layout is (H N D, N D, D).  B H <= 65535, so the head split runs in 32 bits.
+struct Rows16 {
+  int64_t H, sb, sh, sn;
+  __host__ __device__ int64_t head(int64_t bh) const {
+    const int b = (int)bh / (int)H, h = (int)bh - b * (int)H;
+    return (int64_t)b * sb + (int64_t)h * sh;
+  }
+  __host__ __device__ int64_t at(int64_t bh, int64_t n) const { return head(bh) + n * sn; }
+};
+inline Rows16 rows_contiguous(int64_t H, int64_t N, int64_t D) { return Rows16{H, H * N * D, N * D, D}; }
+
 // K smoothing (three kernels: per-run partial sums, per-channel mean, subtract+round).
-hipError_t launch_smooth_k(const void* k, bool is_f16, int64_t BH, int64_t N, int D, float* mean, void* ks,
-                           float* partials, hipStream_t st);
+hipError_t launch_smooth_k(const void* k, const Rows16& kr, bool is_f16, int64_t BH, int64_t N, int D, float* mean,
+                           void* ks, float* partials, hipStream_t st);
 
 // Block quantizers.
 // mean (nullable, [BH, D] fp32): quantize round_to_dtype(x - mean) instead of x (K smoothing
 // applied on the fly, bit-identical to quantizing the smoothing kernel's K_s).
 // hadamard: rows along D times the normalized Hadamard matrix first (D in {64, 128}; INT8
 // blocks of at most 4096 16-byte chunks; FP4 along D only), else hipErrorNotSupported.
-hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, const float* mean,
-                             int8_t* codes, float* scales, hipStream_t st, bool hadamard = false);
-hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int64_t N, int D, uint8_t* codes_t,
-                                    float* scales, hipStream_t st);
-hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
-                            int mode, const float* mean /* nullable; along D only */, uint8_t* codes, uint8_t* scales,
-                            hipStream_t st, bool hadamard = false);
+hipError_t launch_quant_int8(const void* x, const Rows16& xr, bool is_f16, int64_t BH, int64_t N, int D, int T,
+                             const float* mean, int8_t* codes, float* scales, hipStream_t st, bool hadamard = false);
+hipError_t launch_quant_fp8_channel(const void* x, const Rows16& xr, bool is_f16, int64_t BH, int64_t N, int D,
+                                    uint8_t* codes_t, float* scales, hipStream_t st);
+hipError_t launch_quant_fp4(const void* x, const Rows16& xr, bool is_f16, int64_t BH, int64_t N, int D, bool nv,
+                            int along_tokens, int mode, const float* mean /* nullable; along D only */,
+                            uint8_t* codes, uint8_t* scales, hipStream_t st, bool hadamard = false);
 // rows x len elements along the block axis; D_tok = 0 along D, else the channel count of a
 // token-axis (V) layout whose scales are token-group major.
 hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t len, int D_tok,
@@ -29,15 +42,17 @@ hipError_t launch_nvfp4_to_mxfp8(const uint8_t* codes, const uint8_t* scales, in
 hipError_t launch_convert_f32(const float* x, int64_t n, int fmt, void* out, hipStream_t st);
 
 // Thrift block selection.
-hipError_t launch_thrift_select(const uint16_t* q, const uint16_t* ks, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
-                                int D, double frac, int causal, uint8_t* mask, void* ws, hipStream_t st);
+hipError_t launch_thrift_select(const uint16_t* q, const Rows16& qr, const uint16_t* ks, const Rows16& kr, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t N, int D, double frac, int causal, uint8_t* mask,
+                                void* ws, hipStream_t st);
 size_t thrift_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int D);
 // Decode-shaped attention on an NVFP4 KV cache (rows along D, d = 128): split workgroups
 // write partial (O, max, sum) to ws (decode_ws_bytes), a combine kernel writes out.
 size_t decode_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk);
-hipError_t launch_decode(const uint16_t* q, bool q_f16, int64_t B, int64_t Hq, int64_t Hkv, int64_t Nq, int64_t Nk,
-                         const uint8_t* kc, const uint8_t* ks, const uint8_t* vc, const uint8_t* vs, int causal,
-                         float sm_scale, void* out, bool out_bf16, void* ws, hipStream_t st);
+hipError_t launch_decode(const uint16_t* q, const Rows16& qr, bool q_f16, int64_t B, int64_t Hq, int64_t Hkv,
+                         int64_t Nq, int64_t Nk, const uint8_t* kc, const uint8_t* ks, const uint8_t* vc,
+                         const uint8_t* vs, int causal, float sm_scale, void* out, bool out_bf16, void* ws,
+                         hipStream_t st);
 // Static sink-and-recent block mask [BH, nQB, nKB] (blocks of 128 Q rows and 64 keys).
 // The allocation-free decode keeps its split partials in a static device array of this size
 // (SAGE_DECODE_NOALLOC_SCRATCH_BYTES); decode_scratch gives the current device's address of it.
@@ -61,6 +76,9 @@ struct AttnArgs {
   void* out;
   int out_bf16;
   int p_scale_mode;   // NVFP4 P: 0 max-scaling, 1 / 2 ScaleSearch per 16-key block
+  // rows of the 16-bit V (bf16 / fp16 P.V), of the Thrift tiles' Q and K_s, and of the output
+  // (elements of the output dtype); quantized operands are contiguous
+  Rows16 vr, qhr, khr, outr;
 };
 hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st);
 // INT8 QK^T, bf16 P.V, no block mask: the software-pipelined kernel (attn_i8_pipe.hip).

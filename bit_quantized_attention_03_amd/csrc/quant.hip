@@ -97,20 +97,21 @@ __device__ __forceinline__ void fwht_across_lanes(float* v, int cnt) {
 // HAD: the rows are Hadamard-transformed first (D in {64, 128}: a row is D/8 chunks, held by
 // D/8 consecutive lanes); the block is then held as fp32.
 template <bool F16, int CPT, bool SMOOTH, bool HAD = false>   // CPT = 16-byte chunks per thread (T * D / 8 / 256)
-__global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int T,
-                                                         const float* __restrict__ mean, int8_t* __restrict__ codes,
-                                                         float* __restrict__ scales, float hscale = 0.0f) {
+__global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t N, int D,
+                                                         int T, const float* __restrict__ mean,
+                                                         int8_t* __restrict__ codes, float* __restrict__ scales,
+                                                         float hscale = 0.0f) {
   const int64_t nblk = (N + T - 1) / T;
   const int64_t blk = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = blk * T;
   const int rows = (int)((N - t0) < T ? (N - t0) : T);
-  const int nchunk = rows * D / 8;
-  const uint16_t* base = x + (bh * N + t0) * D;
+  const int nchunk = rows * D / 8, cpr = D / 8;
+  const uint16_t* base = x + xr.at(bh, t0);   // chunk c: row c / cpr, channels 8 (c % cpr) ..
   v4i raw[CPT];
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
-    const int c = threadIdx.x + 256 * i;
-    raw[i] = c < nchunk ? *(const v4i*)(base + (int64_t)c * 8) : v4i{0, 0, 0, 0};
+    const int c = threadIdx.x + 256 * i, r = c / cpr;
+    raw[i] = c < nchunk ? *(const v4i*)(base + r * xr.sn + (c - r * cpr) * 8) : v4i{0, 0, 0, 0};
   }
   if (SMOOTH) {
     if ((2048 % D) == 0) {   // chunks tid + 256 i all start at channel 8 tid mod D: one mean slice
@@ -184,18 +185,22 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
 // Blocks too large for registers (over 4096 chunks): amax pass, then an encoding pass whose
 // reads hit L2.
 template <bool F16, bool SMOOTH>
-__global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __restrict__ x, int64_t N, int D, int T,
-                                                          const float* __restrict__ mean, int8_t* __restrict__ codes,
-                                                          float* __restrict__ scales) {
+__global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __restrict__ x, Rows16 xr, int64_t N, int D,
+                                                          int T, const float* __restrict__ mean,
+                                                          int8_t* __restrict__ codes, float* __restrict__ scales) {
   const int64_t nblk = (N + T - 1) / T;
   const int64_t blk = blockIdx.x, bh = blockIdx.y;
   const int64_t t0 = blk * T;
   const int rows = (int)((N - t0) < T ? (N - t0) : T);
-  const int64_t nchunk = (int64_t)rows * D / 8;
-  const uint16_t* base = x + (bh * N + t0) * D;
+  const int64_t nchunk = (int64_t)rows * D / 8, cpr = D / 8;
+  const uint16_t* base = x + xr.at(bh, t0);   // chunk c: row c / cpr, channels 8 (c % cpr) ..
+  auto src = [&](int64_t c) __attribute__((always_inline)) {
+    const int64_t r = c / cpr;
+    return base + r * xr.sn + (c - r * cpr) * 8;
+  };
   float amax = 0.0f;
   for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
-    v4i raw = *(const v4i*)(base + c * 8);
+    v4i raw = *(const v4i*)src(c);
     if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + bh * D + (c * 8) % D);
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -214,7 +219,7 @@ __global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __rest
   if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
   int8_t* out = codes + (bh * N + t0) * D;
   for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
-    v4i raw = *(const v4i*)(base + c * 8);
+    v4i raw = *(const v4i*)src(c);
     if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + bh * D + (c * 8) % D);
     uint32_t packed[2] = {0u, 0u};
 #pragma unroll
@@ -235,8 +240,8 @@ __global__ void fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 }
 
 template <bool F16>
-__global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __restrict__ x, int64_t BH, int64_t N, int D,
-                                                           uint32_t* __restrict__ amax_bits) {
+__global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t BH,
+                                                           int64_t N, int D, uint32_t* __restrict__ amax_bits) {
   // thread: (bh, run of 64 tokens, 8 channels); lanes of one wave cover D/8 channel groups of
   // consecutive runs
   const int64_t nrun = (N + 63) / 64;
@@ -254,22 +259,22 @@ __global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __res
   if (valid) {
     const int64_t t0 = run * 64;
     const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
-    const uint16_t* p = x + (bh * N + t0) * D + c8 * 8;
+    const uint16_t* p = x + xr.at(bh, t0) + c8 * 8;
     if (rows == 64) {   // four batches of 16 rows, the next one in flight while the current is taken
       v4i raw[2][16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * D);
+      for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * xr.sn);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (b + 1 < 4) {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * D);
+          for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * xr.sn);
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) take(raw[b & 1][j]);
       }
     } else {
-      for (int t = 0; t < rows; ++t) take(*(const v4i*)(p + (int64_t)t * D));
+      for (int t = 0; t < rows; ++t) take(*(const v4i*)(p + (int64_t)t * xr.sn));
     }
   }
   // Lanes l, l + cg, l + 2cg, ... hold the same channels of consecutive runs; when the whole
@@ -298,7 +303,8 @@ __global__ void channel_scale_kernel(uint32_t* sc, int64_t n) {
 }
 
 template <bool F16>
-__global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* __restrict__ x, int64_t N, int D,
+__global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t N,
+                                                                int D,
                                                                 const float* __restrict__ scales,
                                                                 uint8_t* __restrict__ codes_t) {
   // block: (64-token run, bh); LDS tile [D][64] bytes, written transposed, stored as rows.
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* 
       for (int e = 0; e < 8; ++e) tile[(c8 + e) * PITCH + t] = 0;
       continue;
     }
-    v4i raw = *(const v4i*)(x + (bh * N + t0 + t) * D + c8);
+    v4i raw = *(const v4i*)(x + xr.at(bh, t0 + t) + c8);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float s = sc[c8 + e];
@@ -442,15 +448,16 @@ __device__ __forceinline__ uint32_t mx_quant32(const float* v, uint32_t* c) {
 // row is Hadamard-transformed first; its D / G groups sit in consecutive lanes, and whole
 // rows leave together at the bound check, so every lane a stage pairs with is active.
 template <bool F16, bool NV, bool SMOOTH, bool HAD = false>
-__global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restrict__ x, int64_t rows, int64_t N, int D,
-                                                       int mode, const float* __restrict__ mean,
+__global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t rows,
+                                                       int64_t N, int D, int mode, const float* __restrict__ mean,
                                                        uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                        float hscale = 0.0f) {
   constexpr int G = NV ? 16 : 32;
   const int gpr = D / G;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= rows * gpr) return;
-  const uint16_t* p = x + gid * G;
+  const int64_t row = gid / gpr, bh_ = row / N;   // group gid: row (bh, n), channels G (gid % gpr) ..
+  const uint16_t* p = x + xr.at(bh_, row - bh_ * N) + (gid - row * gpr) * G;
   float v[G];
 #pragma unroll
   for (int q = 0; q < G / 8; ++q) {
@@ -482,8 +489,9 @@ __global__ __launch_bounds__(256) void fp4_rows_kernel(const uint16_t* __restric
 // (channel, group of G tokens).  Code rows are channels, Np = N rounded up to 64; scales
 // are token-group major [Np/G][D], so consecutive threads write consecutive bytes.
 template <bool F16, bool NV>
-__global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restrict__ x, int64_t N, int D, int mode,
-                                                       uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+__global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t N, int D,
+                                                       int mode, uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
   constexpr int G = NV ? 16 : 32;
   __shared__ float tile[64][129];
   const int64_t run = blockIdx.x, bh = blockIdx.y;
@@ -493,7 +501,7 @@ __global__ __launch_bounds__(256) void fp4_cols_kernel(const uint16_t* __restric
   for (int c = threadIdx.x; c < 64 * D / 8; c += 256) {
     const int t = c / (D / 8), c8 = (c % (D / 8)) * 8;
     if (t < rows) {
-      v4i raw = *(const v4i*)(x + (bh * N + t0 + t) * D + c8);
+      v4i raw = *(const v4i*)(x + xr.at(bh, t0 + t) + c8);
 #pragma unroll
       for (int e = 0; e < 8; ++e) tile[t][c8 + e] = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
     } else {
@@ -583,8 +591,8 @@ __global__ void convert_kernel(const float* __restrict__ x, int64_t n, int fmt, 
 
 float hadamard_scale(int D) { return (float)(1.0 / std::sqrt((double)D)); }
 
-hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, int D, int T, const float* mean,
-                             int8_t* codes, float* scales, hipStream_t st, bool hadamard) {
+hipError_t launch_quant_int8(const void* x, const Rows16& xr, bool is_f16, int64_t BH, int64_t N, int D, int T,
+                             const float* mean, int8_t* codes, float* scales, hipStream_t st, bool hadamard) {
   const int64_t nblk = (N + T - 1) / T;
   if (nblk == 0 || BH == 0) return hipSuccess;
   dim3 g((unsigned)nblk, (unsigned)BH);
@@ -595,11 +603,11 @@ hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, 
     auto goh = [&](auto cpt) {
       constexpr int C = decltype(cpt)::value;
       if (mean) {
-        if (is_f16) quant_int8_kernel<true, C, true, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
-        else quant_int8_kernel<false, C, true, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
+        if (is_f16) quant_int8_kernel<true, C, true, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales, hs);
+        else quant_int8_kernel<false, C, true, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales, hs);
       } else {
-        if (is_f16) quant_int8_kernel<true, C, false, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
-        else quant_int8_kernel<false, C, false, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales, hs);
+        if (is_f16) quant_int8_kernel<true, C, false, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales, hs);
+        else quant_int8_kernel<false, C, false, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales, hs);
       }
     };
     if (chunks <= 256) goh(std::integral_constant<int, 1>{});
@@ -613,11 +621,11 @@ hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, 
   auto go = [&](auto cpt) {
     constexpr int C = decltype(cpt)::value;
     if (mean) {
-      if (is_f16) quant_int8_kernel<true, C, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
-      else quant_int8_kernel<false, C, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+      if (is_f16) quant_int8_kernel<true, C, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
+      else quant_int8_kernel<false, C, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
     } else {
-      if (is_f16) quant_int8_kernel<true, C, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
-      else quant_int8_kernel<false, C, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+      if (is_f16) quant_int8_kernel<true, C, false><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
+      else quant_int8_kernel<false, C, false><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
     }
   };
   if (chunks <= 256) go(std::integral_constant<int, 1>{});
@@ -626,37 +634,37 @@ hipError_t launch_quant_int8(const void* x, bool is_f16, int64_t BH, int64_t N, 
   else if (chunks <= 2048) go(std::integral_constant<int, 8>{});
   else if (chunks <= 4096) go(std::integral_constant<int, 16>{});
   else if (mean) {
-    if (is_f16) quant_int8_twopass<true, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
-    else quant_int8_twopass<false, true><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+    if (is_f16) quant_int8_twopass<true, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
+    else quant_int8_twopass<false, true><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
   } else {
-    if (is_f16) quant_int8_twopass<true, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
-    else quant_int8_twopass<false, false><<<g, 256, 0, st>>>(xs, N, D, T, mean, codes, scales);
+    if (is_f16) quant_int8_twopass<true, false><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
+    else quant_int8_twopass<false, false><<<g, 256, 0, st>>>(xs, xr, N, D, T, mean, codes, scales);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quant_fp8_channel(const void* x, bool is_f16, int64_t BH, int64_t N, int D, uint8_t* codes_t,
-                                    float* scales, hipStream_t st) {
+hipError_t launch_quant_fp8_channel(const void* x, const Rows16& xr, bool is_f16, int64_t BH, int64_t N, int D,
+                                    uint8_t* codes_t, float* scales, hipStream_t st) {
   const int64_t ns = BH * D;
   fill_u32<<<(unsigned)((ns + 255) / 256), 256, 0, st>>>((uint32_t*)scales, ns, 0u);
   const int64_t nrun = (N + 63) / 64;
   const int64_t t1 = BH * nrun * (D / 8);
   if (t1 > 0) {
-    if (is_f16) channel_amax_kernel<true><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, BH, N, D, (uint32_t*)scales);
-    else channel_amax_kernel<false><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, BH, N, D, (uint32_t*)scales);
+    if (is_f16) channel_amax_kernel<true><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, xr, BH, N, D, (uint32_t*)scales);
+    else channel_amax_kernel<false><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, xr, BH, N, D, (uint32_t*)scales);
   }
   channel_scale_kernel<<<(unsigned)((ns + 255) / 256), 256, 0, st>>>((uint32_t*)scales, ns);
   if (nrun > 0) {
     dim3 g((unsigned)nrun, (unsigned)BH);
-    if (is_f16) fp8_channel_codes_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, scales, codes_t);
-    else fp8_channel_codes_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)x, N, D, scales, codes_t);
+    if (is_f16) fp8_channel_codes_kernel<true><<<g, 256, 0, st>>>((const uint16_t*)x, xr, N, D, scales, codes_t);
+    else fp8_channel_codes_kernel<false><<<g, 256, 0, st>>>((const uint16_t*)x, xr, N, D, scales, codes_t);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, int D, bool nv, int along_tokens,
-                            int mode, const float* mean, uint8_t* codes, uint8_t* scales, hipStream_t st,
-                            bool hadamard) {
+hipError_t launch_quant_fp4(const void* x, const Rows16& xr, bool is_f16, int64_t BH, int64_t N, int D, bool nv,
+                            int along_tokens, int mode, const float* mean, uint8_t* codes, uint8_t* scales,
+                            hipStream_t st, bool hadamard) {
   const uint16_t* xs = (const uint16_t*)x;
   if (hadamard && along_tokens) return hipErrorNotSupported;
   if (!along_tokens) {
@@ -666,8 +674,8 @@ hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, i
     const float hs = hadamard ? hadamard_scale(D) : 0.0f;
     auto go = [&](auto f16c, auto nvc, auto smc) {
       constexpr bool F16 = decltype(f16c)::value, NV = decltype(nvc)::value, SM = decltype(smc)::value;
-      if (hadamard) fp4_rows_kernel<F16, NV, SM, true><<<g, 256, 0, st>>>(xs, BH * N, N, D, mode, mean, codes, scales, hs);
-      else fp4_rows_kernel<F16, NV, SM, false><<<g, 256, 0, st>>>(xs, BH * N, N, D, mode, mean, codes, scales);
+      if (hadamard) fp4_rows_kernel<F16, NV, SM, true><<<g, 256, 0, st>>>(xs, xr, BH * N, N, D, mode, mean, codes, scales, hs);
+      else fp4_rows_kernel<F16, NV, SM, false><<<g, 256, 0, st>>>(xs, xr, BH * N, N, D, mode, mean, codes, scales);
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
@@ -683,11 +691,11 @@ hipError_t launch_quant_fp4(const void* x, bool is_f16, int64_t BH, int64_t N, i
     if (nrun == 0 || BH == 0) return hipSuccess;
     dim3 g((unsigned)nrun, (unsigned)BH);
     if (nv) {
-      if (is_f16) fp4_cols_kernel<true, true><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
-      else fp4_cols_kernel<false, true><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
+      if (is_f16) fp4_cols_kernel<true, true><<<g, 256, 0, st>>>(xs, xr, N, D, mode, codes, scales);
+      else fp4_cols_kernel<false, true><<<g, 256, 0, st>>>(xs, xr, N, D, mode, codes, scales);
     } else {
-      if (is_f16) fp4_cols_kernel<true, false><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
-      else fp4_cols_kernel<false, false><<<g, 256, 0, st>>>(xs, N, D, mode, codes, scales);
+      if (is_f16) fp4_cols_kernel<true, false><<<g, 256, 0, st>>>(xs, xr, N, D, mode, codes, scales);
+      else fp4_cols_kernel<false, false><<<g, 256, 0, st>>>(xs, xr, N, D, mode, codes, scales);
     }
   }
   return hipGetLastError();

@@ -18,8 +18,8 @@ namespace {
 constexpr int RUN = 64;
 
 template <bool F16>
-__global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict__ k, int64_t BH, int64_t N, int D,
-                                                      float* __restrict__ part) {
+__global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict__ k, Rows16 kr, int64_t BH,
+                                                      int64_t N, int D, float* __restrict__ part) {
   const int64_t nrun = (N + RUN - 1) / RUN;
   const int cg = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -28,7 +28,8 @@ __global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict
   const int64_t run = (gid / cg) % nrun, bh = gid / cg / nrun;
   const int64_t t0 = run * RUN;
   const int rows = (int)((N - t0) < RUN ? (N - t0) : RUN);
-  const uint16_t* p = k + (bh * N + t0) * D + c8 * 8;
+  const uint16_t* p = k + kr.at(bh, t0) + c8 * 8;
+  const int64_t sn = kr.sn;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   auto add_row = [&](v4i raw) {
 #pragma unroll
@@ -41,18 +42,18 @@ __global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict
                        // the current one is added (in token order)
     v4i raw[2][16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * D);
+    for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * sn);
 #pragma unroll
     for (int b = 0; b < RUN / 16; ++b) {
       if (b + 1 < RUN / 16) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * D);
+        for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * sn);
       }
 #pragma unroll
       for (int j = 0; j < 16; ++j) add_row(raw[b & 1][j]);
     }
   } else {
-    for (int t = 0; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * D));
+    for (int t = 0; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * sn));
   }
   float* o = part + (bh * nrun + run) * D + c8 * 8;
   *(v4f*)o = v4f{s[0], s[1], s[2], s[3]};
@@ -80,14 +81,15 @@ __global__ __launch_bounds__(256) void smooth_mean(const float* __restrict__ par
 }
 
 template <bool F16>
-__global__ __launch_bounds__(256) void smooth_apply(const uint16_t* __restrict__ k, const float* __restrict__ mean,
-                                                    int64_t BH, int64_t N, int D, uint16_t* __restrict__ ks) {
+__global__ __launch_bounds__(256) void smooth_apply(const uint16_t* __restrict__ k, Rows16 kr,
+                                                    const float* __restrict__ mean, int64_t BH, int64_t N, int D,
+                                                    uint16_t* __restrict__ ks) {
   const int64_t n8 = BH * N * D / 8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t e0 = i * 8;
-    const int64_t bh = e0 / (N * D);
-    const int c0 = (int)(e0 % D);
-    v4i raw = *(const v4i*)(k + e0);
+    const int64_t e0 = i * 8;   // element of the contiguous K_s
+    const int64_t row = e0 / D, bh = row / N;
+    const int c0 = (int)(e0 - row * D);
+    v4i raw = *(const v4i*)(k + kr.at(bh, row - bh * N) + c0);
     const float* mu = mean + bh * D + c0;
     v4i outv;
 #pragma unroll
@@ -103,22 +105,22 @@ __global__ __launch_bounds__(256) void smooth_apply(const uint16_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_smooth_k(const void* k, bool is_f16, int64_t BH, int64_t N, int D, float* mean, void* ks,
-                           float* partials, hipStream_t st) {
+hipError_t launch_smooth_k(const void* k, const Rows16& kr, bool is_f16, int64_t BH, int64_t N, int D, float* mean,
+                           void* ks, float* partials, hipStream_t st) {
   const int64_t nrun = (N + RUN - 1) / RUN;
   const int64_t t1 = BH * nrun * (D / 8);
   if (t1 > 0) {
     dim3 g((unsigned)((t1 + 255) / 256));
-    if (is_f16) smooth_partial<true><<<g, 256, 0, st>>>((const uint16_t*)k, BH, N, D, partials);
-    else smooth_partial<false><<<g, 256, 0, st>>>((const uint16_t*)k, BH, N, D, partials);
+    if (is_f16) smooth_partial<true><<<g, 256, 0, st>>>((const uint16_t*)k, kr, BH, N, D, partials);
+    else smooth_partial<false><<<g, 256, 0, st>>>((const uint16_t*)k, kr, BH, N, D, partials);
   }
   smooth_mean<<<(unsigned)((BH * D + 255) / 256), 256, 0, st>>>(partials, BH, N, D, mean);
   if (ks && BH * N > 0) {
     int64_t n8 = BH * N * D / 8;
     int64_t blocks = (n8 + 255) / 256;
     if (blocks > 256 * 64) blocks = 256 * 64;
-    if (is_f16) smooth_apply<true><<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)k, mean, BH, N, D, (uint16_t*)ks);
-    else smooth_apply<false><<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)k, mean, BH, N, D, (uint16_t*)ks);
+    if (is_f16) smooth_apply<true><<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)k, kr, mean, BH, N, D, (uint16_t*)ks);
+    else smooth_apply<false><<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)k, kr, mean, BH, N, D, (uint16_t*)ks);
   }
   return hipGetLastError();
 }

@@ -28,8 +28,8 @@ constexpr int QBLK = 128, KBLK = 64;
 // Block means rounded to bf16; F32OUT stores them widened to fp32 (exact), for the score
 // kernel's scalar operand.
 template <bool F32OUT>
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ x, int64_t BH, int64_t N, int D, int T,
-                                                   void* __restrict__ means) {
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t BH, int64_t N,
+                                                   int D, int T, void* __restrict__ means) {
   const int64_t nblk = (N + T - 1) / T;
   const int cg = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int64_t blk = (gid / cg) % nblk, bh = gid / cg / nblk;
   const int64_t t0 = blk * T;
   const int rows = (int)((N - t0) < T ? (N - t0) : T);
-  const uint16_t* p = x + (bh * N + t0) * D + c8 * 8;
+  const uint16_t* p = x + xr.at(bh, t0) + c8 * 8;
+  const int64_t sn = xr.sn;
   float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   auto add_row = [&](v4i raw) __attribute__((always_inline)) {
 #pragma unroll
@@ -48,11 +49,11 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   for (; t + 16 <= rows; t += 16) {   // 16 row loads in flight, then the adds in token order
     v4i raw[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) raw[j] = *(const v4i*)(p + (int64_t)(t + j) * D);
+    for (int j = 0; j < 16; ++j) raw[j] = *(const v4i*)(p + (int64_t)(t + j) * sn);
 #pragma unroll
     for (int j = 0; j < 16; ++j) add_row(raw[j]);
   }
-  for (; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * D));
+  for (; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * sn));
   v4i o;
 #pragma unroll
   for (int w = 0; w < 4; ++w) o[w] = (int)pack_bf16x2(s[2 * w] / (float)rows, s[2 * w + 1] / (float)rows);
@@ -389,8 +390,9 @@ size_t thrift_ws_bytes(int64_t B, int64_t Hq, int64_t Hkv, int64_t N, int D) {
          (size_t)SEL_PASSES * (size_t)(B * Hq * S) * 256 * 4;
 }
 
-hipError_t launch_thrift_select(const uint16_t* q, const uint16_t* ks, int64_t B, int64_t Hq, int64_t Hkv, int64_t N,
-                                int D, double frac, int causal, uint8_t* mask, void* ws, hipStream_t st) {
+hipError_t launch_thrift_select(const uint16_t* q, const Rows16& qr, const uint16_t* ks, const Rows16& kr, int64_t B,
+                                int64_t Hq, int64_t Hkv, int64_t N, int D, double frac, int causal, uint8_t* mask,
+                                void* ws, hipStream_t st) {
   const int64_t nQB = (N + QBLK - 1) / QBLK, nKB = (N + KBLK - 1) / KBLK;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   float* qbar = (float*)ws;   // Q block means as fp32 (exact widenings of the bf16 means)
@@ -409,9 +411,9 @@ hipError_t launch_thrift_select(const uint16_t* q, const uint16_t* ks, int64_t B
   if (n_sel > n_valid) n_sel = n_valid;
   const int cg = D / 8;
   int64_t t = B * Hq * nQB * cg;
-  pool_kernel<true><<<(unsigned)((t + 255) / 256), 256, 0, st>>>(q, B * Hq, N, D, QBLK, qbar);
+  pool_kernel<true><<<(unsigned)((t + 255) / 256), 256, 0, st>>>(q, qr, B * Hq, N, D, QBLK, qbar);
   t = B * Hkv * nKB * cg;
-  pool_kernel<false><<<(unsigned)((t + 255) / 256), 256, 0, st>>>(ks, B * Hkv, N, D, KBLK, kbar);
+  pool_kernel<false><<<(unsigned)((t + 255) / 256), 256, 0, st>>>(ks, kr, B * Hkv, N, D, KBLK, kbar);
   dim3 g((unsigned)((nQB + CHUNK_QB - 1) / CHUNK_QB), (unsigned)(B * Hq));
   score_kernel<<<g, 256, 0, st>>>(qbar, kbar, Hq, Hkv, nQB, nKB, D, causal, scores, chist);
   for (int pass = 1; pass < SEL_PASSES; ++pass)

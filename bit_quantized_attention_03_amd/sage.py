@@ -24,7 +24,9 @@ _TORCH_FMT = {torch.bfloat16: BF16, torch.float16: FP16, torch.float32: FP32}
 
 
 class Shape(C.Structure):
-    _fields_ = [("B", C.c_int64), ("H", C.c_int64), ("N", C.c_int64), ("D", C.c_int64)]
+    """[B, H, N, D] and element strides (sb, sh, sn); zero strides mean contiguous."""
+    _fields_ = [("B", C.c_int64), ("H", C.c_int64), ("N", C.c_int64), ("D", C.c_int64),
+                ("sb", C.c_int64), ("sh", C.c_int64), ("sn", C.c_int64)]
 
 
 class Block(C.Structure):
@@ -38,7 +40,7 @@ class QTensorC(C.Structure):
 class AttnParamsC(C.Structure):
     _fields_ = [("causal", C.c_int32), ("sm_scale", C.c_float), ("p_fmt", C.c_int),
                 ("block_mask", C.c_void_p), ("q_hi", C.c_void_p), ("k_hi", C.c_void_p), ("hi_dt", C.c_int),
-                ("p_scale_mode", C.c_int)]
+                ("p_scale_mode", C.c_int), ("q_hi_shape", Shape), ("k_hi_shape", Shape)]
 
 
 _lib = None
@@ -64,7 +66,7 @@ def lib():
         L.sage_quantized_bytes.argtypes = [C.c_int, Block, Shape, C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]
         L.sage_nvfp4_to_mxfp8.argtypes = [C.c_void_p, C.c_void_p, Shape, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
         L.sage_attn_fwd.argtypes = [C.POINTER(QTensorC), C.POINTER(QTensorC), C.POINTER(QTensorC),
-                                    C.POINTER(AttnParamsC), C.c_void_p, C.c_int, C.c_void_p]
+                                    C.POINTER(AttnParamsC), C.c_void_p, C.c_int, Shape, C.c_void_p]
         L.thrift_select_blocks.argtypes = [C.c_void_p, C.c_void_p, C.c_int, Shape, Shape, C.c_int, C.c_int, C.c_double,
                                            C.c_int, C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
         L.thrift_workspace_bytes.restype = C.c_size_t
@@ -105,23 +107,36 @@ def _ptr(t: Optional[torch.Tensor]):
 
 
 def _shape(t: torch.Tensor) -> Shape:
+    """The tensor's [B,H,N,D] and, unless it is contiguous, its element strides."""
     B, H, N, D = t.shape
-    return Shape(B, H, N, D)
+    if t.is_contiguous():
+        return Shape(B, H, N, D, 0, 0, 0)
+    sb, sh, sn, _ = t.stride()
+    return Shape(B, H, N, D, sb, sh, sn)
 
 
 def _dev(*ts):
+    """Tensors the library reads or writes densely: on the GPU and contiguous."""
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
             raise ValueError("tensors must be contiguous and on the GPU")
 
 
+def _dev_rows(*ts):
+    """[B,H,N,D] tensors the library addresses by rows (sage_shape strides): on the GPU with
+    contiguous channels; the library checks the rest of the layout."""
+    for t in ts:
+        if t is not None and (not t.is_cuda or t.dim() != 4 or (t.shape[3] > 1 and t.stride(3) != 1)):
+            raise ValueError("tensors must be on the GPU, 4-d, with contiguous channels")
+
+
 # ------------------------------------------------------------------------------------ steps
 def smooth_k(k: torch.Tensor, want_smoothed: bool = True):
     """K smoothing: returns (mean [B,H,D] fp32, K_s like k or None)."""
-    _dev(k)
+    _dev_rows(k)
     B, H, N, D = k.shape
     mean = torch.empty((B, H, D), dtype=torch.float32, device=k.device)
-    ks = torch.empty_like(k) if want_smoothed else None
+    ks = torch.empty(k.shape, dtype=k.dtype, device=k.device) if want_smoothed else None   # contiguous
     shp = _shape(k)
     ws = torch.empty(max(1, lib().sage_smooth_k_workspace_bytes(shp)), dtype=torch.uint8, device=k.device)
     _check("sage_smooth_k", lib().sage_smooth_k(_ptr(k), _TORCH_FMT[k.dtype], shp, _ptr(mean), _ptr(ks), _ptr(ws),
@@ -146,13 +161,15 @@ class QT:
     block: tuple = (0, 0)
 
     def c(self) -> QTensorC:
-        return QTensorC(self.fmt, _ptr(self.codes), _ptr(self.scales), Shape(*self.shape), Block(*self.block))
+        # a 16-bit operand is the tensor itself, with its own layout
+        shape = _shape(self.codes) if self.fmt in (BF16, FP16) and self.codes.dim() == 4 else Shape(*self.shape)
+        return QTensorC(self.fmt, _ptr(self.codes), _ptr(self.scales), shape, Block(*self.block))
 
 
 def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX, hadamard: bool = False) -> QT:
     """Block quantization (layouts as in sage.h); returns a QT with flat code/scale buffers.
     hadamard: quantize the rows along D times the normalized Hadamard matrix (Q and K only)."""
-    _dev(x)
+    _dev_rows(x)
     mode = mode | (ROTATE_HADAMARD if hadamard else 0)
     cb, sb = quantized_bytes(fmt, block, tuple(x.shape))
     codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=x.device)
@@ -165,7 +182,7 @@ def quantize(x: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX, hadama
 def quantize_smoothed(k: torch.Tensor, mean: torch.Tensor, fmt: int, block: tuple, mode: int = ABSMAX,
                       hadamard: bool = False) -> QT:
     """Quantize K_s = round(k - mean) without storing it (same codes as quantize(K_s, ...))."""
-    _dev(k)
+    _dev_rows(k)
     mode = mode | (ROTATE_HADAMARD if hadamard else 0)
     cb, sb = quantized_bytes(fmt, block, tuple(k.shape))
     codes = torch.empty(max(cb, 16), dtype=torch.uint8, device=k.device)
@@ -204,17 +221,23 @@ def attn_fwd(q: QT, k: QT, v: QT, causal: bool, p_fmt: int, sm_scale: float = 0.
         if q_hi is None or k_hi is None or q_hi.dtype != k_hi.dtype:
             raise ValueError("q_hi and k_hi go together and share one 16-bit dtype")
         hi_dt = _TORCH_FMT[q_hi.dtype]   # the library accepts bf16 only (fp16: not supported)
+    _dev_rows(out, q_hi, k_hi)
+    if v.fmt in (BF16, FP16):
+        _dev_rows(v.codes)
+    if tuple(out.shape) != (B, Hq, N, D):
+        raise ValueError(f"out shape {tuple(out.shape)} != {(B, Hq, N, D)}")
     params = AttnParamsC(int(causal), float(sm_scale), p_fmt, _ptr(block_mask), _ptr(q_hi), _ptr(k_hi), hi_dt,
-                         int(p_search))
+                         int(p_search), _shape(q_hi) if q_hi is not None else Shape(),
+                         _shape(k_hi) if k_hi is not None else Shape())
     qc, kc, vc = q.c(), k.c(), v.c()
     _check("sage_attn_fwd", lib().sage_attn_fwd(C.byref(qc), C.byref(kc), C.byref(vc), C.byref(params), _ptr(out),
-                                                _TORCH_FMT[out.dtype], _stream()))
+                                                _TORCH_FMT[out.dtype], _shape(out), _stream()))
     return out
 
 
 def thrift_select(q: torch.Tensor, k_smoothed: torch.Tensor, frac: float, causal: bool,
                   q_block: int = 128, k_block: int = 64) -> torch.Tensor:
-    _dev(q, k_smoothed)
+    _dev_rows(q, k_smoothed)
     B, Hq, N, D = q.shape
     nQB, nKB = (N + q_block - 1) // q_block, (N + k_block - 1) // k_block
     mask = torch.empty((B, Hq, nQB, nKB), dtype=torch.uint8, device=q.device)
@@ -242,7 +265,7 @@ def decode(q: torch.Tensor, k: QT, v: QT, causal: bool = False, sm_scale: float 
            out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Nq new rows q [B,Hq,Nq,D] against an NVFP4 KV cache: k from quantize(K, NVFP4, (1, 16), ...)
     (rows along D), v from quantize(V, NVFP4, (16, 1), ...) (along the tokens)."""
-    _dev(q)
+    _dev_rows(q)
     B, Hq, Nq, D = q.shape
     out = torch.empty((B, Hq, Nq, D), dtype=out_dtype, device=q.device)
     ks = Shape(*k.shape)
@@ -263,7 +286,8 @@ def decode_noalloc(q: torch.Tensor, k: QT, v: QT, out: torch.Tensor, causal: boo
     """decode() without a workspace: the split partials go to the library's per-GPU scratch
     array (sage_decode_fwd_noalloc).  The caller passes the output out [B,Hq,Nq,D] (fp32 or
     bf16); nothing is allocated.  Calls that overlap on one GPU share the scratch and race."""
-    _dev(q, out)
+    _dev_rows(q)
+    _dev(out)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError(f"out shape {tuple(out.shape)} != q shape {tuple(q.shape)}")
     kc, vc = k.c(), v.c()

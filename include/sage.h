@@ -64,10 +64,18 @@ typedef enum {
   SAGE_ROTATE_HADAMARD = 0x100   /* flag, OR'ed into a mode: Hadamard rows first (see below) */
 } sage_scale_mode;
 
-/* Logical [B, H, N, D] of a tensor.  Every entry point that takes one returns SAGE_EINVAL
- * unless B >= 0, H >= 1, N >= 0, D >= 1, B <= 2^20, B * H <= 65535 (heads index a launch
- * dimension) and N <= 2^31.                                                                */
-typedef struct { int64_t B, H, N, D; } sage_shape;
+/* Logical [B, H, N, D] of a tensor, and its layout: element (b, h, n, d) sits at element
+ * b sb + h sh + n sn + d of the buffer (channels are contiguous).  sb = sh = sn = 0 is the
+ * contiguous layout (H N D, N D, D); a model's [B, N, H, D] tensor is (N H D, D, H D).
+ * Every entry point that takes one returns SAGE_EINVAL unless B >= 0, H >= 1, N >= 0,
+ * 1 <= D <= 16384, B <= 2^20, B * H <= 65535 (heads index a launch dimension) and N <= 2^31.
+ * Strides are read where a declaration says so (the 16-bit inputs, and the attention
+ * output); there they must be non-negative multiples of 16 bytes' worth of elements (8 for
+ * 16-bit data, 4 for fp32 output), no two (b, h, n) rows may overlap, and the largest
+ * offset must stay below 2^62, else SAGE_EINVAL.  Everywhere else (quantized codes, tensors
+ * the library writes) the tensor is contiguous: strides zero or exactly the contiguous
+ * ones, else SAGE_EINVAL.                                                                  */
+typedef struct { int64_t B, H, N, D, sb, sh, sn; } sage_shape;
 
 /* Block of a quantizer.  Supported (tokens, channels):
  *   SAGE_INT8 : (T, D) with T >= 1   — T consecutive tokens x all channels (Q: 128, K: 64)
@@ -105,6 +113,8 @@ typedef struct {
                                  rule of sage_quantize_blocks applied to the block of fp32 P
                                  ("Search Your Block Floating Point Scales!", Method > ScaleSearch).
                                  Must be SAGE_SCALE_ABSMAX for every other p_fmt (else SAGE_EINVAL). */
+  sage_shape q_hi_shape;      /* layout of q_hi: all zero = q's dims, contiguous; else q's dims and */
+  sage_shape k_hi_shape;      /* any valid strides (likewise k_hi with k's dims)                    */
 } sage_attn_params;
 
 /* Library version string (static storage). */
@@ -118,9 +128,9 @@ const char* sage_strerror(int status);
  * fixed order (fp32 running sums over each run of 64 tokens in token order, then a running
  * sum of those partials in run order, then one division by N) and, if k_smoothed_out is
  * not NULL, k_smoothed_out = round_to_dtype(fp32(k - mean)) (round-to-nearest-even).
- *   k              [B,H,N,D] dtype dt (SAGE_BF16 | SAGE_FP16)
+ *   k              [B,H,N,D] dtype dt (SAGE_BF16 | SAGE_FP16), strided as ks says
  *   mean_out       [B,H,D] fp32
- *   k_smoothed_out [B,H,N,D] dtype dt, or NULL
+ *   k_smoothed_out [B,H,N,D] dtype dt (contiguous), or NULL
  *   workspace      >= sage_smooth_k_workspace_bytes(ks) bytes of device memory      */
 int sage_smooth_k(const void* k, sage_fmt dt, sage_shape ks, float* mean_out, void* k_smoothed_out,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -158,7 +168,8 @@ size_t sage_smooth_k_workspace_bytes(sage_shape ks);
  * the block rules above then apply to those values.  The matrix is orthogonal, so quantizing
  * both Q and K this way leaves QK^T unchanged up to quantization, and sage_attn_fwd needs no
  * change.  Along D only (INT8 blocks of T * D <= 32768 elements, SAGE_MXFP4 / SAGE_NVFP4
- * along D) with D in {64, 128}; otherwise SAGE_ENOTSUP.                                    */
+ * along D) with D in {64, 128}; otherwise SAGE_ENOTSUP.
+ * x is read with the strides of xs; codes and scales are written contiguous.              */
 int sage_quantize_blocks(const void* x, sage_fmt in_dt, sage_shape xs, sage_fmt fmt, sage_block block,
                          sage_scale_mode mode, void* codes_out, void* scales_out, hipStream_t stream);
 /* Block quantization of smoothed K without storing it — SageAttention (Technical approach:
@@ -203,11 +214,13 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
  *   q, k SAGE_MXFP8 (block (1, 32)) + v SAGE_MXFP8 (block (32, 1)) + p SAGE_NVFP4 (max-scaled
  *        per 16 keys, then to MXFP8 like sage_nvfp4_to_mxfp8)
  * Tile offsets inside the kernels are 32-bit: N <= 2^24 (else SAGE_EINVAL).
- * out: [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16).  D in {64, 128} for the INT8 sets;
+ * Layouts: q and k (codes) contiguous; a 16-bit v, q_hi and k_hi may be strided (v's row
+ * stride sn <= 2^24 elements); out is [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16) with the
+ * layout os (all zero: contiguous; else os's dims must be q's).  D in {64, 128} for the INT8 sets;
  * the microscaled sets take D = 128 (else SAGE_ENOTSUP) and 4-byte aligned scale arrays
  * (else SAGE_EALIGN); their running max is exact (P is quantized relative to it).        */
 int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtensor* v, const sage_attn_params* p,
-                  void* out, sage_fmt out_dt, hipStream_t stream);
+                  void* out, sage_fmt out_dt, sage_shape os, hipStream_t stream);
 
 /* Thrift block selection — "ThriftAttention: Selective Mixed Precision for Long-Context FP4
  * Attention", ¶1 and ¶3: a small fraction of query-key blocks runs in high precision.
@@ -216,7 +229,8 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
  * sums in token order, one division by the block's length).  Per (b, q-head), over the
  * causal-valid pairs (k_block*kb <= q_block*qb + q_block - 1 when causal), the
  * min(n_valid, ceil(frac * n_valid)) highest scores are selected (ties: lower qb*nKB+kb).
- *   q [B,Hq,N,D], k_smoothed [B,Hkv,N,D] in dt (SAGE_BF16);  mask_out [B,Hq,nQB,nKB] u8.
+ *   q [B,Hq,N,D], k_smoothed [B,Hkv,N,D] in dt (SAGE_BF16), each strided as its shape
+ *   says;  mask_out [B,Hq,nQB,nKB] u8.
  *   D a multiple of 8 (else SAGE_EINVAL) and at most 128 (else SAGE_ENOTSUP).
  *   q_block = 128 and k_block = 64 are supported.  0 <= frac <= 1.  A head's pair count
  *   nQB * nKB must not exceed 2^31 - 1 (N up to about 4.2 million tokens), else SAGE_EINVAL. */
@@ -232,12 +246,12 @@ size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_b
  * NVFP4 values (E2M1 x UE4M3): scores fp32, P rounded to f16 for P.V with fp32 accumulation,
  * the softmax sum of the unrounded P; sm_scale 0 selects 1 / sqrt(D).  q-head h reads KV
  * head h / (Hq / Hkv).
- *   q   [B,Hq,Nq,D] in q_dt (SAGE_BF16 | SAGE_FP16), 16-byte aligned;
+ *   q   [B,Hq,Nq,D] in q_dt (SAGE_BF16 | SAGE_FP16), 16-byte aligned, strided as qs says;
  *   k   SAGE_NVFP4 along D, block (1, 16), shape [B,Hkv,Nk,D]: codes [B,Hkv,Nk,D/2] (16-byte
  *       aligned), UE4M3 scales [B,Hkv,Nk,D/16] (2-byte aligned);
  *   v   SAGE_NVFP4 along the tokens, block (16, 1), shape [B,Hkv,Nk,D]: codes [B,Hkv,D,Np/2],
  *       Np = Nk rounded up to 64 (16-byte aligned), UE4M3 scales [B,Hkv,Np/16,D];
- *   out [B,Hq,Nq,D] in out_dt (SAGE_FP32 | SAGE_BF16);
+ *   out [B,Hq,Nq,D] in out_dt (SAGE_FP32 | SAGE_BF16), contiguous;
  *   workspace >= sage_decode_workspace_bytes(q shape, k shape) bytes of device memory
  *   (partial results of the key splits).
  * D = 128 (else SAGE_ENOTSUP); 1 <= Nk <= 2^26 and Nq <= Nk (else SAGE_EINVAL).            */

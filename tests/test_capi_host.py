@@ -64,7 +64,7 @@ def test_validation_before_launch(L):
     assert L.sage_quantize_blocks(None, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 0, None, None, None) == -1
     q = sage.QTensorC(sage.INT8, None, None, shp)
     p = sage.AttnParamsC(0, 0.0, sage.BF16, None, None, None, sage.BF16)
-    assert L.sage_attn_fwd(C.byref(q), C.byref(q), C.byref(q), C.byref(p), None, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(q), C.byref(q), C.byref(q), C.byref(p), None, sage.FP32, sage.Shape(), None) == -1
     # misaligned pointers (never dereferenced: validation fails first)
     fake = 0x1000_0001
     assert L.sage_quantize_blocks(fake, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 0, 0x2000_0000, 0x3000_0000,
@@ -72,14 +72,14 @@ def test_validation_before_launch(L):
     # unsupported head dimension for attention
     s96 = sage.Shape(1, 1, 128, 96)
     q96 = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, s96, sage.Block(128, 96))
-    assert L.sage_attn_fwd(C.byref(q96), C.byref(q96), C.byref(q96), C.byref(p), 0x1000_0000, sage.FP32, None) == -2
+    assert L.sage_attn_fwd(C.byref(q96), C.byref(q96), C.byref(q96), C.byref(p), 0x1000_0000, sage.FP32, sage.Shape(), None) == -2
     # search mode only for NVFP4
     assert L.sage_quantize_blocks(0x1000_0000, sage.BF16, shp, sage.INT8, sage.Block(128, 128), 1, 0x2000_0000,
                                   0x3000_0000, None) == -1
     # GQA needs Hq to be a multiple of Hkv
     qs = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 3, 128, 128))
     ks = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, sage.Shape(1, 2, 128, 128))
-    assert L.sage_attn_fwd(C.byref(qs), C.byref(ks), C.byref(ks), C.byref(p), 0x1000_0000, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(qs), C.byref(ks), C.byref(ks), C.byref(p), 0x1000_0000, sage.FP32, sage.Shape(), None) == -1
     # thrift: workspace required, frac in [0, 1]
     assert L.thrift_select_blocks(0x1000_0000, 0x1000_0000, sage.BF16, shp, shp, 128, 64, 0.05, 1, 0x1000_0000, None, 0,
                                   None) == -4
@@ -95,10 +95,10 @@ def test_validation_before_launch(L):
     # microscaled attention: D = 128 only, dword-aligned scales
     m64 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 128, 64), sage.Block(1, 32))
     p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
-    assert L.sage_attn_fwd(C.byref(m64), C.byref(m64), C.byref(m64), C.byref(p4), 0x1000_0000, sage.FP32, None) == -2
+    assert L.sage_attn_fwd(C.byref(m64), C.byref(m64), C.byref(m64), C.byref(p4), 0x1000_0000, sage.FP32, sage.Shape(), None) == -2
     mis = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0002, shp, sage.Block(1, 32))
     m128 = sage.QTensorC(sage.MXFP4, 0x1000_0000, 0x1000_0000, shp, sage.Block(1, 32))
-    assert L.sage_attn_fwd(C.byref(mis), C.byref(m128), C.byref(m128), C.byref(p4), 0x1000_0000, sage.FP32, None) == -3
+    assert L.sage_attn_fwd(C.byref(mis), C.byref(m128), C.byref(m128), C.byref(p4), 0x1000_0000, sage.FP32, sage.Shape(), None) == -3
     # P's ScaleSearch: a known mode, and NVFP4 P only
     qi = sage.QTensorC(sage.INT8, 0x1000_0000, 0x1000_0000, shp, sage.Block(128, 128))
     vb = sage.QTensorC(sage.BF16, 0x1000_0000, None, shp)
@@ -106,10 +106,10 @@ def test_validation_before_launch(L):
         pp = sage.AttnParamsC(0, 0.0, p_fmt, None, None, None, sage.BF16, mode)
         vv = vb if p_fmt == sage.BF16 else m128
         qq = qi if p_fmt == sage.BF16 else m128
-        assert L.sage_attn_fwd(C.byref(qq), C.byref(qq), C.byref(vv), C.byref(pp), 0x1000_0000, sage.FP32, None) == -1
+        assert L.sage_attn_fwd(C.byref(qq), C.byref(qq), C.byref(vv), C.byref(pp), 0x1000_0000, sage.FP32, sage.Shape(), None) == -1
     # mixed operand sets are not built
     p8 = sage.AttnParamsC(0, 0.0, sage.NVFP4, None, None, None, sage.BF16)
-    assert L.sage_attn_fwd(C.byref(m128), C.byref(m128), C.byref(m128), C.byref(p8), 0x1000_0000, sage.FP32, None) == -2
+    assert L.sage_attn_fwd(C.byref(m128), C.byref(m128), C.byref(m128), C.byref(p8), 0x1000_0000, sage.FP32, sage.Shape(), None) == -2
     # NVFP4 -> MXFP8: axis flag 0/1, D a multiple of 32 along D
     assert L.sage_nvfp4_to_mxfp8(0x1000_0000, 0x1000_0000, shp, 2, 0x1000_0000, 0x1000_0000, None) == -1
     assert L.sage_nvfp4_to_mxfp8(0x1000_0000, 0x1000_0000, sage.Shape(1, 1, 64, 48), 0, 0x1000_0000, 0x1000_0000,
@@ -175,28 +175,28 @@ def test_operand_blocks_dtypes_and_limits(L):
     for bad_q, bad_k in (((64, 128), (64, 128)), ((128, 128), (128, 128)), ((128, 64), (64, 128)), ((0, 0), (64, 128))):
         q = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(*bad_q))
         k = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(*bad_k))
-        assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(vb), C.byref(p), a, sage.FP32, None) == -1
+        assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(vb), C.byref(p), a, sage.FP32, sage.Shape(), None) == -1
     v8 = sage.QTensorC(sage.E4M3, a, a, shp, sage.Block(32, 1))
     p8 = sage.AttnParamsC(0, 0.0, sage.E4M3, None, None, None, sage.BF16)
-    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(v8), C.byref(p8), a, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(v8), C.byref(p8), a, sage.FP32, sage.Shape(), None) == -1
     mq = sage.QTensorC(sage.MXFP4, a, a, shp, sage.Block(1, 32))
     mv_wrong = sage.QTensorC(sage.MXFP4, a, a, shp, sage.Block(1, 32))
     p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
-    assert L.sage_attn_fwd(C.byref(mq), C.byref(mq), C.byref(mv_wrong), C.byref(p4), a, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(mq), C.byref(mq), C.byref(mv_wrong), C.byref(p4), a, sage.FP32, sage.Shape(), None) == -1
     # masked (Thrift / sink) tiles: bf16 Q and K_s only
     pm16 = sage.AttnParamsC(0, 0.0, sage.BF16, a, a, a, sage.FP16)
-    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(pm16), a, sage.FP32, None) == -2
+    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(pm16), a, sage.FP32, sage.Shape(), None) == -2
     pm32 = sage.AttnParamsC(0, 0.0, sage.BF16, a, a, a, sage.FP32)
-    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(pm32), a, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(pm32), a, sage.FP32, sage.Shape(), None) == -1
     # sequence length limit of the 32-bit tile offsets
     big = sage.Shape(1, 1, (1 << 24) + 1, 128)
     qb = sage.QTensorC(sage.INT8, a, a, big, sage.Block(128, 128))
     kb = sage.QTensorC(sage.INT8, a, a, big, sage.Block(64, 128))
     vbig = sage.QTensorC(sage.BF16, a, None, big)
-    assert L.sage_attn_fwd(C.byref(qb), C.byref(kb), C.byref(vbig), C.byref(p), a, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(qb), C.byref(kb), C.byref(vbig), C.byref(p), a, sage.FP32, sage.Shape(), None) == -1
     ok = sage.Shape(1, 1, 1 << 24, 128)
     qk = sage.QTensorC(sage.INT8, None, None, ok, sage.Block(128, 128))   # passes the limit, then null codes
-    assert L.sage_attn_fwd(C.byref(qk), C.byref(qk), C.byref(qk), C.byref(p), a, sage.FP32, None) == -1
+    assert L.sage_attn_fwd(C.byref(qk), C.byref(qk), C.byref(qk), C.byref(p), a, sage.FP32, sage.Shape(), None) == -1
 
 
 def test_python_binding_rejects_fp16_masked_tiles():
@@ -226,11 +226,11 @@ def test_empty_calls_touch_no_pointer(L):
         ki = sage.QTensorC(sage.INT8, None, None, s, sage.Block(64, 128))
         vb = sage.QTensorC(sage.BF16, None, None, s)
         p = sage.AttnParamsC(1, 0.0, sage.BF16, None, None, None, sage.BF16)
-        assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(p), None, sage.FP32, None) == 0
+        assert L.sage_attn_fwd(C.byref(qi), C.byref(ki), C.byref(vb), C.byref(p), None, sage.FP32, sage.Shape(), None) == 0
         m4 = sage.QTensorC(sage.MXFP4, None, None, s, sage.Block(1, 32))
         m4v = sage.QTensorC(sage.MXFP4, None, None, s, sage.Block(32, 1))
         p4 = sage.AttnParamsC(0, 0.0, sage.MXFP4, None, None, None, sage.BF16)
-        assert L.sage_attn_fwd(C.byref(m4), C.byref(m4), C.byref(m4v), C.byref(p4), None, sage.BF16, None) == 0
+        assert L.sage_attn_fwd(C.byref(m4), C.byref(m4), C.byref(m4v), C.byref(p4), None, sage.BF16, sage.Shape(), None) == 0
         assert L.thrift_select_blocks(None, None, sage.BF16, s, s, 128, 64, 0.05, 1, None, None, 0, None) == 0
         assert L.sage_sink_blocks(s, 128, 64, 1, 1, 1, None, None) == 0
     assert L.sage_smooth_k(None, sage.BF16, sage.Shape(0, 2, 64, 128), None, None, None, 0, None) == 0
@@ -287,3 +287,51 @@ def test_decode_noalloc_validation(L):
     ve = sage.QTensorC(sage.NVFP4, None, None, sage.Shape(1, 2, 100, 128), sage.Block(16, 1))
     assert L.sage_decode_fwd_noalloc(None, sage.BF16, sage.Shape(1, 4, 0, 128), C.byref(ke), C.byref(ve), 0, 0.0,
                                      None, sage.FP32, None) == 0
+
+
+def test_strided_layouts_are_validated(L):
+    """sage_shape strides: checked before any launch (16-byte rows, no overlapping rows), and
+    refused where the operand must be contiguous."""
+    from bit_quantized_attention_03_amd import sage
+    a = 0x1000_0000
+    B, H, N, D = 2, 4, 100, 128
+    # smoothing / quantization inputs: [B, N, H, D] memory is fine, bad strides are not
+    bad = [sage.Shape(B, H, N, D, N * H * D, D, H * D + 4),     # row stride not a multiple of 8 elements
+           sage.Shape(B, H, N, D, N * H * D, D, D - 8),         # rows overlap (stride < D)
+           sage.Shape(B, H, N, D, N * H * D, 8, H * D),         # heads overlap inside a row
+           sage.Shape(B, H, N, D, -8, D, H * D)]                # negative
+    for s in bad:
+        assert L.sage_smooth_k(a, sage.BF16, s, a, None, a, 1 << 30, None) == -1
+        assert L.sage_quantize_blocks(a, sage.BF16, s, sage.INT8, sage.Block(128, D), 0, a, a, None) == -1
+        assert L.thrift_select_blocks(a, a, sage.BF16, s, s, 128, 64, 0.05, 1, a, a, 1 << 30, None) == -1
+    # attention: codes must be contiguous; V (16-bit) and the output may be strided
+    qs = sage.Shape(B, H, N, D)
+    q = sage.QTensorC(sage.INT8, a, a, qs, sage.Block(128, D))
+    k = sage.QTensorC(sage.INT8, a, a, qs, sage.Block(64, D))
+    q_strided = sage.QTensorC(sage.INT8, a, a, sage.Shape(B, H, N, D, N * H * D, D, H * D), sage.Block(128, D))
+    v = sage.QTensorC(sage.BF16, a, None, qs)
+    p = sage.AttnParamsC(0, 0.0, sage.BF16, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(q_strided), C.byref(k), C.byref(v), C.byref(p), a, sage.FP32, sage.Shape(),
+                           None) == -1
+    v_far = sage.QTensorC(sage.BF16, a, None, sage.Shape(B, H, N, D, H * N * (1 << 25), N * (1 << 25), 1 << 25))
+    assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(v_far), C.byref(p), a, sage.FP32, sage.Shape(),
+                           None) == -1                                    # V row stride beyond 2^24
+    assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(v), C.byref(p), a, sage.FP32,
+                           sage.Shape(B, H, N, 64), None) == -1           # output dims are q's
+    assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(v), C.byref(p), a, sage.FP32,
+                           sage.Shape(B, H, N, D, N * H * D, D, H * D + 2), None) == -1   # fp32 rows: 4 elements
+    ph = sage.AttnParamsC(0, 0.0, sage.BF16, a, a, a, sage.BF16, 0, sage.Shape(B, H, N, 64), sage.Shape())
+    assert L.sage_attn_fwd(C.byref(q), C.byref(k), C.byref(v), C.byref(ph), a, sage.FP32, sage.Shape(),
+                           None) == -1                                    # q_hi's dims are q's
+    # decode: the new tokens may be strided, the cache is library-written and contiguous
+    qd = sage.Shape(1, 4, 2, 128, 4 * 2 * 128, 128, 4 * 128 + 4)
+    kn = sage.QTensorC(sage.NVFP4, a, a, sage.Shape(1, 2, 100, 128), sage.Block(1, 16))
+    vn = sage.QTensorC(sage.NVFP4, a, a, sage.Shape(1, 2, 100, 128), sage.Block(16, 1))
+    assert L.sage_decode_fwd(a, sage.BF16, qd, C.byref(kn), C.byref(vn), 0, 0.0, a, sage.FP32, a, 1 << 30,
+                             None) == -1
+    kstr = sage.QTensorC(sage.NVFP4, a, a, sage.Shape(1, 2, 100, 128, 0, 0, 256), sage.Block(1, 16))
+    assert L.sage_decode_fwd(a, sage.BF16, sage.Shape(1, 4, 2, 128), C.byref(kstr), C.byref(vn), 0, 0.0, a,
+                             sage.FP32, a, 1 << 30, None) == -1
+    # head dimension bound
+    assert L.sage_quantized_bytes(sage.INT8, sage.Block(128, 1 << 15), sage.Shape(1, 1, 1, 1 << 15),
+                                  C.byref(C.c_size_t()), C.byref(C.c_size_t())) == -1
