@@ -302,6 +302,7 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
 
 size_t thrift_workspace_bytes(sage_shape qs, sage_shape ks, int q_block, int k_block) {
   if (!shape_ok(qs) || !shape_ok(ks) || q_block != QBLK || k_block != KBLK) return 0;
+  if (((qs.N + QBLK - 1) / QBLK) * ((qs.N + KBLK - 1) / KBLK) > INT32_MAX || qs.D > 128) return 0;   // as the call
   return thrift_ws_bytes(qs.B, qs.H, ks.H, qs.N, (int)qs.D);
 }
 
@@ -330,6 +331,7 @@ int thrift_select_blocks(const void* q, const void* k_smoothed, sage_fmt dt, sag
 
 size_t sage_decode_workspace_bytes(sage_shape qs, sage_shape ks) {
   if (!shape_ok(qs) || !shape_ok(ks) || qs.H % ks.H != 0) return 0;
+  if (ks.N < 1 || ks.N > (1 << 26) || qs.N > ks.N) return 0;   // the shapes sage_decode_fwd accepts
   return decode_ws_bytes(qs.B, qs.H, ks.H, qs.N, ks.N);
 }
 
