@@ -137,15 +137,24 @@ __device__ __forceinline__ v8i pad8(v4i lo) { return __builtin_shufflevector(lo,
 // k * 0.3 / 7; 2: the bit offsets -2, -1, 1 .. 6 on c0 that stay within 0x01..0x7E) and keep
 // the first with the least squared error: e = x - E2M1(x * fp32(1 / s)) * s, e * e summed in
 // fp32 as a pairwise tree in key order.
+// A UE4M3 scale code's value and its fp32 reciprocal (correctly rounded, as the element rule
+// states).  The FP8 kernels build the 128-entry table once per workgroup in LDS: the block
+// scales of P and every ScaleSearch candidate read it instead of dividing.
+struct ScaleRecip {
+  float s, r;
+};
+
 template <class Row>
-__device__ __forceinline__ float p_block_sse(const Row& x, uint32_t c) {
-  const float s = e4m3_to_f32(c), r = 1.0f / s;
+__device__ __forceinline__ float p_block_sse(const Row& x, ScaleRecip sr) {
+  const float s = sr.s, r = sr.r;
   float se[16];
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
     const uint32_t code = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x[i] * r, x[i + 1] * r, 1.0f, 0);
     const auto xh = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
-    const float e0 = x[i] - xh[0] * s, e1 = x[i + 1] - xh[1] * s;
+    // xhat * s is exact in fp32 (E2M1 x UE4M3: at most 6 significant bits), so one fma gives
+    // the difference x - xhat * s with the same single rounding as a product and a subtraction
+    const float e0 = __builtin_fmaf(-xh[0], s, x[i]), e1 = __builtin_fmaf(-xh[1], s, x[i + 1]);
     se[i] = e0 * e0;
     se[i + 1] = e1 * e1;
   }
@@ -157,9 +166,9 @@ __device__ __forceinline__ float p_block_sse(const Row& x, uint32_t c) {
 }
 
 template <int PS, class Row>
-__device__ __forceinline__ uint32_t p_scale_search(const Row& x, float smax, uint32_t c0) {
+__device__ __forceinline__ uint32_t p_scale_search(const Row& x, float smax, uint32_t c0, const ScaleRecip* tab) {
   uint32_t best_c = c0;
-  float best = p_block_sse(x, c0);
+  float best = p_block_sse(x, tab[c0 & 127u]);
   if constexpr (PS == 1) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -168,7 +177,7 @@ __device__ __forceinline__ uint32_t p_scale_search(const Row& x, float smax, uin
                               (float)(0.85 + 6 * 0.3 / 7.0), (float)(0.85 + 7 * 0.3 / 7.0)};
       uint32_t ck = f32_to_e4m3(smax * g[k]);
       ck = ck == 0 ? 1u : ck;
-      const float e = p_block_sse(x, ck);
+      const float e = p_block_sse(x, tab[ck & 127u]);
       if (e < best) { best = e; best_c = ck; }
     }
   } else if constexpr (PS == 2) {
@@ -177,7 +186,7 @@ __device__ __forceinline__ uint32_t p_scale_search(const Row& x, float smax, uin
       const int f = j < 2 ? j - 2 : j - 1;   // -2, -1, 1, 2, .., 6
       const int ck = (int)c0 + f;
       if (ck >= 0x01 && ck <= 0x7E) {
-        const float e = p_block_sse(x, (uint32_t)ck);
+        const float e = p_block_sse(x, tab[ck]);
         if (e < best) { best = e; best_c = (uint32_t)ck; }
       }
     }
@@ -192,6 +201,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   constexpr int NKK = D / 64;     // 64-channel steps of S
   constexpr int FMT = FP4 ? 4 : 0;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  __shared__ ScaleRecip ue4m3_tab[FP4 ? 1 : 128];   // FP8 kernels: UE4M3 code -> (value, 1 / value)
 
   const WgMap wm = map_workgroup(p.total_wg, p.nPairs, CAUSAL);
   const int64_t bh = wm.bh, pr = wm.pair;
@@ -273,6 +283,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
   uint32_t pk[FP4 ? 4 : 8]; // P of the tile the next MFMA phase works on
   uint32_t psc = 0;         // its scale byte (this lane's block)
 
+  if (!FP4 && tid < 128) {   // published by the barrier below
+    const float sv = e4m3_to_f32((uint32_t)tid);
+    ue4m3_tab[tid] = ScaleRecip{sv, sv > 0.0f ? 1.0f / sv : 0.0f};
+  }
   MxDma<D, FP4> dma;
   if (grp == 0) {
     dma.init(a, lane, p.Np);
@@ -382,9 +396,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_mx_kernel(MxParams p) {
         const float amax = __builtin_amdgcn_exp2f(__builtin_fmaf(mb[bb], dq, -moff));
         uint32_t c0 = f32_to_e4m3(amax / 6.0f);
         c0 = c0 == 0 ? 1u : c0;
-        if constexpr (PS != 0) c0 = p_scale_search<PS>(s[bb], amax / 6.0f, c0);
-        sc[bb] = e4m3_to_f32(c0);
-        rc[bb] = 1.0f / sc[bb];
+        if constexpr (PS != 0) c0 = p_scale_search<PS>(s[bb], amax / 6.0f, c0, ue4m3_tab);
+        const ScaleRecip sr = ue4m3_tab[c0 & 127u];
+        sc[bb] = sr.s;
+        rc[bb] = sr.r;
         // largest |xhat| of the block: E2M1 rounding is monotonic, so it is the max element's
         const uint32_t cm = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, amax * rc[bb], 0.0f, 1.0f, 0);
         am[bb] = halves_max(__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cm, 1.0f, 0)[0] * sc[bb]);
