@@ -242,39 +242,33 @@ __global__ void fill_u32(uint32_t* p, int64_t n, uint32_t v) {
 template <bool F16>
 __global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __restrict__ x, Rows16 xr, int64_t BH,
                                                            int64_t N, int D, uint32_t* __restrict__ amax_bits) {
-  // thread: (bh, run of 64 tokens, 8 channels); lanes of one wave cover D/8 channel groups of
-  // consecutive runs
+  // thread: (bh, run of 64 tokens, 4 channels); lanes of one wave cover D/4 channel groups of
+  // consecutive runs.  Four channels a thread (8-byte loads) give this one-round kernel twice
+  // the threads, and so the loads in flight, of eight.
   const int64_t nrun = (N + 63) / 64;
-  const int cg = D / 8;
+  const int cg = D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const bool valid = gid < BH * nrun * cg;
-  const int c8 = (int)(gid % cg);
+  const int c4 = (int)(gid % cg);
   const int64_t run = (gid / cg) % nrun, bh = gid / cg / nrun;
-  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto take = [&](v4i raw) __attribute__((always_inline)) {
+  float m[4] = {0, 0, 0, 0};
+  auto take = [&](v2i raw) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 4; ++e)
       m[e] = __builtin_fmaxf(m[e], __builtin_fabsf(in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))))));
   };
   if (valid) {
     const int64_t t0 = run * 64;
     const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
-    const uint16_t* p = x + xr.at(bh, t0) + c8 * 8;
-    if (rows == 64) {   // four batches of 16 rows, the next one in flight while the current is taken
-      v4i raw[2][16];
+    const uint16_t* p = x + xr.at(bh, t0) + c4 * 4;
+    if (rows == 64) {   // all 64 rows in flight at once
+      v2i raw[64];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * xr.sn);
+      for (int j = 0; j < 64; ++j) raw[j] = *(const v2i*)(p + (int64_t)j * xr.sn);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b + 1 < 4) {
-#pragma unroll
-          for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * xr.sn);
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) take(raw[b & 1][j]);
-      }
+      for (int j = 0; j < 64; ++j) take(raw[j]);
     } else {
-      for (int t = 0; t < rows; ++t) take(*(const v4i*)(p + (int64_t)t * xr.sn));
+      for (int t = 0; t < rows; ++t) take(*(const v2i*)(p + (int64_t)t * xr.sn));
     }
   }
   // Lanes l, l + cg, l + 2cg, ... hold the same channels of consecutive runs; when the whole
@@ -285,15 +279,15 @@ __global__ __launch_bounds__(256) void channel_amax_kernel(const uint16_t* __res
   const bool fold = (cg & (cg - 1)) == 0 && cg < 64 && __all(valid) && bh0 == bh63;
   if (fold) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 4; ++e)
       for (int sft = cg; sft < 64; sft <<= 1) m[e] = __builtin_fmaxf(m[e], __shfl_xor(m[e], sft));
     if (lane < cg) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) atomicMax(amax_bits + bh * D + c8 * 8 + e, __float_as_uint(m[e]));
+      for (int e = 0; e < 4; ++e) atomicMax(amax_bits + bh * D + c4 * 4 + e, __float_as_uint(m[e]));
     }
   } else if (valid) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) atomicMax(amax_bits + bh * D + c8 * 8 + e, __float_as_uint(m[e]));
+    for (int e = 0; e < 4; ++e) atomicMax(amax_bits + bh * D + c4 * 4 + e, __float_as_uint(m[e]));
   }
 }
 
@@ -648,7 +642,7 @@ hipError_t launch_quant_fp8_channel(const void* x, const Rows16& xr, bool is_f16
   const int64_t ns = BH * D;
   fill_u32<<<(unsigned)((ns + 255) / 256), 256, 0, st>>>((uint32_t*)scales, ns, 0u);
   const int64_t nrun = (N + 63) / 64;
-  const int64_t t1 = BH * nrun * (D / 8);
+  const int64_t t1 = BH * nrun * (D / 4);
   if (t1 > 0) {
     if (is_f16) channel_amax_kernel<true><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, xr, BH, N, D, (uint32_t*)scales);
     else channel_amax_kernel<false><<<(unsigned)((t1 + 255) / 256), 256, 0, st>>>((const uint16_t*)x, xr, BH, N, D, (uint32_t*)scales);

@@ -3,9 +3,11 @@
 // before 8-bit quantization by subtracting each channel's mean over the tokens.
 //
 // HBM-bound, 6 bytes per element for 16-bit K (read K twice, write K_s once):
-//   1. smooth_partial: fp32 running sum over each run of 64 tokens, in token order, for 8
-//      channels per thread (one 16-byte load per token row; batches of 16 rows, the next
-//      batch in flight while the current one is added) -> partials [BH, runs, D].
+//   1. smooth_partial: fp32 running sum over each run of 64 tokens, in token order, for 4
+//      channels per thread (one 8-byte load per token row, all 64 rows in flight before the
+//      adds) -> partials [BH, runs, D].  The kernel is a single round of threads, so its time
+//      is about one load round trip: four channels a thread rather than eight double the
+//      threads, and so the bytes in flight.
 //   2. smooth_mean:    per (bh, channel) running sum of the partials in run order, / N.
 //   3. smooth_apply:   K_s = round_to_dtype(fp32(k - mean)), 8 elements per thread.
 // The fixed summation order makes the mean reproducible bit for bit.
@@ -21,43 +23,33 @@ template <bool F16>
 __global__ __launch_bounds__(256) void smooth_partial(const uint16_t* __restrict__ k, Rows16 kr, int64_t BH,
                                                       int64_t N, int D, float* __restrict__ part) {
   const int64_t nrun = (N + RUN - 1) / RUN;
-  const int cg = D / 8;
+  const int cg = D / 4;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= BH * nrun * cg) return;
-  const int c8 = (int)(gid % cg);
+  const int c4 = (int)(gid % cg);
   const int64_t run = (gid / cg) % nrun, bh = gid / cg / nrun;
   const int64_t t0 = run * RUN;
   const int rows = (int)((N - t0) < RUN ? (N - t0) : RUN);
-  const uint16_t* p = k + kr.at(bh, t0) + c8 * 8;
+  const uint16_t* p = k + kr.at(bh, t0) + c4 * 4;
   const int64_t sn = kr.sn;
-  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  auto add_row = [&](v4i raw) {
+  float s[4] = {0, 0, 0, 0};
+  auto add_row = [&](v2i raw) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       uint16_t h = (uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1)));
       s[e] = s[e] + in16_to_f32<F16>(h);
     }
   };
-  if (rows == RUN) {   // a full run: four batches of 16 rows, the next batch in flight while
-                       // the current one is added (in token order)
-    v4i raw[2][16];
+  if (rows == RUN) {   // a full run: all 64 rows in flight at once, then added in token order
+    v2i raw[RUN];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) raw[0][j] = *(const v4i*)(p + (int64_t)j * sn);
+    for (int j = 0; j < RUN; ++j) raw[j] = *(const v2i*)(p + (int64_t)j * sn);
 #pragma unroll
-    for (int b = 0; b < RUN / 16; ++b) {
-      if (b + 1 < RUN / 16) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) raw[(b + 1) & 1][j] = *(const v4i*)(p + (int64_t)(16 * (b + 1) + j) * sn);
-      }
-#pragma unroll
-      for (int j = 0; j < 16; ++j) add_row(raw[b & 1][j]);
-    }
+    for (int j = 0; j < RUN; ++j) add_row(raw[j]);
   } else {
-    for (int t = 0; t < rows; ++t) add_row(*(const v4i*)(p + (int64_t)t * sn));
+    for (int t = 0; t < rows; ++t) add_row(*(const v2i*)(p + (int64_t)t * sn));
   }
-  float* o = part + (bh * nrun + run) * D + c8 * 8;
-  *(v4f*)o = v4f{s[0], s[1], s[2], s[3]};
-  *(v4f*)(o + 4) = v4f{s[4], s[5], s[6], s[7]};
+  *(v4f*)(part + (bh * nrun + run) * D + c4 * 4) = v4f{s[0], s[1], s[2], s[3]};
 }
 
 __global__ __launch_bounds__(256) void smooth_mean(const float* __restrict__ part, int64_t BH, int64_t N, int D,
@@ -108,7 +100,7 @@ __global__ __launch_bounds__(256) void smooth_apply(const uint16_t* __restrict__
 hipError_t launch_smooth_k(const void* k, const Rows16& kr, bool is_f16, int64_t BH, int64_t N, int D, float* mean,
                            void* ks, float* partials, hipStream_t st) {
   const int64_t nrun = (N + RUN - 1) / RUN;
-  const int64_t t1 = BH * nrun * (D / 8);
+  const int64_t t1 = BH * nrun * (D / 4);
   if (t1 > 0) {
     dim3 g((unsigned)((t1 + 255) / 256));
     if (is_f16) smooth_partial<true><<<g, 256, 0, st>>>((const uint16_t*)k, kr, BH, N, D, partials);
