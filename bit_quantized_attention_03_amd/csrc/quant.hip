@@ -46,6 +46,24 @@ __device__ __forceinline__ v4i smooth_chunk(v4i raw, const float* __restrict__ m
   return smooth_vals<F16>(raw, *(const v4f*)mu, *(const v4f*)(mu + 4));
 }
 
+// ------------------------------------------------------------------ INT8 codes
+// The reciprocal of a block scale s > 0, saturated at the largest finite fp32 (1 / s overflows
+// only for a block whose largest magnitude is below about 3.7e-37; an element 0 then keeps code 0).
+__device__ __forceinline__ float int8_recip(float s) {
+  return s > 0.0f ? __builtin_fminf(1.0f / s, 3.40282347e38f) : 0.0f;
+}
+// The INT8 code of fp32(x * r) in the low byte: the product clamped to [-127, 127], then rounded
+// to the nearest integer, ties to even, by one fp32 add of 1.5 * 2^23, after which the low bits
+// of the sum's mantissa hold that integer in two's complement (|value| < 2^22).  Clamping first
+// and rounding after gives the same integer as rounding first.
+__device__ __forceinline__ uint32_t int8_code_bits(float x, float r) {
+  const float v = __builtin_fminf(__builtin_fmaxf(x * r, -127.0f), 127.0f);
+  return __float_as_uint(v + 12582912.0f);
+}
+__device__ __forceinline__ uint32_t pack_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return (a & 0xffu) | ((b & 0xffu) << 8) | ((c & 0xffu) << 16) | (d << 24);
+}
+
 // ------------------------------------------------------------------ Hadamard along D
 // The fast Walsh-Hadamard transform of a row of D values in fp32: stages h = 1, 2, ...,
 // D/2, each replacing the pair (v[j], v[j+h]) (j mod 2h < h) by (v[j] + v[j+h],
@@ -108,10 +126,19 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   const int nchunk = rows * D / 8, cpr = D / 8;
   const uint16_t* base = x + xr.at(bh, t0);   // chunk c: row c / cpr, channels 8 (c % cpr) ..
   v4i raw[CPT];
+  if (256 % cpr == 0) {   // chunks tid + 256 i share their channels: row tid / cpr + i * (256 / cpr)
+    const int r0 = (int)threadIdx.x / cpr, rstep = 256 / cpr;
+    const uint16_t* p0 = base + r0 * xr.sn + ((int)threadIdx.x - r0 * cpr) * 8;
+    const int64_t step = rstep * xr.sn;
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int c = threadIdx.x + 256 * i, r = c / cpr;
-    raw[i] = c < nchunk ? *(const v4i*)(base + r * xr.sn + (c - r * cpr) * 8) : v4i{0, 0, 0, 0};
+    for (int i = 0; i < CPT; ++i)
+      raw[i] = r0 + i * rstep < rows ? *(const v4i*)(p0 + i * step) : v4i{0, 0, 0, 0};
+  } else {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = threadIdx.x + 256 * i, r = c / cpr;
+      raw[i] = c < nchunk ? *(const v4i*)(base + r * xr.sn + (c - r * cpr) * 8) : v4i{0, 0, 0, 0};
+    }
   }
   if (SMOOTH) {
     if ((2048 % D) == 0) {   // chunks tid + 256 i all start at channel 8 tid mod D: one mean slice
@@ -163,22 +190,20 @@ __global__ __launch_bounds__(256) void quant_int8_kernel(const uint16_t* __restr
   __syncthreads();
   amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
   const float s = amax / 127.0f;
-  const float r = s > 0.0f ? 1.0f / s : 0.0f;
+  const float r = int8_recip(s);
   if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
   int8_t* out = codes + (bh * N + t0) * D;
 #pragma unroll
   for (int i = 0; i < CPT; ++i) {
     const int c = threadIdx.x + 256 * i;
     if (c >= nchunk) continue;
-    uint32_t packed[2] = {0u, 0u};
+    uint32_t cb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float xv = HAD ? hv[i][e] : in16_to_f32<F16>((uint16_t)((uint32_t)raw[i][e >> 1] >> (16 * (e & 1))));
-      float q = __builtin_rintf(xv * r);
-      q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-      packed[e >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (e & 3));
+      cb[e] = int8_code_bits(xv, r);
     }
-    *(v2i*)(out + (int64_t)c * 8) = v2i{(int)packed[0], (int)packed[1]};
+    *(v2i*)(out + (int64_t)c * 8) = v2i{(int)pack_bytes(cb[0], cb[1], cb[2], cb[3]), (int)pack_bytes(cb[4], cb[5], cb[6], cb[7])};
   }
 }
 
@@ -215,21 +240,16 @@ __global__ __launch_bounds__(256) void quant_int8_twopass(const uint16_t* __rest
   __syncthreads();
   amax = __builtin_fmaxf(__builtin_fmaxf(red[0], red[1]), __builtin_fmaxf(red[2], red[3]));
   const float s = amax / 127.0f;
-  const float r = s > 0.0f ? 1.0f / s : 0.0f;
+  const float r = int8_recip(s);
   if (threadIdx.x == 0) scales[bh * nblk + blk] = s;
   int8_t* out = codes + (bh * N + t0) * D;
   for (int64_t c = threadIdx.x; c < nchunk; c += 256) {
     v4i raw = *(const v4i*)src(c);
     if (SMOOTH) raw = smooth_chunk<F16>(raw, mean + bh * D + (c * 8) % D);
-    uint32_t packed[2] = {0u, 0u};
+    uint32_t cb[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t h = (uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1)));
-      float q = __builtin_rintf(in16_to_f32<F16>(h) * r);
-      q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
-      packed[e >> 2] |= ((uint32_t)(int)q & 0xffu) << (8 * (e & 3));
-    }
-    *(v2i*)(out + c * 8) = v2i{(int)packed[0], (int)packed[1]};
+    for (int e = 0; e < 8; ++e) cb[e] = int8_code_bits(in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1)))), r);
+    *(v2i*)(out + c * 8) = v2i{(int)pack_bytes(cb[0], cb[1], cb[2], cb[3]), (int)pack_bytes(cb[4], cb[5], cb[6], cb[7])};
   }
 }
 
@@ -308,7 +328,14 @@ __global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* 
   const int64_t t0 = run * 64;
   const int64_t Np = (N + 63) / 64 * 64;
   const int rows = (int)((N - t0) < 64 ? (N - t0) : 64);
-  const float* sc = scales + bh * D;
+  // the channels' reciprocal scales, once per workgroup (saturated at the largest finite fp32,
+  // as for INT8)
+  __shared__ __attribute__((aligned(16))) float rcp[128];
+  for (int c = threadIdx.x; c < D; c += 256) {
+    const float s = scales[bh * D + c];
+    rcp[c] = s > 0.0f ? __builtin_fminf(1.0f / s, 3.40282347e38f) : 0.0f;
+  }
+  __syncthreads();
   const int nchunk = 64 * D / 8;
   for (int c = threadIdx.x; c < nchunk; c += 256) {
     const int t = c / (D / 8), c8 = (c % (D / 8)) * 8;
@@ -318,12 +345,12 @@ __global__ __launch_bounds__(256) void fp8_channel_codes_kernel(const uint16_t* 
       continue;
     }
     v4i raw = *(const v4i*)(x + xr.at(bh, t0 + t) + c8);
+    const v4f r0 = *(const v4f*)&rcp[c8], r1 = *(const v4f*)&rcp[c8 + 4];
+    const float r[8] = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float s = sc[c8 + e];
-      float r = s > 0.0f ? 1.0f / s : 0.0f;
       float v = in16_to_f32<F16>((uint16_t)((uint32_t)raw[e >> 1] >> (16 * (e & 1))));
-      tile[(c8 + e) * PITCH + t] = f32_to_e4m3(v * r);
+      tile[(c8 + e) * PITCH + t] = f32_to_e4m3(v * r[e]);
     }
   }
   __syncthreads();

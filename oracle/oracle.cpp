@@ -285,7 +285,8 @@ void orc_hadamard_rows(const uint16_t* x, int dt, int64_t rows, int64_t D, float
 // A block is `block_tokens` consecutive tokens x all D channels of one (b, h); the last
 // block may be short.  Symmetric absmax rule: s = fp32(amax / 127), r = fp32(1 / s),
 // code = clamp(round_half_even(fp32(x * r)), -127, 127); an all-zero block has s = 0 and
-// codes 0.  Scales are [B, H, ceil(N / block_tokens)] fp32.  hadamard: quantize the
+// codes 0.  r is saturated at the largest finite fp32: 1 / s overflows only when amax is
+// below about 3.7e-37, and an infinite r would turn an element 0 into 0 * inf = NaN.  Scales are [B, H, ceil(N / block_tokens)] fp32.  hadamard: quantize the
 // transformed rows (hadamard_row) instead of x.
 void orc_quant_int8(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N, int64_t D,
                     int64_t block_tokens, int hadamard, int8_t* codes, float* scales) {
@@ -300,7 +301,7 @@ void orc_quant_int8(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N
           for (int64_t c = 0; c < D; ++c) amax = std::max(amax, std::fabs(x[idx4(b, h, t, c, H, N, D)]));
         float s = amax / 127.0f;
         scales[(b * H + h) * nblk + blk] = s;
-        float r = s > 0.0f ? 1.0f / s : 0.0f;
+        float r = s > 0.0f ? std::min(1.0f / s, std::numeric_limits<float>::max()) : 0.0f;
         for (int64_t t = t0; t < t1; ++t)
           for (int64_t c = 0; c < D; ++c) {
             int64_t i = idx4(b, h, t, c, H, N, D);
@@ -311,8 +312,8 @@ void orc_quant_int8(const uint16_t* x16, int dt, int64_t B, int64_t H, int64_t N
 }
 
 // ----- FP8 E4M3 per-channel quantization of V -----
-// Per (b, h, channel): s_c = fp32(amax_c / 448) over all N tokens, r_c = fp32(1 / s_c),
-// code = E4M3(fp32(v * r_c)).  Codes are written channel-major, [B, H, D, Np] with Np = N
+// Per (b, h, channel): s_c = fp32(amax_c / 448) over all N tokens, r_c = fp32(1 / s_c)
+// (saturated at the largest finite fp32, as for INT8), code = E4M3(fp32(v * r_c)).  Codes are written channel-major, [B, H, D, Np] with Np = N
 // rounded up to 64 and zero codes in the padding (tokens contiguous: the contraction axis of
 // P.V), scales [B, H, D] fp32.
 void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int64_t N, int64_t D,
@@ -324,7 +325,7 @@ void orc_quant_fp8_channel(const uint16_t* v, int dt, int64_t B, int64_t H, int6
         for (int64_t t = 0; t < N; ++t) amax = std::max(amax, std::fabs(in_value(v, idx4(b, h, t, c, H, N, D), dt)));
         float s = amax / 448.0f;
         scales[(b * H + h) * D + c] = s;
-        float r = s > 0.0f ? 1.0f / s : 0.0f;
+        float r = s > 0.0f ? std::min(1.0f / s, std::numeric_limits<float>::max()) : 0.0f;   // saturated as for INT8
         const int64_t Np = (N + 63) / 64 * 64;
         for (int64_t t = 0; t < Np; ++t)
           codes_t[((b * H + h) * D + c) * Np + t] = t < N ? e4m3_encode(in_value(v, idx4(b, h, t, c, H, N, D), dt) * r) : 0;

@@ -93,6 +93,29 @@ def test_int8_ties_round_half_even_bit_exact():
                           s_o.view(np.uint32))
 
 
+def test_tiny_block_reciprocal_saturates_bit_exact():
+    # a block and a channel whose largest magnitude is 2^-126 (1 / s overflows): the same
+    # saturated reciprocal as the oracle, and the hand-derived codes of the oracle pins
+    from tests.test_oracle_quant import TINY_E4M3, TINY_INT8, tiny_input
+    sage = _sage()
+    xb, vals = tiny_input()
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    print("[case] tiny INT8 block and E4M3 channel", flush=True)
+    qt = sage.quantize(x, sage.INT8, (64, x.shape[-1]))
+    got = qt.codes.cpu().numpy().view(np.int8).reshape(xb.shape)
+    c_o, s_o = oracle.quant_int8(xb, 0, 64)
+    assert np.array_equal(got, c_o)
+    assert list(got[0, 0, :len(vals), 0]) == [c for a in TINY_INT8 for c in (a, -a)]
+    assert np.array_equal(qt.scales.cpu().view(torch.float32).numpy().reshape(s_o.shape).view(np.uint32),
+                          s_o.view(np.uint32))
+    qf = sage.quantize(x, sage.E4M3, (0, 1))
+    c_f, s_f = oracle.quant_fp8_channel(xb, 0)
+    assert np.array_equal(u8(qf.codes).reshape(c_f.shape), c_f)
+    assert list(c_f[0, 0, 0, :len(vals)]) == [c for a in TINY_E4M3 for c in (a, a | 0x80)]
+    assert np.array_equal(qf.scales.cpu().view(torch.float32).numpy().reshape(s_f.shape).view(np.uint32),
+                          s_f.view(np.uint32))
+
+
 @pytest.mark.parametrize("fmt,block,mode", [("INT8", (64, 128), 0), ("INT8", (100, 128), 0), ("INT8", (4096, 128), 0),
                                             ("MXFP4", (1, 32), 0), ("NVFP4", (1, 16), 1), ("NVFP4", (1, 16), 2)])
 def test_quantize_smoothed_equals_quantize_of_smoothed(fmt, block, mode):

@@ -142,7 +142,47 @@ def test_int8_ties_round_half_even():
     assert np.array_equal(codes, want)
 
 
+# A block (or channel) whose largest magnitude is 2^-126: its scale s = amax / 127 (or / 448)
+# is subnormal and 1 / s overflows fp32.  The reciprocal saturates at the largest finite fp32,
+# F = (2 - 2^-23) * 2^127, so x * r = x * F exactly for these powers of two: 2^-126 -> 4 - 2^-22,
+# 3 * 2^-128 -> 3 - 2^-22 (rounded), 2^-127 -> 2 - 2^-23, 2^-128 -> 1 - 2^-24, 2^-129 ->
+# 0.5 - 2^-25; and an element 0 keeps code 0 (an infinite r would give 0 * inf = NaN).  Every
+# value is exact in bf16 (subnormals from 2^-127 down).
+TINY_VALUES = [2.0 ** -126, 3 * 2.0 ** -128, 2.0 ** -127, 2.0 ** -128, 2.0 ** -129, 0.0]
+TINY_INT8 = [4, 3, 2, 1, 0, 0]                      # round half to even of the products above
+# E4M3 (bias 7, 3 mantissa bits) nearest to the products: 4.0, 3.0, 2.0, 1.0, 0.5, 0
+TINY_E4M3 = [0x48, 0x44, 0x40, 0x38, 0x30, 0x00]
+
+
+def tiny_input(D=64):
+    """One 64-token block: TINY_VALUES and their negatives along channel 0 (tokens 0..11),
+    zeros elsewhere.  Returns the bf16 input [1, 1, 64, D] and the values."""
+    x = np.zeros((1, 1, 64, D), np.float32)
+    vals = [v for a in TINY_VALUES for v in (a, -a)]
+    x[0, 0, :len(vals), 0] = vals
+    return _bf16(x), np.array(vals)
+
+
+def test_int8_tiny_block_reciprocal_saturates():
+    xb, vals = tiny_input()
+    assert np.array_equal(_val(xb)[0, 0, :len(vals), 0], vals.astype(np.float32))   # exact in bf16
+    codes, scales = oracle.quant_int8(xb, oracle.BF16, 64)
+    assert 0 < scales[0, 0, 0] < 2.0 ** -126 and np.isinf(np.float32(1) / scales[0, 0, 0])
+    want = [c for a in TINY_INT8 for c in (a, -a)]
+    assert list(codes[0, 0, :len(vals), 0]) == want
+    assert np.all(codes[0, 0, len(vals):] == 0) and np.all(codes[0, 0, :, 1:] == 0)
+
+
 # ---------------------------------------------------------------- FP8 per channel
+
+def test_fp8_channel_tiny_reciprocal_saturates():
+    xb, vals = tiny_input()
+    codes, scales = oracle.quant_fp8_channel(xb, oracle.BF16)     # codes [1, 1, D, 64]
+    assert 0 < scales[0, 0, 0] < 2.0 ** -126 and np.all(scales[0, 0, 1:] == 0)
+    want = [c for a in TINY_E4M3 for c in (a, a | 0x80)]      # -0 keeps its sign: 0x80
+    assert list(codes[0, 0, 0, :len(vals)]) == want
+    assert np.all(codes[0, 0, 0, len(vals):] == 0) and np.all(codes[0, 0, 1:] == 0)
+
 
 def test_fp8_channel_half_step(llm_small):
     _, _, v = llm_small
