@@ -51,8 +51,8 @@ STEP_TEXT = {
                     "nvfp4_to_mxfp8 + attn_fwd",
 }
 
-KERNEL_SOURCES = {"int8": ("attn_i8_pipe.hip", "attn_common.hpp"), "thrift": ("attn_i8.hip", "attn_common.hpp"),
-                  "sink": ("attn_i8.hip", "attn_common.hpp"),
+KERNEL_SOURCES = {"int8": ("attn_i8_pipe.hip", "attn_common.hpp"), "thrift": ("attn_i8_pipe.hip", "attn_common.hpp"),
+                  "sink": ("attn_i8_pipe.hip", "attn_common.hpp"),
                   "int8_fp8pv": ("attn_i8.hip", "attn_common.hpp"),
                   "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp"),
                   "decode": ("decode.hip",)}

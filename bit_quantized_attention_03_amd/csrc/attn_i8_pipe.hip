@@ -29,6 +29,13 @@
 // iteration t issues K(t+3) and V(t+1), each wave waits for its own share two phases later,
 // and the barrier that opens the next phase publishes them.  Three buffers of each kind
 // rotate inside one LDS array.
+//
+// Thrift (ThriftAttention, ¶1, ¶3: one softmax over INT8 tiles and a few tiles in high
+// precision, chosen by a block mask).  With a mask, the S of a flagged tile is computed again
+// on bf16 Q and K_s rows read from global memory, after the interleaved INT8 products (whose
+// result it replaces), and stored in the same accumulators as integers S * 2^k, so that the
+// softmax treats both kinds alike; the tile's dequantization factor is sm_scale * log2(e) *
+// 2^-k.  The workgroup's two mask rows are copied to LDS at the start.
 #include "attn_common.hpp"
 #include "device.hpp"
 #include "kernels.hpp"
@@ -48,7 +55,12 @@ struct PipeParams {
   int64_t Hq, Hkv, N, nQB, nKB, nPairs, total_wg;
   float sm_log2;   // sm_scale * log2(e), rounded to fp32
   Rows16 vr, outr; // rows of V (per KV head) and of the output
+  // Thrift: block mask [B, Hq, nQB, nKB] (1: the tile runs on bf16 Q and K_s) and those rows
+  const uint8_t* mask;
+  const uint16_t* qhi; const uint16_t* khi;
+  Rows16 qhr, khr;
 };
+
 
 // K tile (int8 [64][D]): 16-byte chunk c of row r at chunk position c ^ k_swz(r).  An operand
 // read (ds_read_b128) serves 16 lanes per pass, which must fall in 16 distinct 16-byte bank
@@ -167,7 +179,7 @@ struct PipeDma {
   }
 };
 
-template <int D, bool CAUSAL, bool VF16, bool OUT_BF16>
+template <int D, bool CAUSAL, bool VF16, bool OUT_BF16, bool THRIFT>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p, const float* __restrict__ k_scales) {
   constexpr int NCC = D / 32;   // 32-channel chunks of O and 32-channel k-slices of S
   constexpr int K_BYTES = KT * D, V_BYTES = KT * 2 * D;
@@ -238,11 +250,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   uint32_t pk[16];   // bf16 P of the tile the next P.V products work on (pairs of keys)
   // dequantization factor (s_q s_k sm_scale log2 e) of the tile being softmaxed, from the K
   // block scale loaded at the end of the previous iteration
-  auto dq_of = [&](float ks) __attribute__((always_inline)) {
-    return __builtin_fmaxf(qscale * ks * p.sm_log2, 1.17549435e-38f);
-  };
   float dq = 0.0f;
   float ksc_next = nT > 0 ? kscales[0] : 0.0f;
+  // Thrift: whether the tile whose S is being computed runs on bf16, its scores then in units
+  // of 2^-k (wave-uniform); the dequantization factor of the next softmax is qs_use * ksc_next *
+  // sm_scale * log2(e), qs_use * ksc_next being s_q s_k for an INT8 tile and 2^-k for a bf16 one
+  bool hi_nxt = false;
+  int k_nxt = 0;
+  float qs_use = qscale;
+
+  // Thrift: the mask rows of the workgroup's two Q blocks (wave group g reads row g), zero past
+  // the mask's last Q block; published by the barrier below
+  __shared__ uint8_t mlds[THRIFT ? 2 * PIPE_MAX_MASK_TILES : 1];
+  if constexpr (THRIFT) {
+    for (int i = tid; i < 2 * (int)p.nKB; i += NTHREADS) {
+      const int64_t qbi = 2 * pr + i / (int)p.nKB;
+      mlds[i] = qbi < p.nQB ? p.mask[(bh * p.nQB + qbi) * p.nKB + i % (int)p.nKB] : (uint8_t)0;
+    }
+  }
+  // tile tt of this wave runs on bf16 Q and K_s (wave-uniform)
+  auto hi_tile = [&](int tt) __attribute__((always_inline)) -> bool {
+    if constexpr (!THRIFT) return false;
+    else return tt <= tl && __builtin_amdgcn_readfirstlane((int)mlds[(w >> 2) * (int)p.nKB + tt]) != 0;
+  };
 
   PipeDma<D> dma;
   dma.init(p, bkv, w, lane);
@@ -267,6 +297,46 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     for (int kc = 1; kc < NCC; ++kc)
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) sacc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kc][bb], qf[kc], sacc[bb], 0, 0, 0);
+  };
+  // Thrift tile tt: S^T on bf16 K_s and Q fragments straight from global memory (L2), in the
+  // key order of the INT8 products.  The fp32 scores are stored in the INT8 accumulators as
+  // integers S * 2^k, k the wave-uniform exponent that brings the tile's largest |S| into
+  // [2^22, 2^23): the softmax then converts them like INT8 sums, and dequantizes them with
+  // sm_scale * log2(e) * 2^-k.  The scaling by 2^k is exact; the rounding to an integer moves a
+  // score by at most 2^-24 of the tile's largest.  Returns k.
+  auto s_hi = [&](int tt) __attribute__((always_inline)) -> int {
+    v16f f[2] = {v16f{}, v16f{}};
+    // rows past N read row N-1 instead (no branches around the loads): their keys are masked
+    // and their query rows are never stored, and every input value is finite
+    const int64_t last = p.N - 1;
+    const int64_t k0 = (int64_t)tt * KT + tile_key(0, li), k1 = (int64_t)tt * KT + tile_key(1, li);
+    const uint16_t* qp = p.qhi + p.qhr.at(bh, qrow < last ? qrow : last) + 8 * lh;
+    const uint16_t* kp0 = p.khi + p.khr.at(bkv, k0 < last ? k0 : last) + 8 * lh;
+    const uint16_t* kp1 = p.khi + p.khr.at(bkv, k1 < last ? k1 : last) + 8 * lh;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const v8bf qh = *(const v8bf*)(qp + 16 * kc);
+      const v8bf kh0 = *(const v8bf*)(kp0 + 16 * kc);
+      const v8bf kh1 = *(const v8bf*)(kp1 + 16 * kc);
+      f[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh0, qh, f[0], 0, 0, 0);
+      f[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh1, qh, f[1], 0, 0, 0);
+    }
+    float mx = 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = __builtin_fmaxf(mx, __builtin_fabsf(f[bb][r]));
+    mx = wave_max(mx);
+    // mx = m * 2^e with 1 <= m < 2 (mx = 0: e = -127): k = 22 - e, kept within fp32's exponents
+    const uint32_t mb = (uint32_t)__builtin_amdgcn_readfirstlane((int)__float_as_uint(mx));
+    const int e = (int)((mb >> 23) & 255u) - 127;
+    const int k = 22 - e > 126 ? 126 : 22 - e;
+    const float sc = __builtin_ldexpf(1.0f, k);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[bb][r] = (int)__builtin_rintf(f[bb][r] * sc);
+    return k;
   };
   auto v_read = [&](uint32_t vbs, int kg, int cc) __attribute__((always_inline)) -> v8bf {
     const uint8_t* a0 = smem + vbs + vro[cc] + 8 * kg * 2 * D;
@@ -363,9 +433,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
 
   // ---- prologue: S(0); the copies of K(2) and V(0) land during iteration 0
   if (tl >= 0) {
-    v4i kf0[NCC][2];
-    k_frags(kbuf(0), kf0);
-    s_mfma(kf0);
+    if (hi_tile(0)) {
+      ksc_next = __builtin_ldexpf(1.0f, -s_hi(0));
+      qs_use = 1.0f;
+    } else {
+      v4i kf0[NCC][2];
+      k_frags(kbuf(0), kf0);
+      s_mfma(kf0);
+    }
   }
   // the copies of "phase -2" (K(2), V(0); a tile past the last re-copies the last)
   dma.k_tile(nT > 2 ? 2 : nT - 1, lds0 + kbuf(2), w);
@@ -419,7 +494,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     // consumed here, before any LDS read of this half, because scalar and LDS returns share a
     // counter and scalar ones come back out of order (an LDS wait with a scalar load
     // outstanding waits for everything).
-    dq = dq_of(ksc_next);
+    dq = __builtin_fmaxf(qs_use * ksc_next * p.sm_log2, 1.17549435e-38f);
     pin(dq);
     __builtin_amdgcn_sched_barrier(0);
     const int j1 = j == 2 ? 0 : j + 1, j2 = j == 0 ? 2 : j - 1;
@@ -484,6 +559,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     constexpr int KIND = decltype(kindc)::value;
     constexpr bool FAST = KIND == 0;
     begin_half();
+    hi_nxt = false;
     if constexpr (KIND != 2) {
       if (FAST) {
         if (grp == 1) copies(t + 1, j == 2 ? 0 : j + 1);
@@ -497,10 +573,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
 #pragma unroll
         for (int i = 0; i < 2 * NCC; ++i) { SCHED_GROUP(SG_MFMA, 1, 0); SCHED_GROUP(SG_VALU, 14, 0); }
         __builtin_amdgcn_sched_barrier(0);
+        hi_nxt = hi_tile(t + 1);   // Thrift: S(t+1) redone on bf16 (rare; outside the interleave)
+        if (THRIFT && hi_nxt) k_nxt = s_hi(t + 1);
       } else {
         const bool do_sm = t <= tl, do_s = do_sm && t + 1 <= tl;
         if (grp == 1) copies(t + 1, j == 2 ? 0 : j + 1);
         if (do_s) s_mfma(kf);
+        hi_nxt = do_s && hi_tile(t + 1);
+        if (THRIFT && hi_nxt) k_nxt = s_hi(t + 1);
         if (do_sm) {
           soft_b(sm, 2);
           soft_b(sm, 3);
@@ -511,6 +591,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
       copies(t + 1, j == 2 ? 0 : j + 1);
     }
     if (t + 1 < nT) ksc_next = kscales[t + 1];   // consumed after the next barrier
+    qs_use = qscale;
+    if (THRIFT && hi_nxt) {
+      ksc_next = __builtin_ldexpf(1.0f, -k_nxt);
+      qs_use = 1.0f;
+    }
     // group 0: the copies of phase 2t-2 (its H1(t-1)) have landed; those of phase 2t may fly
     if (grp == 0) wait_copies();
   };
@@ -561,8 +646,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
 template <int D, bool CAUSAL, bool VF16, bool OUT_BF16>
 hipError_t launch_pipe(const PipeParams& p, hipStream_t st) {
   if (p.total_wg == 0) return hipSuccess;
-  hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16>), dim3((unsigned)p.total_wg), dim3(NTHREADS), 0,
-                     st, p, p.ks);
+  if (p.mask)
+    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16, true>), dim3((unsigned)p.total_wg), dim3(NTHREADS),
+                       0, st, p, p.ks);
+  else
+    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16, false>), dim3((unsigned)p.total_wg),
+                       dim3(NTHREADS), 0, st, p, p.ks);
   return hipGetLastError();
 }
 
@@ -586,6 +675,9 @@ hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st) {
   p.v = (const uint16_t*)a.v_codes;
   p.out = a.out;
   p.vr = a.vr; p.outr = a.outr;
+  p.mask = a.mask; p.qhi = a.q_hi; p.khi = a.k_hi;
+  p.qhr = a.qhr; p.khr = a.khr;
+  if (p.mask && (a.N + KT - 1) / KT > PIPE_MAX_MASK_TILES) return hipErrorInvalidValue;   // mask rows past LDS
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;
   p.nPairs = (p.nQB + 1) / 2;
