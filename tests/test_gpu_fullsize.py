@@ -37,17 +37,19 @@ def test_full_size_sampled_parity(name, causal, variant):
 
 LARGE = [
     # a ragged sequence four times the longest workload's, GQA 2:1, causal
-    (dict(B=1, Hq=2, Hkv=1, N=131149), True),
+    (dict(B=1, Hq=2, Hkv=1, N=131149), True, "int8"),
     # B * H at the library's limit of 65535 (heads index a launch dimension)
-    (dict(B=3, Hq=21845, Hkv=21845, N=16, D=64), False),
+    (dict(B=3, Hq=21845, Hkv=21845, N=16, D=64), False, "int8"),
+    # Thrift past the pipelined kernel's 4096 K tiles of mask in LDS (4097 tiles): the other kernel
+    (dict(B=1, Hq=2, Hkv=1, N=262185), True, "thrift"),
 ]
 
 
-@pytest.mark.parametrize("ov,causal", LARGE)
-def test_large_sizes_sampled_parity(ov, causal):
-    w = I.workload("llm_int8", **ov)
-    print(f"[case] large {ov} causal={causal}", flush=True)
-    _sampled_parity(w, causal, "int8", whole_heads=False)
+@pytest.mark.parametrize("ov,causal,variant", LARGE)
+def test_large_sizes_sampled_parity(ov, causal, variant):
+    w = I.workload("thrift_long" if variant == "thrift" else "llm_int8", **ov)
+    print(f"[case] large {ov} causal={causal} variant={variant}", flush=True)
+    _sampled_parity(w, causal, variant, whole_heads=False)
 
 
 def _sampled_parity(w, causal, variant, whole_heads=True):
