@@ -382,6 +382,8 @@ ATT_CASES = [
     ("fp4_search", dict(B=2, Hq=4, Hkv=2, N=640), False, "nvfp4_search"),  # GQA
     ("thrift_long", dict(B=1, Hq=4, Hkv=2, N=1100), True, "sink"),
     ("thrift_long", dict(B=1, Hq=2, Hkv=1, N=640), False, "sink"),
+    ("thrift_long", dict(B=1, Hq=4, Hkv=2, N=777, D=64), True, "thrift"),   # d = 64 forms
+    ("thrift_long", dict(B=1, Hq=2, Hkv=2, N=450, D=64), False, "sink"),
 ]
 
 
