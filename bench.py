@@ -191,6 +191,13 @@ def run_decode(args, w):
             ev.append((e0, e1))
         return out
 
+    # a call takes about 65 us: a few warm-up calls leave the GPU clocks ramping, so untimed calls
+    # run for 0.2 s first and the timed steps see the steady state a serving loop sees
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < 0.2:
+        for _ in range(64):
+            step(False)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
