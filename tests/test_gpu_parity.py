@@ -403,6 +403,26 @@ def test_attention_parity(name, ov, causal, variant):
     print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
 
 
+@pytest.mark.parametrize("frac", [0.0, 1.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_thrift_no_tile_or_every_tile(frac, causal):
+    # the selection at its two ends: no tile in bf16, or every tile (the first, the ragged last
+    # and the causal diagonal included), against the oracle with the same selection
+    sage = _sage()
+    w = I.workload("thrift_long", B=1, Hq=2, Hkv=1, N=333)
+    q, k, v = I.make_qkv(w, seed=4)
+    print(f"[case] thrift frac={frac} causal={causal}", flush=True)
+    res = sage.forward(*_cuda(q, k, v), causal=causal, variant="thrift", thrift_frac=frac)
+    torch.cuda.synchronize()
+    orc = oracle_pass(q, k, v, causal, "thrift", frac=frac)
+    assert np.array_equal(res.mask.cpu().numpy(), orc["mask"])
+    if frac == 1.0:
+        nQB, nKB = orc["mask"].shape[-2:]
+        valid = [(i, j) for i in range(nQB) for j in range(nKB) if not causal or 64 * j <= 128 * i + 127]
+        assert all(orc["mask"][0, 0, i, j] for i, j in valid)
+    check_out(res.out.cpu().numpy(), orc["out"], f"thrift frac={frac} causal={causal}")
+
+
 @pytest.mark.parametrize("variant", ["sink", "thrift"])
 def test_fp16_masked_tiles_rejected(variant):
     # the masked tiles run on bf16 matrix instructions: fp16 Q and K_s get a clean error
