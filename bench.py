@@ -41,6 +41,16 @@ CPU_SHARE = 16
 
 # what one timed step runs, per variant
 _Q_K = "smooth_k (mean) + quantize (Q per 128-token block; K per 64-token block, the smoothing fused)"
+_K_ONLY = "smooth_k (mean) + quantize (K per 64-token block, the smoothing fused)"
+_Q_IN = " (Q in 16 bits, quantized per 128-token block inside the attention kernel)"
+# the bf16 P.V INT8 variants with Q quantized inside the attention kernel (--fuse-q)
+STEP_TEXT_FUSED_Q = {
+    "int8": _K_ONLY + " + attn_fwd" + _Q_IN + " (V stays bf16)",
+    "thrift": _K_ONLY + " + thrift_select (pooled-score block mask) + attn_fwd" + _Q_IN
+              + " (V bf16; selected tiles on bf16 Q, K)",
+    "sink": _K_ONLY + " + sink_select (first and last valid K block) + attn_fwd" + _Q_IN
+            + " (V bf16; those tiles on bf16 Q, K)",
+}
 STEP_TEXT = {
     "int8": _Q_K + " + attn_fwd (V stays bf16)",
     "thrift": _Q_K + " + thrift_select (pooled-score block mask) + attn_fwd (V bf16; selected tiles on bf16 Q, K)",
@@ -287,9 +297,15 @@ def traffic_from(dirs, key: str, kernel_res, out_path: str):
     print(json.dumps({key: db[key]}))
 
 
-def prepare(sage, variant: str, q, k, v, causal: bool, had: bool = False):
+def fuses_q(variant: str, had: bool, fuse_q: bool) -> bool:
+    """Whether Q goes to the attention kernel in 16 bits (quantized there)."""
+    return fuse_q and not had and variant in ("int8", "thrift", "sink")
+
+
+def prepare(sage, variant: str, q, k, v, causal: bool, had: bool = False, fuse_q: bool = False):
     """Smoothing, quantization and block selection of one step: (q, k, v operands, P format,
-    block mask or None, K_s or None)."""
+    block mask or None, K_s or None).  fuse_q: Q is handed over in 16 bits where the variant
+    allows (the attention kernel then quantizes it to the same codes)."""
     import torch
     D = q.shape[-1]
     # K_s is stored only where Thrift's bf16 tiles read it; otherwise K is quantized with the
@@ -302,7 +318,10 @@ def prepare(sage, variant: str, q, k, v, causal: bool, had: bool = False):
 
     mask = None
     if variant in ("int8", "thrift", "sink", "int8_fp8pv"):
-        qq = sage.quantize(q, sage.INT8, (128, D), hadamard=had)
+        if fuses_q(variant, had, fuse_q):
+            qq = sage.QT(sage.BF16 if q.dtype == torch.bfloat16 else sage.FP16, q, None, tuple(q.shape))
+        else:
+            qq = sage.quantize(q, sage.INT8, (128, D), hadamard=had)
         kq = quant_k(sage.INT8, (64, D))
         if variant == "int8_fp8pv":
             vq, pf = sage.quantize(v, sage.E4M3, (0, 1)), sage.E4M3
@@ -507,6 +526,9 @@ def main():
                          "(1: the 0.85-1.15 grid, 2: the bit offsets) instead of max-scaling")
     ap.add_argument("--graph", action="store_true",
                     help="decode only: capture the call into a HIP graph once and time its replays")
+    ap.add_argument("--fuse-q", action="store_true",
+                    help="int8, thrift, sink: hand Q to the attention in 16 bits and quantize it there "
+                         "(the attention kernel's time then includes that quantization)")
     ap.add_argument("--hadamard", action="store_true",
                     help="Hadamard incoherence processing of Q and K_s inside their quantizers")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -555,7 +577,7 @@ def main():
     ev = []
 
     def step(record: bool):
-        qq, kq, vq, pf, mask, ks = prepare(sage, variant, q, k, v, causal, args.hadamard)
+        qq, kq, vq, pf, mask, ks = prepare(sage, variant, q, k, v, causal, args.hadamard, args.fuse_q)
         if record:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -582,7 +604,8 @@ def main():
     peak = PEAK[VARIANT_PEAK[variant]]
     # half the counted ops are QK^T, half P.V: the ceiling of the pair of MFMA dtypes used
     mixed = 1.0 / (0.5 / peak + 0.5 / PEAK[PV_PEAK[variant]])
-    traffic = load_traffic(w.name, causal, variant)
+    # counters were taken with Q quantized in its own kernel: not for the fused form
+    traffic = None if fuses_q(variant, args.hadamard, args.fuse_q) else load_traffic(w.name, causal, variant)
     rec = {
         "metric": "quantized attention fwd TOPS (4*B*H*N^2*d/t) at d=128 N=4096 + % of MFMA peak",
         "value": round(ops / (ms_step * 1e-3) / 1e12, 2),
@@ -598,7 +621,8 @@ def main():
         "data": "synthetic (seeded PCG64; shapes and value recipe of the workload)",
         "config": {"workload": w.name, "B": B, "Hq": Hq, "Hkv": w.Hkv, "N": N, "D": D, "causal": causal,
                    "variant": variant, "input_dtype": str(w.dtype).replace("torch.", ""),
-                   "step": STEP_TEXT[variant]
+                   "step": (STEP_TEXT_FUSED_Q[variant] if fuses_q(variant, args.hadamard, args.fuse_q)
+                            else STEP_TEXT[variant])
                    + (" (Q, K_s Hadamard-transformed in their quantizers)" if args.hadamard else "")
                    + (f" (P's 16-key blocks scaled by ScaleSearch mode {args.p_search})" if args.p_search else "")},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",

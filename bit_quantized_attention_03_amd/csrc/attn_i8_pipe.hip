@@ -58,6 +58,9 @@ struct PipeParams {
   // Thrift: block mask [B, Hq, nQB, nKB] (1: the tile runs on bf16 Q and K_s) and those rows
   const uint8_t* mask;
   const uint16_t* qhi; const uint16_t* khi;
+  // 16-bit Q [B, Hq, N, D] (rows q16r) quantized here per 128-token block, or null (q / qs hold
+  // the codes and scales)
+  const uint16_t* q16; Rows16 q16r; int q16_f16;
   Rows16 qhr, khr;
 };
 
@@ -234,12 +237,35 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     for (int cc = 0; cc < NCC; ++cc) vro[cc] = v_off<D>(rv, 2 * (32 * cc + 16 * (g16 & 1) + 4 * (j & 3)));
   }
 
-  // ---- Q fragments (B operand of S^T = K Q^T): row qrow, channels 32kc + 16lh .. +16
+  // ---- Q fragments (B operand of S^T = K Q^T): row qrow, channels 32kc + 16lh .. +16.
+  //      From 16-bit Q, the kernel quantizes them itself, as the INT8 quantizer does for a block
+  //      of 128 tokens (SageAttention, Technical approach): s = amax / 127 over the block, the
+  //      rows of one wave group.  The loads fly with the first K copies; each wave's largest
+  //      magnitude then goes through LDS at the barrier below, and the codes are formed after it.
   v4i qf[NCC];
+  float qscale = 0.0f;
+  const bool q_fused = p.q16 != nullptr;
+  v4i q16raw[NCC][2];   // this lane's 16 NCC values of 16-bit Q
+  __shared__ float qamax[NWAVES];
+  auto q16_val = [&](int kc, int e) __attribute__((always_inline)) -> float {
+    const uint16_t h = (uint16_t)((uint32_t)q16raw[kc][e >> 3][(e >> 1) & 3] >> (16 * (e & 1)));
+    return p.q16_f16 ? in16_to_f32<true>(h) : in16_to_f32<false>(h);
+  };
+  // A row past N loads row N-1 instead (no branch, so no wait, around the loads): its scores,
+  // softmax and products stay in its own lane column and it is never stored.
+  const int64_t qrow_ld = row_ok ? qrow : p.N - 1;
+  if (q_fused) {   // loads in flight with the first K copies (the wait below covers both)
+    const uint16_t* src = p.q16 + p.q16r.at(bh, qrow_ld) + 16 * lh;
 #pragma unroll
-  for (int kc = 0; kc < NCC; ++kc)
-    qf[kc] = row_ok ? *(const v4i*)(p.q + (bh * p.N + qrow) * D + 32 * kc + 16 * lh) : v4i{0, 0, 0, 0};
-  const float qscale = tl >= 0 ? p.qs[__builtin_amdgcn_readfirstlane((int)(bh * p.nQB + qb))] : 0.0f;
+    for (int kc = 0; kc < NCC; ++kc) {
+      q16raw[kc][0] = *(const v4i*)(src + 32 * kc);
+      q16raw[kc][1] = *(const v4i*)(src + 32 * kc + 8);
+    }
+  } else {
+#pragma unroll
+    for (int kc = 0; kc < NCC; ++kc) qf[kc] = *(const v4i*)(p.q + (bh * p.N + qrow_ld) * D + 32 * kc + 16 * lh);
+    qscale = tl >= 0 ? p.qs[__builtin_amdgcn_readfirstlane((int)(bh * p.nQB + qb))] : 0.0f;
+  }
   const float* kscales = k_scales + bkv * p.nKB;   // read-only: scalar loads
 
   v16f o[NCC];
@@ -279,7 +305,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   if (nT > 0) dma.k_tile(0, lds0 + kbuf(0), w);
   if (nT > 1) dma.k_tile(1, lds0 + kbuf(1), w);
   wait_vm(0);
+  if (q_fused) {
+    __builtin_amdgcn_sched_barrier(0);
+    float am = 0.0f;
+#pragma unroll
+    for (int kc = 0; kc < NCC; ++kc)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(q16_val(kc, e)));
+    am = wave_max(row_ok ? am : 0.0f);   // the block's rows only
+    if (lane == 0) qamax[w] = am;
+  }
   __syncthreads();
+  if (q_fused) {
+    const int g0 = 4 * (w >> 2);
+    const float amax = __builtin_fmaxf(__builtin_fmaxf(qamax[g0], qamax[g0 + 1]), __builtin_fmaxf(qamax[g0 + 2], qamax[g0 + 3]));
+    const float s = amax / 127.0f;
+    const float r = int8_recip(s);
+#pragma unroll
+    for (int kc = 0; kc < NCC; ++kc) {
+      uint32_t cb[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) cb[e] = int8_code_bits(q16_val(kc, e), r);
+      qf[kc] = v4i{(int)pack_bytes(cb[0], cb[1], cb[2], cb[3]), (int)pack_bytes(cb[4], cb[5], cb[6], cb[7]),
+                   (int)pack_bytes(cb[8], cb[9], cb[10], cb[11]), (int)pack_bytes(cb[12], cb[13], cb[14], cb[15])};
+    }
+    qscale = tl >= 0 ? s : 0.0f;
+    qs_use = qscale;
+  }
 
   // ---- matrix work of one wave.  S^T(t) = K(t) Q^T from the K tile at LDS offset kbs
   //      (fragments read first, so their LDS latency runs under other work); O^T += V^T P^T for
@@ -676,6 +728,7 @@ hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st) {
   p.out = a.out;
   p.vr = a.vr; p.outr = a.outr;
   p.mask = a.mask; p.qhi = a.q_hi; p.khi = a.k_hi;
+  p.q16 = a.q16; p.q16r = a.q16r; p.q16_f16 = a.q16_f16;
   p.qhr = a.qhr; p.khr = a.khr;
   if (p.mask && (a.N + KT - 1) / KT > PIPE_MAX_MASK_TILES) return hipErrorInvalidValue;   // mask rows past LDS
   p.Hq = a.Hq; p.Hkv = a.Hkv; p.N = a.N;

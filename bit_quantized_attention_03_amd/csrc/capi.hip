@@ -229,7 +229,14 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
   // layouts: quantized operands contiguous; 16-bit V, the Thrift tiles' Q and K_s and the
   // output may be strided
   AttnArgs a;
-  if (!contiguous(qs) || !contiguous(ks)) return SAGE_EINVAL;
+  // 16-bit Q with INT8 K: the kernel quantizes Q itself (it may be strided)
+  const bool q16 = is16(q->fmt) && k->fmt == SAGE_INT8;
+  if (q16) {
+    if (!layout_of(qs, 8, &a.q16r)) return SAGE_EINVAL;
+  } else if (!contiguous(qs)) {
+    return SAGE_EINVAL;
+  }
+  if (!contiguous(ks)) return SAGE_EINVAL;
   if (is16(v->fmt)) {
     if (!layout_of(vs, 8, &a.vr) || a.vr.sn > V_MAX_ROW_STRIDE) return SAGE_EINVAL;
   } else {
@@ -266,9 +273,18 @@ int sage_attn_fwd(const sage_qtensor* q, const sage_qtensor* k, const sage_qtens
     return SAGE_EINVAL;
   if (p->p_scale_mode != SAGE_SCALE_ABSMAX && p->p_fmt != SAGE_NVFP4) return SAGE_EINVAL;
 
-  if (q->fmt == SAGE_INT8 && k->fmt == SAGE_INT8) {
-    if (!empty && (!q->scales || !k->scales)) return SAGE_EINVAL;
-    if (!block_is(q, QBLK, (int32_t)qs.D) || !block_is(k, KBLK, (int32_t)ks.D)) return SAGE_EINVAL;
+  if ((q->fmt == SAGE_INT8 || q16) && k->fmt == SAGE_INT8) {
+    if (!empty && ((!q16 && !q->scales) || !k->scales)) return SAGE_EINVAL;
+    if ((!q16 && !block_is(q, QBLK, (int32_t)qs.D)) || !block_is(k, KBLK, (int32_t)ks.D)) return SAGE_EINVAL;
+    if (q16) {
+      // the pipelined kernel's operand sets: bf16 P.V, fp16 V only at D = 64, a block mask of at
+      // most PIPE_MAX_MASK_TILES K tiles
+      if (!is16(v->fmt) || p->p_fmt != SAGE_BF16 || (v->fmt == SAGE_FP16 && qs.D == 128) ||
+          (p->block_mask && (qs.N + KBLK - 1) / KBLK > PIPE_MAX_MASK_TILES))
+        return SAGE_ENOTSUP;
+      a.q16 = (const uint16_t*)q->codes;
+      a.q16_f16 = q->fmt == SAGE_FP16;
+    }
     if (is16(v->fmt) && p->p_fmt == SAGE_BF16) {
       if (p->block_mask) {
         if (!empty && (!p->q_hi || !p->k_hi)) return SAGE_EINVAL;

@@ -124,6 +124,25 @@ __device__ __forceinline__ int mx_exp_e4m3(float a) {
 }
 __device__ __forceinline__ float exp2i(int e) { return __builtin_ldexpf(1.0f, e); }
 
+// ---- INT8 block codes (SageAttention, Technical approach: s = amax / 127, code =
+//      clamp(round_half_even(x * (1/s)), -127, 127)) ------------------------------------------
+// The reciprocal of a block scale s > 0, saturated at the largest finite fp32 (1 / s overflows
+// only for a block whose largest magnitude is below about 3.7e-37; an element 0 then keeps code 0).
+__device__ __forceinline__ float int8_recip(float s) {
+  return s > 0.0f ? __builtin_fminf(1.0f / s, 3.40282347e38f) : 0.0f;
+}
+// The INT8 code of fp32(x * r) in the low byte: the product clamped to [-127, 127], then rounded
+// to the nearest integer, ties to even, by one fp32 add of 1.5 * 2^23, after which the low bits
+// of the sum's mantissa hold that integer in two's complement (|value| < 2^22).  Clamping first
+// and rounding after gives the same integer as rounding first.
+__device__ __forceinline__ uint32_t int8_code_bits(float x, float r) {
+  const float v = __builtin_fminf(__builtin_fmaxf(x * r, -127.0f), 127.0f);
+  return __float_as_uint(v + 12582912.0f);
+}
+__device__ __forceinline__ uint32_t pack_bytes(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return (a & 0xffu) | ((b & 0xffu) << 8) | ((c & 0xffu) << 16) | (d << 24);
+}
+
 // ---- wave reductions (64 lanes; DPP / swizzle via shuffles) -----------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -71,6 +71,10 @@ struct AttnArgs {
   const void* k_codes; const void* k_scales;
   const void* v_codes; const void* v_scales;   // v_codes = 16-bit V for the bf16/fp16 P.V path
   int v_is_f16;
+  // 16-bit Q quantized to INT8 in the kernel (per 128-token block, as the quantizer does):
+  // then q_codes / q_scales are unused.  Pipelined kernel only.
+  const uint16_t* q16 = nullptr;
+  int q16_f16 = 0;
   // Thrift
   const uint8_t* mask; const uint16_t* q_hi; const uint16_t* k_hi;
   void* out;
@@ -78,7 +82,7 @@ struct AttnArgs {
   int p_scale_mode;   // NVFP4 P: 0 max-scaling, 1 / 2 ScaleSearch per 16-key block
   // rows of the 16-bit V (bf16 / fp16 P.V), of the Thrift tiles' Q and K_s, and of the output
   // (elements of the output dtype); quantized operands are contiguous
-  Rows16 vr, qhr, khr, outr;
+  Rows16 vr, qhr, khr, outr, q16r;
 };
 hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st);
 // INT8 QK^T, bf16 P.V: the software-pipelined kernel (attn_i8_pipe.hip).  With a Thrift block

@@ -313,7 +313,7 @@ class Pass:
     """Intermediate tensors of one forward pass (kept for parity checks)."""
     mean: torch.Tensor
     k_smoothed: Optional[torch.Tensor]   # None when K was quantized with smoothing on the fly
-    q: QT
+    q: QT                                # 16-bit Q itself when the attention kernel quantized it
     k: QT
     v: QT
     mask: Optional[torch.Tensor]
@@ -323,7 +323,7 @@ class Pass:
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, variant: str = "int8",
             sm_scale: float = 0.0, thrift_frac: float = 0.05, search_mode: int = SEARCH,
             out_dtype: torch.dtype = torch.float32, keep_smoothed: bool = False, hadamard: bool = False,
-            sink_first: int = 1, sink_last: int = 1, p_search: int = ABSMAX) -> Pass:
+            sink_first: int = 1, sink_last: int = 1, p_search: int = ABSMAX, fuse_q: bool = False) -> Pass:
     """K smoothing -> block quantization -> (Thrift selection) -> fused attention.  K_s is only
     materialized when Thrift needs it (or keep_smoothed); otherwise K is quantized with the
     smoothing applied on the fly (identical codes).  hadamard: Q and K_s are quantized after
@@ -331,7 +331,9 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
     tiles take the original rows).  variant "sink": INT8 tiles except each Q block's first
     sink_first and last sink_last valid K blocks, which run in bf16 (a static Thrift mask).
     p_search (variant "nvfp4_search"): the rule by which each 16-key block of P picks its
-    scale (ABSMAX, SEARCH or SEARCH_OFFSETS)."""
+    scale (ABSMAX, SEARCH or SEARCH_OFFSETS).  fuse_q (variants "int8", "thrift", "sink",
+    without hadamard): Q goes to the attention kernel in 16 bits and is quantized there, per
+    128-token block, to the same codes and scales as quantize() gives (one pass over Q fewer)."""
     B, Hq, N, D = q.shape
     need_ks = variant in ("thrift", "sink") or keep_smoothed
     mean, ks = smooth_k(k, want_smoothed=need_ks)
@@ -342,7 +344,10 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool, var
 
     mask = None
     if variant in ("int8", "int8_fp8pv", "thrift", "sink"):
-        qq = quantize(q, INT8, (128, D), hadamard=hadamard)
+        if fuse_q and variant != "int8_fp8pv" and not hadamard:
+            qq = QT(_TORCH_FMT[q.dtype], q, None, tuple(q.shape))
+        else:
+            qq = quantize(q, INT8, (128, D), hadamard=hadamard)
         kq = quant_k(INT8, (64, D))
         if variant == "int8_fp8pv":
             vq = quantize(v, E4M3, (0, 1))

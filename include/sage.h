@@ -207,6 +207,11 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
  * h / (Hq / Hkv)), with the blocks each operand must carry:
  *   q, k SAGE_INT8 (blocks (128, D) / (64, D)) + v SAGE_BF16 | SAGE_FP16 + p SAGE_BF16
  *        (+ optional block_mask with bf16 q_hi / k_hi)
+ *   the same with q SAGE_BF16 | SAGE_FP16 (codes = the 16-bit Q, scales NULL, block unused;
+ *        Q may be strided like v): the kernel quantizes Q itself, per block of 128 tokens, to
+ *        the codes and scales sage_quantize_blocks(SAGE_INT8, (128, D), SAGE_SCALE_ABSMAX)
+ *        would give, and the output is bit-identical to that two-step call.  Not with fp16 v
+ *        at D = 128, nor with a block_mask of more than 4096 K tiles (SAGE_ENOTSUP).
  *   q, k SAGE_INT8 (blocks (128, D) / (64, D)) + v SAGE_E4M3 (block (0, 1): per channel)
  *        + p SAGE_E4M3 (P scaled by 448)
  *   q, k SAGE_MXFP4 (block (1, 32): along D) + v SAGE_MXFP4 (block (32, 1): along tokens)
@@ -214,7 +219,7 @@ int sage_nvfp4_to_mxfp8(const void* codes, const void* scales, sage_shape xs, in
  *   q, k SAGE_MXFP8 (block (1, 32)) + v SAGE_MXFP8 (block (32, 1)) + p SAGE_NVFP4 (max-scaled
  *        per 16 keys, then to MXFP8 like sage_nvfp4_to_mxfp8)
  * Tile offsets inside the kernels are 32-bit: N <= 2^24 (else SAGE_EINVAL).
- * Layouts: q and k (codes) contiguous; a 16-bit v, q_hi and k_hi may be strided (v's row
+ * Layouts: q and k (codes) contiguous; a 16-bit q, v, q_hi and k_hi may be strided (v's row
  * stride sn <= 2^24 elements); out is [B,Hq,N,D] in out_dt (SAGE_FP32 | SAGE_BF16) with the
  * layout os (all zero: contiguous; else os's dims must be q's).  D in {64, 128} for the INT8 sets;
  * the microscaled sets take D = 128 (else SAGE_ENOTSUP) and 4-byte aligned scale arrays

@@ -289,6 +289,40 @@ def test_decode_noalloc_validation(L):
                                      None, sage.FP32, None) == 0
 
 
+def test_sixteen_bit_q_operand_set(L):
+    """16-bit Q with INT8 K (quantized inside the pipelined kernel): only with a 16-bit V and
+    bf16 P, not fp16 V at D = 128, not past the kernel's mask-row limit; its strides and
+    alignment are checked like V's."""
+    from bit_quantized_attention_03_amd import sage
+    a = 0x1000_0000
+    shp = sage.Shape(1, 2, 256, 128)
+    q16 = sage.QTensorC(sage.BF16, a, None, shp)
+    ki = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(64, 128))
+    vb = sage.QTensorC(sage.BF16, a, None, shp)
+    vh = sage.QTensorC(sage.FP16, a, None, shp)
+    v8 = sage.QTensorC(sage.E4M3, a, a, shp, sage.Block(0, 1))
+    p = sage.AttnParamsC(0, 0.0, sage.BF16, None, None, None, sage.BF16)
+    p8 = sage.AttnParamsC(0, 0.0, sage.E4M3, None, None, None, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(q16), C.byref(ki), C.byref(v8), C.byref(p8), a, sage.FP32, sage.Shape(), None) == -2
+    assert L.sage_attn_fwd(C.byref(q16), C.byref(ki), C.byref(vh), C.byref(p), a, sage.FP32, sage.Shape(), None) == -2
+    # a block mask beyond 4096 K tiles
+    N = 4096 * 64 + 1
+    big = sage.Shape(1, 1, N, 128)
+    qb = sage.QTensorC(sage.BF16, a, None, big)
+    kb = sage.QTensorC(sage.INT8, a, a, big, sage.Block(64, 128))
+    vbig = sage.QTensorC(sage.BF16, a, None, big)
+    pm = sage.AttnParamsC(1, 0.0, sage.BF16, a, a, a, sage.BF16)
+    assert L.sage_attn_fwd(C.byref(qb), C.byref(kb), C.byref(vbig), C.byref(pm), a, sage.FP32, sage.Shape(), None) == -2
+    # layout and alignment of the 16-bit Q
+    q_bad = sage.QTensorC(sage.BF16, a, None, sage.Shape(1, 2, 256, 128, 2 * 256 * 128, 128, 2 * 128 + 4))
+    assert L.sage_attn_fwd(C.byref(q_bad), C.byref(ki), C.byref(vb), C.byref(p), a, sage.FP32, sage.Shape(), None) == -1
+    q_mis = sage.QTensorC(sage.BF16, a + 8, None, shp)
+    assert L.sage_attn_fwd(C.byref(q_mis), C.byref(ki), C.byref(vb), C.byref(p), a, sage.FP32, sage.Shape(), None) == -3
+    # K must still carry its INT8 block
+    k_bad = sage.QTensorC(sage.INT8, a, a, shp, sage.Block(128, 128))
+    assert L.sage_attn_fwd(C.byref(q16), C.byref(k_bad), C.byref(vb), C.byref(p), a, sage.FP32, sage.Shape(), None) == -1
+
+
 def test_strided_layouts_are_validated(L):
     """sage_shape strides: checked before any launch (16-byte rows, no overlapping rows), and
     refused where the operand must be contiguous."""

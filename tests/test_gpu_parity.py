@@ -403,6 +403,41 @@ def test_attention_parity(name, ov, causal, variant):
     print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f} cos_vs_fp64={cosine(res.out.cpu().numpy(), ref):.6f}")
 
 
+FUSED_Q_CASES = [
+    ("llm_int8", dict(B=1, Hq=2, Hkv=2, N=333), False, "int8", "bf16"),
+    ("llm_int8", dict(B=2, Hq=2, Hkv=2, N=1024), True, "int8", "bf16"),
+    ("thrift_long", dict(B=1, Hq=4, Hkv=2, N=700), True, "int8", "bf16"),        # GQA
+    ("thrift_long", dict(B=1, Hq=4, Hkv=2, N=1100), True, "thrift", "bf16"),
+    ("thrift_long", dict(B=1, Hq=2, Hkv=2, N=450, D=64), False, "sink", "bf16"),  # d = 64
+    ("llm_int8", dict(B=1, Hq=2, Hkv=2, N=200, D=64), True, "int8", "fp16"),      # fp16 Q and V
+    ("llm_int8", dict(B=2, Hq=4, Hkv=4, N=300), False, "int8", "strided"),        # Q as a [B,N,H,D] view
+]
+
+
+@pytest.mark.parametrize("name,ov,causal,variant,form", FUSED_Q_CASES)
+def test_attention_fused_q_bit_identical(name, ov, causal, variant, form):
+    """16-bit Q quantized inside the attention kernel: the output equals, bit for bit, that of
+    the quantizer followed by the attention on the same operands, and meets the oracle bar."""
+    sage = _sage()
+    w = I.workload(name, **ov)
+    q, k, v = I.make_qkv(w, seed=2)
+    if form == "fp16":
+        q, k, v = (t.to(torch.float16) for t in (q, k, v))
+    qc, kc, vc = _cuda(q, k, v)
+    if form == "strided":
+        qc = qc.transpose(1, 2).contiguous().transpose(1, 2)   # same values, [B, N, H, D] memory
+        assert not qc.is_contiguous()
+    print(f"[case] fused Q {name} {ov} causal={causal} variant={variant} {form}", flush=True)
+    two = sage.forward(qc, kc, vc, causal=causal, variant=variant)
+    one = sage.forward(qc, kc, vc, causal=causal, variant=variant, fuse_q=True)
+    torch.cuda.synchronize()
+    assert one.q.fmt == (sage.FP16 if form == "fp16" else sage.BF16) and one.q.scales is None
+    assert torch.equal(one.out, two.out)
+    orc = oracle_pass(q, k, v, causal, variant)
+    rel, cos = check_out(one.out.cpu().numpy(), orc["out"], f"fused Q {name} {variant} causal={causal} {form}")
+    print(f"  rel_err_vs_oracle={rel:.2e} cos_vs_oracle={cos:.6f}")
+
+
 @pytest.mark.parametrize("frac", [0.0, 1.0])
 @pytest.mark.parametrize("causal", [True, False])
 def test_thrift_no_tile_or_every_tile(frac, causal):
