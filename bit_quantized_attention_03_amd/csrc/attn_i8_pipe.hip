@@ -118,38 +118,51 @@ __device__ __forceinline__ void wait_vm(int n) {
 __device__ __forceinline__ void lds_dma16(int voff, v4i rsrc, uint32_t lds_off) {
   __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_off) : "memory");
 }
-// Descriptor of a raw byte buffer (stride 0) of n bytes at base; the last word is the gfx9
-// family's data format for untyped buffer access.
-__device__ __forceinline__ v4i buffer_desc(const void* base, int n) {
-  const uint64_t a = (uint64_t)base;
+// Descriptor of a raw byte buffer (stride 0) of n bytes at base (both wave-uniform, in scalar
+// registers); the last word is the gfx9 family's data format for untyped buffer access.
+__device__ __forceinline__ v4i buffer_desc(uint64_t base, int n) {
   v4i r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
-  r[2] = __builtin_amdgcn_readfirstlane(n);
+  r[0] = (int)(uint32_t)base;
+  r[1] = (int)(uint32_t)(base >> 32);   // base < 2^48 (masked once), so the stride field is 0
+  r[2] = n;
   r[3] = 0x00020000;
   return r;
 }
 
 // Tile copies shared by the 8 waves.  Instruction i of a tile (one kilobyte) is issued by wave
 // i % 8.  Lane l of instruction i fills LDS chunk position 64 i + l, whose source chunk (the
-// swizzle undone) sits at a per-lane constant offset from the tile's first row.
+// swizzle undone) sits at a per-lane constant offset from the tile's first row.  K and V tiles
+// are copied in ascending order, each stream from a scalar address advanced by one tile per
+// copy and a count of the keys left below N (and below the workgroup's last tile) from that
+// tile on.  A copy takes the rows of its tile that lie below that bound: none past the
+// workgroup's last tile (its buffer load then reads only zeros and touches no memory; such a
+// buffer is never read).
 template <int D>
 struct PipeDma {
   static constexpr int K_INSTR = KT * D / 16 / 64;        // D/16: 8 (D = 128) or 4
   static constexpr int V_INSTR = KT * 2 * D / 16 / 64;    // D/8: 16 or 8
   static constexpr int K_PER = (K_INSTR + 7) / 8, V_PER = V_INSTR / 8;
-  const int8_t* kbase;       // K and V of this (b, kv-head)
-  const uint16_t* vbase;
-  int vsn;                   // V row stride (elements)
-  int N;
+  uint64_t kaddr, vaddr;     // first byte of the next K tile and of the next V tile to copy
+  int krem, vrem;            // keys from those tiles' first rows to N (<= 0: past the end)
+  int vrow2;                 // bytes between V rows
   int koff[K_PER], voff[V_PER];
-  // rows of the tile at key0 that lie below N (1 .. KT): the record count stays far below 2^32
-  __device__ __forceinline__ int rows_left(int key0) const { return N - key0 < KT ? N - key0 : KT; }
-  __device__ __forceinline__ void init(const PipeParams& p, int64_t bkv, int w, int lane) {
-    kbase = p.k + bkv * p.N * D;
-    vbase = p.v + p.vr.head(bkv);
-    vsn = (int)p.vr.sn;
-    N = (int)p.N;
+  // wave-uniform copy state, kept in scalar registers (the scalar unit does its arithmetic)
+  template <typename T>
+  __device__ __forceinline__ static void sgpr(T& x) { __asm__ volatile("" : "+s"(x)); }
+  // min(max(rem, 0), KT) on the scalar unit (the pin keeps the pair from being fused into a
+  // vector med3)
+  __device__ __forceinline__ static int rows_of(int rem) {
+    int r = rem < KT ? rem : KT;
+    sgpr(r);
+    return r > 0 ? r : 0;
+  }
+  // nT: the workgroup's tile count; rows from tile nT on are not copied
+  __device__ __forceinline__ void init(const PipeParams& p, int64_t bkv, int nT, int w, int lane) {
+    // 48-bit addresses; a copy's advance stays inside its buffer, so bit 48 is never reached
+    kaddr = (uint64_t)(p.k + bkv * p.N * D) & 0xffffffffffffull;
+    vaddr = (uint64_t)(p.v + p.vr.head(bkv)) & 0xffffffffffffull;
+    krem = vrem = (int)(p.N < (int64_t)nT * KT ? p.N : (int64_t)nT * KT);
+    vrow2 = 2 * (int)p.vr.sn;
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
       const int i = w + 8 * j;
@@ -161,24 +174,34 @@ struct PipeDma {
     for (int j = 0; j < V_PER; ++j) {
       const int pos = 64 * (w + 8 * j) + lane, row = pos / (2 * D / 16);
       const int c = (pos % (2 * D / 16)) ^ v_swz<D>(row);
-      voff[j] = row * 2 * vsn + 16 * c;   // < 2^31: the row stride is checked at the boundary
+      voff[j] = row * vrow2 + 16 * c;   // < 2^31: the row stride is checked at the boundary
     }
   }
-  __device__ __forceinline__ void k_tile(int t, uint32_t kb, int w) const {
-    const int key0 = t * KT;   // t < nT, so at least one row remains
-    const v4i rsrc = buffer_desc(kbase + (int64_t)key0 * D, rows_left(key0) * D);
+  // the next K tile into the LDS buffer at kb
+  __device__ __forceinline__ void k_next(uint32_t kb, int w) {
+
+
+    const v4i rsrc = buffer_desc(kaddr, rows_of(krem) * D);
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
       if (K_INSTR % 8 != 0 && w + 8 * j >= K_INSTR) break;   // every wave copies when D = 128
       lds_dma16(koff[j], rsrc, kb + (w + 8 * j) * 1024);
     }
+    kaddr += KT * D;
+    krem -= KT;
   }
-  __device__ __forceinline__ void v_tile(int t, uint32_t vb, int w) const {
-    const int key0 = t * KT;
-    // the record count ends right after the last row below N: rows past it read zeros
-    const v4i rsrc = buffer_desc(vbase + (int64_t)key0 * vsn, ((rows_left(key0) - 1) * vsn + D) * 2);
+  // the next V tile into the LDS buffer at vb.  The record count covers whole row strides of
+  // the rows below N: a lane reads 16 bytes of the first 2D of its row, so the lanes of rows
+  // below N read only their rows, and those of later rows read zeros.
+  __device__ __forceinline__ void v_next(uint32_t vb, int w) {
+
+
+    // at most 64 rows of 2^25 bytes (the row stride is capped at the boundary): 32 bits unsigned
+    const v4i rsrc = buffer_desc(vaddr, (int)((uint32_t)rows_of(vrem) * (uint32_t)vrow2));
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) lds_dma16(voff[j], rsrc, vb + (w + 8 * j) * 1024);
+    vaddr += (uint64_t)KT * (uint32_t)vrow2;
+    vrem -= KT;
   }
 };
 
@@ -301,9 +324,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   };
 
   PipeDma<D> dma;
-  dma.init(p, bkv, w, lane);
-  if (nT > 0) dma.k_tile(0, lds0 + kbuf(0), w);
-  if (nT > 1) dma.k_tile(1, lds0 + kbuf(1), w);
+  dma.init(p, bkv, nT, w, lane);
+  dma.k_next(lds0 + kbuf(0), w);   // K(0), K(1)
+  dma.k_next(lds0 + kbuf(1), w);
   wait_vm(0);
   if (q_fused) {
     __builtin_amdgcn_sched_barrier(0);
@@ -494,9 +517,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
       s_mfma(kf0);
     }
   }
-  // the copies of "phase -2" (K(2), V(0); a tile past the last re-copies the last)
-  dma.k_tile(nT > 2 ? 2 : nT - 1, lds0 + kbuf(2), w);
-  dma.v_tile(0, lds0 + vbuf(0), w);
+  // the copies of "phase -2" (K(2), V(0); a tile past the last reads nothing)
+  dma.k_next(lds0 + kbuf(2), w);
+  dma.v_next(lds0 + vbuf(0), w);
 
   // ---- The schedule.  Each wave's iteration t is two halves:
   //        H1: P.V(t-1), 16 products (k-groups 0-3)  under part A of the softmax of tile t and
@@ -521,13 +544,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   v4i kf[NCC][2];      // K fragments of S(t+1) between the halves
   v8bf vf[2][NCC];
   // Phase 2t's copies (this wave's share), always issued: the target buffers are free in that
-  // phase whatever t is, and a tile index past the last re-copies the last tile, so the copy
-  // code and the wait counts are the same in every phase (no branches).
+  // phase whatever t is, and a tile past the last copies no rows (zeros that are never read),
+  // so the copy code and the wait counts are the same in every phase (no branches).
   constexpr int NLOAD_MAX = PipeDma<D>::K_PER + PipeDma<D>::V_PER;
   auto copies = [&](int t, int j) __attribute__((always_inline)) {
     const int j1 = j == 2 ? 0 : j + 1;
-    dma.k_tile(t + 3 < nT ? t + 3 : nT - 1, lds0 + kbuf(j), w);
-    dma.v_tile(t + 1 < nT ? t + 1 : nT - 1, lds0 + vbuf(j1), w);
+    dma.k_next(lds0 + kbuf(j), w);    // K(t+3)
+    dma.v_next(lds0 + vbuf(j1), w);   // V(t+1)
   };
   // wait until at most one phase's copies of this wave are in flight
   auto wait_copies = [&]() __attribute__((always_inline)) {
