@@ -633,9 +633,10 @@ hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st) {
   }
   const bool thrift = a.mask != nullptr;
   const bool causal = a.causal != 0;
-  // plain INT8 Q.K with bf16 P.V: the software-pipelined kernel (fp16 V at D = 128 stays here)
-  if (!pv_fp8 && !(a.v_is_f16 && a.D == 128) && (!thrift || (a.N + KT - 1) / KT <= PIPE_MAX_MASK_TILES))
-    return launch_attn_int8_pipe(a, st);
+  // the software-pipelined kernel: INT8 Q.K with bf16 P.V (fp16 V at D = 128 stays here), and
+  // with FP8 P.V on INT8 tiles (Thrift masks with FP8 P.V stay here)
+  if (pv_fp8 ? !thrift : (!(a.v_is_f16 && a.D == 128) && (!thrift || (a.N + KT - 1) / KT <= PIPE_MAX_MASK_TILES)))
+    return launch_attn_int8_pipe(a, pv_fp8, st);
   if (a.q16) return hipErrorNotSupported;   // 16-bit Q is quantized by the pipelined kernel only
   if (a.D == 64) {
     if (causal) return pv_fp8 ? dispatch_rest<64, true, true>(p, thrift, a.v_is_f16, a.out_bf16, st)

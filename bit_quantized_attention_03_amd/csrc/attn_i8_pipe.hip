@@ -54,6 +54,10 @@ struct PipeParams {
   void* out;
   int64_t Hq, Hkv, N, nQB, nKB, nPairs, total_wg;
   float sm_log2;   // sm_scale * log2(e), rounded to fp32
+  float sm_log2_lo;   // sm_scale * log2(e) - sm_log2 (FP8 P carries the product to ~2^-40)
+  // FP8 P.V: V^T codes [B, Hkv, D, Np] (E4M3, channel-major, tokens padded to Np) and the
+  // per-channel V scales [B, Hkv, D] (then v is unused)
+  const uint8_t* v8; const float* vs; int64_t Np;
   Rows16 vr, outr; // rows of V (per KV head) and of the output
   // Thrift: block mask [B, Hq, nQB, nKB] (1: the tile runs on bf16 Q and K_s) and those rows
   const uint8_t* mask;
@@ -85,6 +89,15 @@ template <int D>
 __device__ __forceinline__ int v_off(int row, int byte) {   // byte offset within the row (< 2D)
   return row * 2 * D + 16 * ((byte >> 4) ^ v_swz<D>(row)) + (byte & 15);
 }
+// FP8 V^T tile ([D][64] bytes): chunk c (of 4) of channel row r at c ^ v8_swz(r), so the 16
+// rows one operand read pass touches (4 consecutive rows x 4 row groups) cover all chunk slots.
+__device__ __forceinline__ int v8_swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int v8_off(int row, int c) { return row * KT + 16 * (c ^ v8_swz(row)); }
+// E4M3 P codes are formed from S - S_max read off integer sums that start at the bit pattern of
+// 1.5 * 2^23: as floats they are 1.5 * 2^23 + S exactly (|S| < 2^22), and the difference of two
+// is exact.
+constexpr float kMagic = 12582912.0f;
+constexpr int kMagicBits = 0x4B400000;
 // Scheduling hints for the machine scheduler (instruction classes of sched_group_barrier):
 // a region's instructions are placed in the order of the groups requested.
 constexpr int SG_MFMA = 0x008, SG_VALU = 0x002, SG_DS_READ = 0x100;
@@ -137,11 +150,15 @@ __device__ __forceinline__ v4i buffer_desc(uint64_t base, int n) {
 // tile on.  A copy takes the rows of its tile that lie below that bound: none past the
 // workgroup's last tile (its buffer load then reads only zeros and touches no memory; such a
 // buffer is never read).
-template <int D>
+template <int D, bool PV8>
 struct PipeDma {
-  static constexpr int K_INSTR = KT * D / 16 / 64;        // D/16: 8 (D = 128) or 4
-  static constexpr int V_INSTR = KT * 2 * D / 16 / 64;    // D/8: 16 or 8
-  static constexpr int K_PER = (K_INSTR + 7) / 8, V_PER = V_INSTR / 8;
+  static constexpr int K_INSTR = KT * D / 16 / 64;                  // D/16: 8 (D = 128) or 4
+  static constexpr int V_INSTR = (PV8 ? D : 2 * D) * KT / 16 / 64;  // bf16: D/8; FP8 V^T: D/16
+  static constexpr int K_PER = (K_INSTR + 7) / 8, V_PER = (V_INSTR + 7) / 8;
+  // copy instructions of wave w per phase (the vmcnt of one phase's copies)
+  __device__ __forceinline__ static int loads_of(int w) {
+    return (K_INSTR % 8 == 0 ? K_PER : (w < K_INSTR ? 1 : 0)) + (V_INSTR % 8 == 0 ? V_PER : (w < V_INSTR ? 1 : 0));
+  }
   uint64_t kaddr, vaddr;     // first byte of the next K tile and of the next V tile to copy
   int krem, vrem;            // keys from those tiles' first rows to N (<= 0: past the end)
   int vrow2;                 // bytes between V rows
@@ -160,9 +177,9 @@ struct PipeDma {
   __device__ __forceinline__ void init(const PipeParams& p, int64_t bkv, int nT, int w, int lane) {
     // 48-bit addresses; a copy's advance stays inside its buffer, so bit 48 is never reached
     kaddr = (uint64_t)(p.k + bkv * p.N * D) & 0xffffffffffffull;
-    vaddr = (uint64_t)(p.v + p.vr.head(bkv)) & 0xffffffffffffull;
+    vaddr = (PV8 ? (uint64_t)(p.v8 + bkv * D * p.Np) : (uint64_t)(p.v + p.vr.head(bkv))) & 0xffffffffffffull;
     krem = vrem = (int)(p.N < (int64_t)nT * KT ? p.N : (int64_t)nT * KT);
-    vrow2 = 2 * (int)p.vr.sn;
+    vrow2 = PV8 ? (int)p.Np : 2 * (int)p.vr.sn;
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
       const int i = w + 8 * j;
@@ -172,15 +189,19 @@ struct PipeDma {
     }
 #pragma unroll
     for (int j = 0; j < V_PER; ++j) {
-      const int pos = 64 * (w + 8 * j) + lane, row = pos / (2 * D / 16);
-      const int c = (pos % (2 * D / 16)) ^ v_swz<D>(row);
-      voff[j] = row * vrow2 + 16 * c;   // < 2^31: the row stride is checked at the boundary
+      if (PV8) {   // V^T: channel row of 4 chunks of 16 tokens (N <= 2^24, so row * Np < 2^31)
+        const int i = w + 8 * j;
+        const int pos = 64 * (i < V_INSTR ? i : 0) + lane, row = pos / 4;
+        voff[j] = row * vrow2 + 16 * ((pos % 4) ^ v8_swz(row));
+      } else {
+        const int pos = 64 * (w + 8 * j) + lane, row = pos / (2 * D / 16);
+        const int c = (pos % (2 * D / 16)) ^ v_swz<D>(row);
+        voff[j] = row * vrow2 + 16 * c;   // < 2^31: the row stride is checked at the boundary
+      }
     }
   }
   // the next K tile into the LDS buffer at kb
   __device__ __forceinline__ void k_next(uint32_t kb, int w) {
-
-
     const v4i rsrc = buffer_desc(kaddr, rows_of(krem) * D);
 #pragma unroll
     for (int j = 0; j < K_PER; ++j) {
@@ -194,21 +215,31 @@ struct PipeDma {
   // the rows below N: a lane reads 16 bytes of the first 2D of its row, so the lanes of rows
   // below N read only their rows, and those of later rows read zeros.
   __device__ __forceinline__ void v_next(uint32_t vb, int w) {
-
-
-    // at most 64 rows of 2^25 bytes (the row stride is capped at the boundary): 32 bits unsigned
-    const v4i rsrc = buffer_desc(vaddr, (int)((uint32_t)rows_of(vrem) * (uint32_t)vrow2));
+    if constexpr (PV8) {
+      // the tile's 64 token columns of every channel row (the rows are padded to Np tokens)
+      const v4i rsrc = buffer_desc(vaddr, rows_of(vrem) > 0 ? (D - 1) * vrow2 + KT : 0);
 #pragma unroll
-    for (int j = 0; j < V_PER; ++j) lds_dma16(voff[j], rsrc, vb + (w + 8 * j) * 1024);
-    vaddr += (uint64_t)KT * (uint32_t)vrow2;
+      for (int j = 0; j < V_PER; ++j) {
+        if (V_INSTR % 8 != 0 && w + 8 * j >= V_INSTR) break;
+        lds_dma16(voff[j], rsrc, vb + (w + 8 * j) * 1024);
+      }
+      vaddr += KT;
+    } else {
+      // at most 64 rows of 2^25 bytes (the row stride is capped at the boundary): 32 bits unsigned
+      const v4i rsrc = buffer_desc(vaddr, (int)((uint32_t)rows_of(vrem) * (uint32_t)vrow2));
+#pragma unroll
+      for (int j = 0; j < V_PER; ++j) lds_dma16(voff[j], rsrc, vb + (w + 8 * j) * 1024);
+      vaddr += (uint64_t)KT * (uint32_t)vrow2;
+    }
     vrem -= KT;
   }
 };
 
-template <int D, bool CAUSAL, bool VF16, bool OUT_BF16, bool THRIFT>
+template <int D, bool CAUSAL, bool VF16, bool OUT_BF16, bool THRIFT, bool PV8>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p, const float* __restrict__ k_scales) {
   constexpr int NCC = D / 32;   // 32-channel chunks of O and 32-channel k-slices of S
-  constexpr int K_BYTES = KT * D, V_BYTES = KT * 2 * D;
+  constexpr int K_BYTES = KT * D, V_BYTES = PV8 ? D * KT : KT * 2 * D;
+  static_assert(!PV8 || (!THRIFT && !VF16), "FP8 P.V: INT8 tiles and FP8 V only");
   // three K tiles then three V tiles
   __shared__ __attribute__((aligned(16))) uint8_t smem[3 * K_BYTES + 3 * V_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) uint8_t*)smem);
@@ -257,7 +288,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     const int g16 = lane >> 4, j = lane & 15;
     const int rv = 32 * (g16 >> 1) + (j >> 2);
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) vro[cc] = v_off<D>(rv, 2 * (32 * cc + 16 * (g16 & 1) + 4 * (j & 3)));
+    for (int cc = 0; cc < NCC; ++cc) vro[cc] = PV8 ? 32 * cc + li : v_off<D>(rv, 2 * (32 * cc + 16 * (g16 & 1) + 4 * (j & 3)));
   }
 
   // ---- Q fragments (B operand of S^T = K Q^T): row qrow, channels 32kc + 16lh .. +16.
@@ -300,6 +331,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   // dequantization factor (s_q s_k sm_scale log2 e) of the tile being softmaxed, from the K
   // block scale loaded at the end of the previous iteration
   float dq = 0.0f;
+  float dq_lo = 0.0f;   // FP8 P: dq + dq_lo = s_q s_k sm_scale log2(e) to ~2^-40
+  float m_lo = 0.0f;    // FP8 P: the running max is the pair m_run + m_lo
+  // FP8 P: the integer S sums start at kMagicBits (held in registers, opaque to the compiler)
+  v16i magic;
+  if constexpr (PV8) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      int m;
+      __asm__ volatile("v_mov_b32 %0, %1" : "=v"(m) : "s"(kMagicBits));
+      magic[r] = m;
+    }
+  }
   float ksc_next = nT > 0 ? kscales[0] : 0.0f;
   // Thrift: whether the tile whose S is being computed runs on bf16, its scores then in units
   // of 2^-k (wave-uniform); the dequantization factor of the next softmax is qs_use * ksc_next *
@@ -323,7 +366,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     else return tt <= tl && __builtin_amdgcn_readfirstlane((int)mlds[(w >> 2) * (int)p.nKB + tt]) != 0;
   };
 
-  PipeDma<D> dma;
+  PipeDma<D, PV8> dma;
   dma.init(p, bkv, nT, w, lane);
   dma.k_next(lds0 + kbuf(0), w);   // K(0), K(1)
   dma.k_next(lds0 + kbuf(1), w);
@@ -367,7 +410,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   };
   auto s_mfma = [&](const v4i (&kf)[NCC][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) sacc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0][bb], qf[0], v16i{}, 0, 0, 0);
+    for (int bb = 0; bb < 2; ++bb) sacc[bb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[0][bb], qf[0], PV8 ? magic : v16i{}, 0, 0, 0);
 #pragma unroll
     for (int kc = 1; kc < NCC; ++kc)
 #pragma unroll
@@ -442,7 +485,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   //      per k-group kg (under the P.V(t-1) products of the same k-group, whose P registers it
   //      then overwrites): P = exp2(s dq - m) for the group's 8 keys of this lane, their sum,
   //      bf16 pairs.  k-group kg is keys s[kg/2][8(kg%2) .. 8(kg%2)+7] of the lane.
-  struct Soft { float s[2][16]; float dq, alpha, lsum; };
+  struct Soft { float s[2][16]; float dq, alpha, lsum, c0; };
   auto soft_a = [&](Soft& sm, int64_t key0, bool edge) __attribute__((always_inline)) {
     sm.dq = dq;
 #pragma unroll
@@ -489,6 +532,104 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
       sm.lsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2_ones(), __builtin_bit_cast(bf16x2_t, pk[4 * kg + e]), sm.lsum, false);
     pin(sm.lsum);
   };
+  // ---- FP8 P (video-generation form: P rounded to E4M3 after scaling by 448, V in E4M3 with
+  //      per-channel scales).  E4M3 codes round 448 P, so P is formed to about one fp32 ulp: the
+  //      exponent is (S - S_max) dq + c0, with the integer tile max taken out exactly (both read
+  //      off the magic-started sums), c0 = tile max - running max + log2(1.75), and both maxima
+  //      carried as exact two-float sums; the remaining 2^8 of 448 = 1.75 * 2^8 is applied by
+  //      the conversion's scale operand.  Part A (under P.V(t-1)): masks, integer row max, new
+  //      running max, rescale factor, S - S_max, then part B of the first key block.  Part B
+  //      of a block of 16 keys: exp2, the row sum of 1.75 P, E4M3 codes; the second block's
+  //      runs under S(t+1).
+  constexpr int SENT = 0;   // below every kMagic + S: a masked key
+  auto soft_a8 = [&](Soft& sm, int64_t key0, bool edge) __attribute__((always_inline)) {
+    sm.dq = dq;
+    if (edge) {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t kg = key0 + 32 * lh + 16 * bb + r;
+          if (kg >= p.N || (CAUSAL && kg > qrow)) sacc[bb][r] = SENT;
+        }
+    }
+    // integer row max as a tree of 3-input maxima (short dependency chains)
+    auto imax = [](int x, int y) __attribute__((always_inline)) { return x > y ? x : y; };
+    int mq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const v16i& x = sacc[q >> 1];
+      const int o8 = 8 * (q & 1);
+      mq[q] = imax(imax(imax(x[o8], x[o8 + 1]), x[o8 + 2]), imax(imax(x[o8 + 3], x[o8 + 4]), x[o8 + 5]));
+      mq[q] = imax(mq[q], imax(x[o8 + 6], x[o8 + 7]));
+    }
+    int im = imax(imax(imax(mq[0], mq[1]), mq[2]), mq[3]);
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap((uint32_t)im, (uint32_t)im, false, false);
+      const int i0 = (int)sw[0], i1 = (int)sw[1];
+      im = i0 > i1 ? i0 : i1;
+    }
+    const float fi = __int_as_float(im) - kMagic;   // exact
+    float th = -__builtin_inff(), tlo = 0.0f;        // tile row max (log2 units) = th + tlo
+    if (im > SENT) {
+      th = fi * dq;
+      tlo = __builtin_fmaf(fi, dq, -th) + fi * dq_lo;
+    }
+    const float gt = (th - m_run) + (tlo - m_lo);
+    const bool up = gt > 0.0f;
+    sm.alpha = up ? __builtin_amdgcn_exp2f((m_run - th) + (m_lo - tlo)) : 1.0f;   // 0 on the first tile
+    if (up) { m_run = th; m_lo = tlo; }
+    sm.c0 = ((th - m_run) + (tlo - m_lo)) + 0.807354922057604f;   // + log2(1.75)
+    const float fm = __int_as_float(im);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sm.s[bb][r] = __int_as_float(sacc[bb][r]) - fm;   // S - S_max, exact
+  };
+  // part B for key block bb (keys 32 lh + 16 bb .. +15 of the lane): exp2, masked keys
+  // cleared, their sum, and E4M3 codes into pk[4 bb .. 4 bb + 3]
+  auto soft_b8 = [&](Soft& sm, int64_t key0, bool edge, int bb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.s[bb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sm.s[bb][r], sm.dq, sm.c0));   // 1.75 P
+    if (edge) {   // a zero scale leaves masked keys at exp2(c0): clear them
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t kg = key0 + 32 * lh + 16 * bb + r;
+        if (kg >= p.N || (CAUSAL && kg > qrow)) sm.s[bb][r] = 0.0f;
+      }
+    }
+    float ps[8];   // the block's sum as a pairwise tree (short dependency chains)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) ps[r] = sm.s[bb][r] + sm.s[bb][r + 8];
+#pragma unroll
+    for (int w2 = 1; w2 < 8; w2 *= 2)
+#pragma unroll
+      for (int r = 0; r < 8; r += 2 * w2) ps[r] = ps[r] + ps[r + w2];
+    sm.lsum = bb == 0 ? ps[0] : sm.lsum + ps[0];
+#pragma unroll
+    for (int q4 = 4 * bb; q4 < 4 * bb + 4; ++q4) {   // E4M3(1.75 P * 2^8): the scale operand divides by 2^-8
+      const int r = 4 * (q4 & 3);
+      const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2s{0, 0}, sm.s[bb][r], sm.s[bb][r + 1], 0x1p-8f, false);
+      const v2s w2 = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, sm.s[bb][r + 2], sm.s[bb][r + 3], 0x1p-8f, true);
+      pk[q4] = __builtin_bit_cast(uint32_t, w2);
+    }
+  };
+  // O^T += V^T P^T for the whole tile on the scaled FP8 product (unit scales): operand bytes
+  // 16e .. 16e+15 of lane (li, lh) are V^T row 32 cc + li, tokens 32 lh + 16 e ..
+  auto v8_frags = [&](uint32_t vbs, v8i (&vf)[NCC]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const v4i v0 = *(const v4i*)(smem + vbs + v8_off(vro[cc], 2 * lh));
+      const v4i v1 = *(const v4i*)(smem + vbs + v8_off(vro[cc], 2 * lh + 1));
+      vf[cc] = v8i{v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    }
+  };
+  auto pv8_mfma = [&](const v8i (&vf)[NCC]) __attribute__((always_inline)) {
+    const v8i pf = v8i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3], (int)pk[4], (int)pk[5], (int)pk[6], (int)pk[7]};
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) o[cc] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[cc], pf, o[cc], 0, 0, 0, 127, 0, 127);
+  };
+
   // alpha is exactly 1 for a row whose max did not move: O is rescaled only when some row of
   // the wave has a new max (a wave-uniform branch; the products then overwrite O in place).
   // Late in a long row most tiles leave every max where it was.
@@ -546,7 +687,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   // Phase 2t's copies (this wave's share), always issued: the target buffers are free in that
   // phase whatever t is, and a tile past the last copies no rows (zeros that are never read),
   // so the copy code and the wait counts are the same in every phase (no branches).
-  constexpr int NLOAD_MAX = PipeDma<D>::K_PER + PipeDma<D>::V_PER;
   auto copies = [&](int t, int j) __attribute__((always_inline)) {
     const int j1 = j == 2 ? 0 : j + 1;
     dma.k_next(lds0 + kbuf(j), w);    // K(t+3)
@@ -554,8 +694,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   };
   // wait until at most one phase's copies of this wave are in flight
   auto wait_copies = [&]() __attribute__((always_inline)) {
-    if constexpr (PipeDma<D>::K_INSTR % 8 == 0) wait_vm(NLOAD_MAX);   // every wave copies K
-    else wait_vm((w < PipeDma<D>::K_INSTR ? 1 : 0) + PipeDma<D>::V_PER);
+    wait_vm(PipeDma<D, PV8>::loads_of(w));
   };
   auto begin_half = [&]() __attribute__((always_inline)) {
     phase_barrier();
@@ -569,13 +708,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     // consumed here, before any LDS read of this half, because scalar and LDS returns share a
     // counter and scalar ones come back out of order (an LDS wait with a scalar load
     // outstanding waits for everything).
-    dq = __builtin_fmaxf(qs_use * ksc_next * p.sm_log2, 1.17549435e-38f);
+    if constexpr (PV8) {   // exact two-float product of the block scales and sm_scale * log2(e)
+      const float kh = qscale * ksc_next, kl = __builtin_fmaf(qscale, ksc_next, -kh);
+      dq = kh * p.sm_log2;
+      dq_lo = __builtin_fmaf(kh, p.sm_log2, -dq) + __builtin_fmaf(kh, p.sm_log2_lo, kl * p.sm_log2);
+      pin(dq_lo);
+    } else {
+      dq = __builtin_fmaxf(qs_use * ksc_next * p.sm_log2, 1.17549435e-38f);
+    }
     pin(dq);
     __builtin_amdgcn_sched_barrier(0);
     const int j1 = j == 2 ? 0 : j + 1, j2 = j == 0 ? 2 : j - 1;
     const uint32_t kbs = kbuf(j1);   // K(t+1)
     const uint32_t vbs = vbuf(j2);   // V(t-1)
-    if constexpr (KIND != 2) {
+    if constexpr (PV8 && KIND != 2) {
+      const bool do_sm = t <= tl, do_s = do_sm && t + 1 <= tl, do_pv = t >= 1 && t - 1 <= tl;
+      if (FAST) {
+        v8i v8f[NCC];
+        k_frags(kbs, kf);
+        v8_frags(vbs, v8f);
+        soft_a8(sm, (int64_t)t * KT, false);
+        pv8_mfma(v8f);
+        soft_b8(sm, (int64_t)t * KT, false, 0);   // P(t) codes 0-3 after P.V(t-1) has read them
+        pin(sm.alpha);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pin(pk[e]);
+        SCHED_GROUP(SG_DS_READ, 2 * NCC + 2 * NCC, 0);
+#pragma unroll
+        for (int i = 0; i < NCC; ++i) { SCHED_GROUP(SG_MFMA, 1, 0); SCHED_GROUP(SG_VALU, 24, 0); }
+        __builtin_amdgcn_sched_barrier(0);
+        if (grp == 0) copies(t, j);
+      } else {
+        if (do_s) k_frags(kbs, kf);
+        if (do_sm) soft_a8(sm, (int64_t)t * KT, tail_edge && t == tl);
+        if (do_pv) {
+          v8i v8f[NCC];
+          v8_frags(vbs, v8f);
+          pv8_mfma(v8f);
+        }
+        if (do_sm) soft_b8(sm, (int64_t)t * KT, tail_edge && t == tl, 0);
+        if (grp == 0) copies(t, j);
+      }
+    } else if constexpr (KIND != 2) {
       if (FAST) {
         k_frags(kbs, kf);
         v_frags(vbs, 0, vf[0]);
@@ -635,7 +809,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
     constexpr bool FAST = KIND == 0;
     begin_half();
     hi_nxt = false;
-    if constexpr (KIND != 2) {
+    if constexpr (PV8 && KIND != 2) {
+      const bool do_sm = t <= tl, do_s = do_sm && t + 1 <= tl;
+      if (grp == 1) copies(t + 1, j == 2 ? 0 : j + 1);
+      if (FAST) {
+        s_mfma(kf);
+        soft_b8(sm, (int64_t)t * KT, false, 1);
+        rescale(sm);
+        pin_o();
+#pragma unroll
+        for (int e = 4; e < 8; ++e) pin(pk[e]);
+#pragma unroll
+        for (int i = 0; i < 2 * NCC; ++i) { SCHED_GROUP(SG_MFMA, 1, 0); SCHED_GROUP(SG_VALU, 8, 0); }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        if (do_s) s_mfma(kf);
+        if (do_sm) {
+          soft_b8(sm, (int64_t)t * KT, tail_edge && t == tl, 1);
+          rescale(sm);
+        }
+      }
+    } else if constexpr (KIND != 2) {
       if (FAST) {
         if (grp == 1) copies(t + 1, j == 2 ? 0 : j + 1);
         s_mfma(kf);
@@ -701,7 +895,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
   if (grp == 0) begin_half();
 
   // ---- epilogue: O / l; lane (li, lh) holds row qrow, channels 32cc + 8(r/4) + 4lh + (r%4)
-  const float l_tot = halves_sum(l_run);
+  // (FP8 P: l sums 1.75 P and O sums E4M3(448 P) V, so O / l carries an extra 256; the V
+  // channel scales are applied here)
+  const float l_tot = halves_sum(l_run) * (PV8 ? 256.0f : 1.0f);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_ok) {
 #pragma unroll
@@ -709,8 +905,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_i8_pipe_kernel(PipeParams p,
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int ch = 32 * cc + 8 * g + 4 * lh;
-        const float v0 = o[cc][4 * g] * inv, v1 = o[cc][4 * g + 1] * inv, v2 = o[cc][4 * g + 2] * inv,
-                    v3 = o[cc][4 * g + 3] * inv;
+        float v0 = o[cc][4 * g] * inv, v1 = o[cc][4 * g + 1] * inv, v2 = o[cc][4 * g + 2] * inv,
+              v3 = o[cc][4 * g + 3] * inv;
+        if (PV8) {
+          const float* vsc = p.vs + bkv * D + ch;
+          v0 *= vsc[0]; v1 *= vsc[1]; v2 *= vsc[2]; v3 *= vsc[3];
+        }
         const int64_t off = p.outr.at(bh, qrow) + ch;
         if (OUT_BF16) *(v2i*)((uint16_t*)p.out + off) = v2i{(int)pack_bf16x2(v0, v1), (int)pack_bf16x2(v2, v3)};
         else *(v4f*)((float*)p.out + off) = v4f{v0, v1, v2, v3};
@@ -722,10 +922,13 @@ template <int D, bool CAUSAL, bool VF16, bool OUT_BF16>
 hipError_t launch_pipe(const PipeParams& p, hipStream_t st) {
   if (p.total_wg == 0) return hipSuccess;
   if (p.mask)
-    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16, true>), dim3((unsigned)p.total_wg), dim3(NTHREADS),
-                       0, st, p, p.ks);
+    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16, true, false>), dim3((unsigned)p.total_wg),
+                       dim3(NTHREADS), 0, st, p, p.ks);
+  else if (p.v8)
+    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, false, OUT_BF16, false, true>), dim3((unsigned)p.total_wg),
+                       dim3(NTHREADS), 0, st, p, p.ks);
   else
-    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16, false>), dim3((unsigned)p.total_wg),
+    hipLaunchKernelGGL((attn_i8_pipe_kernel<D, CAUSAL, VF16, OUT_BF16, false, false>), dim3((unsigned)p.total_wg),
                        dim3(NTHREADS), 0, st, p, p.ks);
   return hipGetLastError();
 }
@@ -743,8 +946,12 @@ hipError_t dispatch_pipe(const PipeParams& p, bool vf16, bool out_bf16, hipStrea
 
 }  // namespace
 
-hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attn_int8_pipe(const AttnArgs& a, int pv_fp8, hipStream_t st) {
   PipeParams p;
+  // FP8 P.V: FP8 V^T codes and channel scales (INT8 tiles only: no Thrift mask, no fp16 V)
+  p.v8 = pv_fp8 ? (const uint8_t*)a.v_codes : nullptr;
+  p.vs = pv_fp8 ? (const float*)a.v_scales : nullptr;
+  if (pv_fp8 && (a.mask || a.v_is_f16)) return hipErrorNotSupported;
   p.q = (const int8_t*)a.q_codes; p.qs = (const float*)a.q_scales;
   p.k = (const int8_t*)a.k_codes; p.ks = (const float*)a.k_scales;
   p.v = (const uint16_t*)a.v_codes;
@@ -758,7 +965,12 @@ hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st) {
   p.nQB = (a.N + QB - 1) / QB; p.nKB = (a.N + KT - 1) / KT;
   p.nPairs = (p.nQB + 1) / 2;
   p.total_wg = a.B * a.Hq * p.nPairs;
-  p.sm_log2 = (float)((double)a.sm_scale * 1.4426950408889634074);
+  {
+    const double l2 = (double)a.sm_scale * 1.4426950408889634074;
+    p.sm_log2 = (float)l2;
+    p.sm_log2_lo = (float)(l2 - (double)p.sm_log2);
+  }
+  p.Np = (a.N + KT - 1) / KT * KT;
   const bool causal = a.causal != 0;
   if (a.D == 64) return causal ? dispatch_pipe<64, true>(p, a.v_is_f16, a.out_bf16, st)
                                : dispatch_pipe<64, false>(p, a.v_is_f16, a.out_bf16, st);

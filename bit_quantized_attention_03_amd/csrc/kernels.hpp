@@ -85,10 +85,10 @@ struct AttnArgs {
   Rows16 vr, qhr, khr, outr, q16r;
 };
 hipError_t launch_attn_int8(const AttnArgs& a, int pv_fp8, hipStream_t st);
-// INT8 QK^T, bf16 P.V: the software-pipelined kernel (attn_i8_pipe.hip).  With a Thrift block
+// INT8 QK^T, bf16 or FP8 P.V: the software-pipelined kernel (attn_i8_pipe.hip).  With a Thrift block
 // mask it keeps the workgroup's two mask rows in LDS, so it takes at most this many K tiles.
 constexpr int64_t PIPE_MAX_MASK_TILES = 4096;
-hipError_t launch_attn_int8_pipe(const AttnArgs& a, hipStream_t st);
+hipError_t launch_attn_int8_pipe(const AttnArgs& a, int pv_fp8, hipStream_t st);
 hipError_t launch_attn_mx(const AttnArgs& a, int nvfp4_variant, hipStream_t st);
 
 }  // namespace sage

@@ -374,6 +374,9 @@ ATT_CASES = [
     ("thrift_long", dict(B=1, Hq=2, Hkv=1, N=640), False, "thrift"),
     ("video_fp8", dict(B=1, Hq=2, Hkv=2, N=700), False, "int8_fp8pv"),
     ("video_fp8", dict(B=1, Hq=2, Hkv=2, N=1024), True, "int8_fp8pv"),
+    ("video_fp8", dict(B=1, Hq=4, Hkv=2, N=333), True, "int8_fp8pv"),     # GQA, ragged
+    ("llm_int8", dict(B=1, Hq=2, Hkv=2, N=333), False, "int8_fp8pv"),     # d = 128 FP8 P.V
+    ("llm_int8", dict(B=1, Hq=2, Hkv=2, N=700), True, "int8_fp8pv"),
     ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=333), False, "mxfp4"),
     ("fp4_search", dict(B=1, Hq=2, Hkv=2, N=512), True, "mxfp4"),
     ("fp4_search", dict(B=1, Hq=4, Hkv=2, N=700), True, "mxfp4"),          # GQA
