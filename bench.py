@@ -63,7 +63,7 @@ STEP_TEXT = {
 
 KERNEL_SOURCES = {"int8": ("attn_i8_pipe.hip", "attn_common.hpp"), "thrift": ("attn_i8_pipe.hip", "attn_common.hpp"),
                   "sink": ("attn_i8_pipe.hip", "attn_common.hpp"),
-                  "int8_fp8pv": ("attn_i8.hip", "attn_common.hpp"),
+                  "int8_fp8pv": ("attn_i8_pipe.hip", "attn_common.hpp"),
                   "mxfp4": ("attn_mx.hip", "attn_common.hpp"), "nvfp4_search": ("attn_mx.hip", "attn_common.hpp"),
                   "decode": ("decode.hip",)}
 # kernels whose counters add up to one launch of the measured step

@@ -2,7 +2,9 @@
 //
 // SageAttention ("Accurate 8-Bit Attention for Plug-and-play Inference Acceleration",
 // Technical approach): QK^T on 8-bit Q and smoothed K with per-block scales, an fp32 online
-// softmax, and P and V kept at 16 bits for P.V (here bf16 with fp32 accumulation).
+// softmax, and P and V kept at 16 bits for P.V (here bf16 with fp32 accumulation).  The
+// video-generation form keeps P and V in FP8 instead (P scaled by 448 and V per channel, both
+// E4M3) on the scaled FP8 product; its softmax is described at soft_a8 below.
 //
 // Work decomposition.  A workgroup of 8 waves owns two adjacent Q blocks of 128 rows of one
 // (b, q-head): wave w takes rows 32w .. 32w+31 of the pair.  All waves stream the same K/V
